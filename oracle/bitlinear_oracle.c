@@ -1,0 +1,211 @@
+/*
+ * CPU oracle for the ternary BitLinear layer: TEST INFRASTRUCTURE ONLY.
+ * See bitlinear_oracle.h for the sources and the scope.  Built with
+ * gcc -O2 -ffp-contract=off -fno-fast-math so every float operation below is
+ * one IEEE operation in the precision its operands have.
+ */
+#include "bitlinear_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Qb = 2^(b-1) for b = 8 bit activations ([U] 2. Aktivierungsquantisierung). */
+#define ORACLE_QB 128.0f
+/* Largest code kept by the clip: the bounds -Qb+eps .. Qb-eps with a small
+ * eps leave the integers -127 .. 127. */
+#define ORACLE_QMAX 127.0f
+
+void oracle_bf16_to_f32(const uint16_t* in, int64_t n, float* out) {
+    for (int64_t i = 0; i < n; ++i) {
+        uint32_t bits = ((uint32_t)in[i]) << 16;
+        memcpy(&out[i], &bits, sizeof bits);
+    }
+}
+
+/* Round to the nearest integer, ties to the even neighbour, written out so it
+ * does not depend on the floating-point environment.  |t| <= 128 here, so
+ * t - floor(t) is exact. */
+static float round_half_even(float t) {
+    float f = floorf(t);
+    float frac = t - f;
+    if (frac > 0.5f) return f + 1.0f;
+    if (frac < 0.5f) return f;
+    return (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;
+}
+
+static double round_half_even_d(double t) {
+    double f = floor(t);
+    double frac = t - f;
+    if (frac > 0.5) return f + 1.0;
+    if (frac < 0.5) return f;
+    return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;
+}
+
+/* One token: gamma = ||x||_inf; each entry is divided by gamma, scaled by Qb,
+ * rounded and clipped to [-127, 127].  gamma = 0 quantises to zeros. */
+static float quant_row(const float* x, int64_t K, int8_t* q) {
+    float gamma = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float a = fabsf(x[k]);
+        if (a > gamma) gamma = a;
+    }
+    for (int64_t k = 0; k < K; ++k) {
+        if (gamma == 0.0f) {
+            q[k] = 0;
+            continue;
+        }
+        float ratio = x[k] / gamma;   /* one correctly rounded fp32 division */
+        float t = ratio * ORACLE_QB;  /* exact: Qb is a power of two */
+        float r = round_half_even(t);
+        if (r > ORACLE_QMAX) r = ORACLE_QMAX;
+        if (r < -ORACLE_QMAX) r = -ORACLE_QMAX;
+        q[k] = (int8_t)r;
+    }
+    return gamma;
+}
+
+void oracle_quant_act(const float* x, int64_t M, int64_t K, int8_t* q, float* gamma) {
+    for (int64_t m = 0; m < M; ++m) gamma[m] = quant_row(x + m * K, K, q + m * K);
+}
+
+/* RMSNorm: x * g / sqrt(mean(x^2) + eps) ([D], figure list: RMS norm before
+ * quantisation).  The quantiser divides by the absmax of its input, so the
+ * common factor r = 1/sqrt(mean(x^2)+eps) cancels from the codes: they are the
+ * codes of u = g*x (fp32), and r survives only in gamma = r * max|u|, with r
+ * and that product evaluated in float64 and rounded once to fp32. */
+void oracle_rmsnorm_quant_act(const float* x, const float* g, float eps, int64_t M,
+                              int64_t K, int8_t* q, float* gamma) {
+    float* u = (float*)malloc((size_t)(K > 0 ? K : 1) * sizeof(float));
+    for (int64_t m = 0; m < M; ++m) {
+        const float* xm = x + m * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) ss += (double)xm[k] * (double)xm[k];
+        double mean = K > 0 ? ss / (double)K : 0.0;
+        double r = 1.0 / sqrt(mean + (double)eps);
+        for (int64_t k = 0; k < K; ++k) u[k] = g[k] * xm[k];
+        float absmax_u = quant_row(u, K, q + m * K);
+        gamma[m] = (float)(r * (double)absmax_u);
+    }
+    free(u);
+}
+
+/* The same two steps evaluated literally in float64: normalise, then quantise
+ * the normalised vector.  Codes may differ from the fp32 contract only where
+ * the scaled value sits within rounding distance of a half-integer. */
+void oracle_rmsnorm_quant_act_literal(const float* x, const float* g, float eps,
+                                      int64_t M, int64_t K, int8_t* q, double* gamma) {
+    double* y = (double*)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    for (int64_t m = 0; m < M; ++m) {
+        const float* xm = x + m * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) ss += (double)xm[k] * (double)xm[k];
+        double r = 1.0 / sqrt((K > 0 ? ss / (double)K : 0.0) + (double)eps);
+        double gm = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            y[k] = (double)xm[k] * r * (double)g[k];
+            if (fabs(y[k]) > gm) gm = fabs(y[k]);
+        }
+        gamma[m] = gm;
+        for (int64_t k = 0; k < K; ++k) {
+            double t = gm == 0.0 ? 0.0 : y[k] / gm * 128.0;
+            double rq = round_half_even_d(t);
+            if (rq > 127.0) rq = 127.0;
+            if (rq < -127.0) rq = -127.0;
+            q[m * K + k] = (int8_t)rq;
+        }
+    }
+    free(y);
+}
+
+/* Storage of ternary weights ([U] Das Konzept: three states per weight, just
+ * over one bit of information) as 2-bit codes: code = w + 1, so -1 -> 0,
+ * 0 -> 1, +1 -> 2; 3 marks an entry that was not ternary.  Sixteen
+ * consecutive weights of a row form one little-endian uint32 word; the weight
+ * at position e = 4j + b inside the group sits at bit 8b + 2j. */
+int64_t oracle_pack(const int8_t* w, int64_t N, int64_t K, uint32_t* packed) {
+    int64_t bad = 0;
+    int64_t words = K / 16;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t c = 0; c < words; ++c) {
+            uint32_t word = 0;
+            for (int e = 0; e < 16; ++e) {
+                int v = w[n * K + c * 16 + e];
+                uint32_t code;
+                if (v == -1) code = 0;
+                else if (v == 0) code = 1;
+                else if (v == 1) code = 2;
+                else { code = 3; ++bad; }
+                int j = e / 4, b = e % 4;
+                word |= code << (8 * b + 2 * j);
+            }
+            packed[n * words + c] = word;
+        }
+    }
+    return bad;
+}
+
+void oracle_unpack(const uint32_t* packed, int64_t N, int64_t K, int8_t* w) {
+    int64_t words = K / 16;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t c = 0; c < words; ++c)
+            for (int e = 0; e < 16; ++e) {
+                int j = e / 4, b = e % 4;
+                int code = (int)((packed[n * words + c] >> (8 * b + 2 * j)) & 3u);
+                w[n * K + c * 16 + e] = (int8_t)(code - 1);
+            }
+}
+
+/* Ternary accumulation: multiplying by -1 negates, by 0 gives nothing, by +1
+ * passes the value through ([D] MatMul vervangen door ternaire bewerkingen),
+ * so each output is a signed sum of the quantised activations. */
+int oracle_accumulate(const int8_t* q, int64_t M, int64_t K, const int8_t* w,
+                      int64_t N, int32_t* acc) {
+    int overflow = 0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(| : overflow)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t* qm = q + m * K;
+            const int8_t* wn = w + n * K;
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k) {
+                if (wn[k] == 1) s += qm[k];
+                else if (wn[k] == -1) s -= qm[k];
+            }
+            if (s > INT32_MAX || s < INT32_MIN) overflow = 1;
+            acc[m * N + n] = (int32_t)s;
+        }
+    }
+    return overflow;
+}
+
+/* Output scale beta * gamma / Qb ([U] 3. BitLinear-Betrieb). */
+void oracle_rescale(const int32_t* acc, const float* gamma, int64_t M, int64_t N,
+                    float beta, float* y) {
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double v = (double)acc[m * N + n] * (double)beta * (double)gamma[m] / 128.0;
+            y[m * N + n] = (float)v;
+        }
+}
+
+/* GLU channel mixer glue ([D] Kerncomponenten: MLGRU EN GLU): one projection
+ * goes through SiLU(z) = z / (1 + e^-z) and is multiplied elementwise by the
+ * other. */
+void oracle_silu_mul(const float* gate, const float* up, int64_t n, double* h) {
+    for (int64_t i = 0; i < n; ++i) {
+        double z = (double)gate[i];
+        h[i] = z / (1.0 + exp(-z)) * (double)up[i];
+    }
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

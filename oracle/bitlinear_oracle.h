@@ -1,0 +1,72 @@
+/*
+ * CPU oracle for the ternary BitLinear layer: TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, obviously correct loops that restate the published formulas.
+ * Only the test-suite, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this library; the product path never does.  It shares no
+ * code, header, table or helper with the HIP library.
+ *
+ * Sources (cited by title and section):
+ *   [U] "Microsofts Inference Framework bringt 1-Bit große Sprachmodelle auf
+ *       lokale Geräte" (unite.ai), section "Mathematische Grundlagen":
+ *       2. Aktivierungsquantisierung and 3. BitLinear-Betrieb; section
+ *       "Ternäres Gewichtssystem / Das Konzept".
+ *   [D] "MatMul-free language models" (datacamp.com, Dutch), sections
+ *       "MatMul vervangen door ternaire bewerkingen" and
+ *       "Kerncomponenten: MLGRU EN GLU".
+ *
+ * Parity status: every function below is pinned by the CPU tests except the
+ * float64 SiLU evaluation, whose transcendental is checked only through
+ * identities and limits (parity unpinned beyond those).
+ */
+#ifndef BITLINEAR_ORACLE_H
+#define BITLINEAR_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* bf16 bit patterns -> fp32 by exact widening. */
+void oracle_bf16_to_f32(const uint16_t* in, int64_t n, float* out);
+
+/* Per-token absmax int8 quantisation, [U] 2. Aktivierungsquantisierung.
+ * x fp32 [M][K] -> q int8 [M][K], gamma fp32 [M]. */
+void oracle_quant_act(const float* x, int64_t M, int64_t K, int8_t* q, float* gamma);
+
+/* RMSNorm ([D] RMS norm before quantisation) followed by the quantiser above.
+ * g fp32 [K] is the gain; eps the fp32 epsilon. */
+void oracle_rmsnorm_quant_act(const float* x, const float* g, float eps, int64_t M,
+                              int64_t K, int8_t* q, float* gamma);
+
+/* Literal RMSNorm-then-quantise evaluated in float64 (informational). */
+void oracle_rmsnorm_quant_act_literal(const float* x, const float* g, float eps,
+                                      int64_t M, int64_t K, int8_t* q, double* gamma);
+
+/* 2-bit code packing of ternary weights w int8 [N][K] -> uint32 [N][K/16].
+ * Returns the number of entries outside {-1,0,+1}. */
+int64_t oracle_pack(const int8_t* w, int64_t N, int64_t K, uint32_t* packed);
+
+/* Inverse of oracle_pack (code 3 unpacks to 2, an out-of-range marker). */
+void oracle_unpack(const uint32_t* packed, int64_t N, int64_t K, int8_t* w);
+
+/* acc[m][n] = sum_k w[n][k] * q[m][k]  ([U] 3. BitLinear-Betrieb, [D] ternary
+ * accumulation).  Returns 0, or 1 if a result does not fit int32. */
+int oracle_accumulate(const int8_t* q, int64_t M, int64_t K, const int8_t* w,
+                      int64_t N, int32_t* acc);
+
+/* y[m][n] = acc[m][n] * beta * gamma[m] / 128, float64 then rounded to fp32. */
+void oracle_rescale(const int32_t* acc, const float* gamma, int64_t M, int64_t N,
+                    float beta, float* y);
+
+/* h[i] = silu(gate[i]) * up[i] in float64 ([D] MatMul-vrije GLU). */
+void oracle_silu_mul(const float* gate, const float* up, int64_t n, double* h);
+
+/* Number of OpenMP threads the accumulate loop runs on. */
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
