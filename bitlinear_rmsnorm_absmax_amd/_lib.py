@@ -1,0 +1,190 @@
+"""ctypes binding of ``libbitlinear.so`` (argument marshalling only).
+
+Torch tensors supply device memory and the current HIP stream; every step of
+the computation runs in the library's kernels.  Importing this module fails
+loudly when the library has not been built -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbitlinear.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "bitlinear.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_HIP, ERR_VALUE = range(7)
+F32, BF16 = 0, 1
+PATH_AUTO, PATH_GEMV, PATH_SKINNY, PATH_GEMM = range(4)
+MAX_K = 131072
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+
+_SIGNATURES = {
+    "bitlinear_quant_act": [_vp, ctypes.c_int, _i64, _i64, _vp, _f32, _vp, _vp, _vp],
+    "bitlinear_pack_weights": [_vp, _i64, _i64, _vp, _vp, _vp],
+    "bitlinear_forward": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _vp],
+    "bitlinear_forward_path": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, ctypes.c_int, _vp],
+    "bitlinear_silu_mul_quant": [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp],
+    "bitlinear_last_error": [],
+    "bitlinear_abi_version": [],
+}
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, args in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.bitlinear_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def declared_symbols() -> list:
+    """Entry points declared in include/bitlinear.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(bitlinear_\w+)\s*\(", text, re.M)))
+
+
+def last_error() -> str:
+    return lib.bitlinear_last_error().decode()
+
+
+def abi_version() -> int:
+    return int(lib.bitlinear_abi_version())
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise BitLinearError(status, last_error())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def quant_act(x: torch.Tensor, rms_gain: Optional[torch.Tensor] = None, rms_eps: float = 1e-6,
+              out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Per-token absmax int8 quantisation of x [M][K] (fp32 or bf16), optionally
+    after RMSNorm with gain ``rms_gain`` [K].  Returns (x_q int8, gamma fp32)."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    M, K = x.shape
+    if rms_gain is not None:
+        _dev(rms_gain, "rms_gain", (torch.float32,))
+    if out is None:
+        x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        gamma = torch.empty((M,), dtype=torch.float32, device=x.device)
+    else:
+        x_q, gamma = out
+    dt = BF16 if x.dtype == torch.bfloat16 else F32
+    _check(lib.bitlinear_quant_act(x.data_ptr(), dt, M, K, _ptr(rms_gain), float(rms_eps),
+                                   x_q.data_ptr(), gamma.data_ptr(), _stream(x)))
+    return x_q, gamma
+
+
+def pack_weights(w: torch.Tensor, check: bool = True):
+    """Ternary int8 [N][K] -> packed words [N][K/16] (int32 storage of the
+    uint32 words).  With ``check`` the count of non-ternary entries is read
+    back and a ValueError raised if it is not zero."""
+    _dev(w, "w", (torch.int8,))
+    N, K = w.shape
+    packed = torch.empty((N, K // 16), dtype=torch.int32, device=w.device)
+    bad = torch.zeros((1,), dtype=torch.int32, device=w.device)
+    _check(lib.bitlinear_pack_weights(w.data_ptr(), N, K, packed.data_ptr(), bad.data_ptr(),
+                                      _stream(w)))
+    if check:
+        nbad = int(bad.item())
+        if nbad:
+            raise ValueError(f"{nbad} weight entries are not in {{-1, 0, +1}}")
+    return packed, bad
+
+
+def forward(x_q: torch.Tensor, gamma: torch.Tensor, w_packed: torch.Tensor, beta: float,
+            path: int = PATH_AUTO, want_acc: bool = False,
+            out: Optional[torch.Tensor] = None, acc_out: Optional[torch.Tensor] = None):
+    """y [M][N] = BitLinear(x_q, gamma; w_packed, beta).  Returns y, or
+    (y, acc) with ``want_acc``."""
+    _dev(x_q, "x_q", (torch.int8,))
+    _dev(gamma, "gamma", (torch.float32,))
+    _dev(w_packed, "w_packed", (torch.int32, torch.uint32))
+    M, K = x_q.shape
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 16 != K:
+        raise ValueError(f"w_packed has {w_packed.shape[1]} words per row, K={K} needs {K // 16}")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x_q.device)
+    acc = acc_out
+    if want_acc and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device)
+    _check(lib.bitlinear_forward_path(x_q.data_ptr(), gamma.data_ptr(), M, K, w_packed.data_ptr(),
+                                      N, float(beta), y.data_ptr(), _ptr(acc), int(path),
+                                      _stream(x_q)))
+    return (y, acc) if want_acc else y
+
+
+def silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, want_h: bool = False):
+    """h = SiLU(gate) * up (float64 inside, fp32 out) -> (h_q, gamma_h[, h])."""
+    _dev(gate, "gate", (torch.float32,))
+    _dev(up, "up", (torch.float32,))
+    M, F = gate.shape
+    h_q = torch.empty((M, F), dtype=torch.int8, device=gate.device)
+    g = torch.empty((M,), dtype=torch.float32, device=gate.device)
+    h = torch.empty((M, F), dtype=torch.float32, device=gate.device) if want_h else None
+    _check(lib.bitlinear_silu_mul_quant(gate.data_ptr(), up.data_ptr(), M, F, _ptr(h),
+                                        h_q.data_ptr(), g.data_ptr(), _stream(gate)))
+    return (h_q, g, h) if want_h else (h_q, g)
+
+
+def bitlinear(x: torch.Tensor, w_packed: torch.Tensor, beta: float,
+              rms_gain: Optional[torch.Tensor] = None, rms_eps: float = 1e-6):
+    """Whole layer from fp32 / bf16 activations: quantise then multiply."""
+    x_q, gamma = quant_act(x, rms_gain, rms_eps)
+    return forward(x_q, gamma, w_packed, beta)
+
+
+def glu(x: torch.Tensor, w_gate, w_up, w_down, betas, rms_gain, rms_eps: float = 1e-6,
+        path: int = PATH_AUTO, stages: bool = False):
+    """MatMul-free GLU channel mixer: RMSNorm+quant -> gate, up -> SiLU(gate)*up
+    -> requant -> down.  With ``stages`` every intermediate is returned."""
+    x_q, gamma = quant_act(x, rms_gain, rms_eps)
+    y_gate, acc_gate = forward(x_q, gamma, w_gate, betas[0], path, want_acc=stages)
+    y_up, acc_up = forward(x_q, gamma, w_up, betas[1], path, want_acc=stages)
+    h_q, gamma_h, h = silu_mul_quant(y_gate, y_up, want_h=stages)
+    y, acc_down = forward(h_q, gamma_h, w_down, betas[2], path, want_acc=stages)
+    if not stages:
+        return y
+    return dict(q=x_q, gamma=gamma, acc_gate=acc_gate, y_gate=y_gate, acc_up=acc_up, y_up=y_up,
+                h=h, h_q=h_q, gamma_h=gamma_h, acc_down=acc_down, y=y)

@@ -1,0 +1,186 @@
+// C ABI of the ternary BitLinear library: argument validation, kernel choice
+// by M, launches on the caller's stream.  Validation touches no HIP API, so
+// every error path returns before the runtime is involved.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/bitlinear.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bitlinear_status_t fail(bitlinear_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bitlinear_status_t ok() {
+    g_err[0] = '\0';
+    return BITLINEAR_OK;
+}
+
+bitlinear_status_t from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(BITLINEAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Largest M handled by one grid dimension of the GEMM (65535 row tiles of 128).
+constexpr int64_t kMaxM = 65535LL * 128;
+constexpr int64_t kMaxN = (1LL << 31) - 1;
+
+bitlinear_status_t check_k(const char* fn, const char* name, int64_t K) {
+    if (K < 0 || K % 16 != 0 || K > BITLINEAR_MAX_K)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: %s=%lld must be in [0, %d] and a multiple of 16", fn,
+                    name, (long long)K, BITLINEAR_MAX_K);
+    return BITLINEAR_OK;
+}
+
+bitlinear_status_t check_rows(const char* fn, const char* name, int64_t v, int64_t max) {
+    if (v < 0 || v > max)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: %s=%lld out of range [0, %lld]", fn, name,
+                    (long long)v, (long long)max);
+    return BITLINEAR_OK;
+}
+
+#define BL_TRY(expr)                                  \
+    do {                                              \
+        bitlinear_status_t st_ = (expr);              \
+        if (st_ != BITLINEAR_OK) return st_;          \
+    } while (0)
+
+bitlinear_status_t need(const char* fn, const char* name, const void* p, bool required,
+                        size_t align) {
+    if (!required) return BITLINEAR_OK;
+    if (!p) return fail(BITLINEAR_ERR_NULL, "%s: %s is NULL", fn, name);
+    if (!aligned(p, align))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: %s is not %zu-byte aligned", fn, name, align);
+    return BITLINEAR_OK;
+}
+
+bitlinear_status_t forward_impl(const char* fn, const int8_t* x_q, const float* gamma,
+                                int64_t M, int64_t K, const uint32_t* w_packed, int64_t N,
+                                float beta, float* y, int32_t* acc, int path,
+                                hipStream_t stream) {
+    BL_TRY(check_rows(fn, "M", M, kMaxM));
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    BL_TRY(check_k(fn, "K", K));
+    if (path < BITLINEAR_PATH_AUTO || path > BITLINEAR_PATH_GEMM)
+        return fail(BITLINEAR_ERR_VALUE, "%s: unknown path %d", fn, path);
+    if (!std::isfinite(beta)) return fail(BITLINEAR_ERR_VALUE, "%s: beta is not finite", fn);
+    const bool any_out = M > 0 && N > 0;
+    const bool any_in = any_out && K > 0;
+    BL_TRY(need(fn, "x_q", x_q, any_in, 16));
+    BL_TRY(need(fn, "gamma", gamma, any_in, 4));
+    BL_TRY(need(fn, "w_packed", w_packed, any_in, 16));
+    BL_TRY(need(fn, "y", y, any_out, 4));
+    if (acc && !aligned(acc, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: acc is not 4-byte aligned", fn);
+    if (path == BITLINEAR_PATH_GEMV && M > 4)
+        return fail(BITLINEAR_ERR_VALUE, "%s: the GEMV path takes M <= 4 (M=%lld)", fn, (long long)M);
+    if (path == BITLINEAR_PATH_SKINNY && M > 64)
+        return fail(BITLINEAR_ERR_VALUE, "%s: the skinny path takes M <= 64 (M=%lld)", fn, (long long)M);
+    if (!any_out) return ok();
+    if (K == 0) return from_hip(bl::launch_fill_zero(y, acc, M * N, stream), fn);
+
+    if (path == BITLINEAR_PATH_AUTO) path = (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
+    const int m = (int)M, n = (int)N, k = (int)K;
+    hipError_t e;
+    switch (path) {
+        case BITLINEAR_PATH_GEMV:
+            e = bl::launch_gemv_valu(x_q, gamma, m, k, w_packed, n, beta, y, acc, stream);
+            break;
+        case BITLINEAR_PATH_SKINNY:
+            e = bl::launch_skinny_mfma(x_q, gamma, m, k, w_packed, n, beta, y, acc, stream);
+            break;
+        default:
+            e = bl::launch_gemm_mfma(x_q, gamma, m, k, w_packed, n, beta, y, acc, stream);
+            break;
+    }
+    return from_hip(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+bitlinear_status_t bitlinear_quant_act(const void* x, bitlinear_dtype_t x_dtype, int64_t M,
+                                       int64_t K, const float* rms_gain, float rms_eps,
+                                       int8_t* x_q, float* gamma, hipStream_t stream) {
+    const char* fn = "bitlinear_quant_act";
+    BL_TRY(check_rows(fn, "M", M, (1LL << 31) - 1));
+    BL_TRY(check_k(fn, "K", K));
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16)
+        return fail(BITLINEAR_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)x_dtype);
+    if (rms_gain && !(std::isfinite(rms_eps) && rms_eps >= 0.0f))
+        return fail(BITLINEAR_ERR_VALUE, "%s: rms_eps must be finite and >= 0", fn);
+    const bool any = M > 0 && K > 0;
+    BL_TRY(need(fn, "x", x, any, 16));
+    BL_TRY(need(fn, "x_q", x_q, any, 16));
+    BL_TRY(need(fn, "gamma", gamma, M > 0, 4));
+    if (rms_gain && !aligned(rms_gain, 16))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: rms_gain is not 16-byte aligned", fn);
+    if (M == 0) return ok();
+    return from_hip(bl::launch_quant_act(x, x_dtype == BITLINEAR_BF16, M, K, rms_gain, rms_eps,
+                                         x_q, gamma, stream),
+                    fn);
+}
+
+bitlinear_status_t bitlinear_pack_weights(const int8_t* w, int64_t N, int64_t K,
+                                          uint32_t* w_packed, int32_t* bad_count,
+                                          hipStream_t stream) {
+    const char* fn = "bitlinear_pack_weights";
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    BL_TRY(check_k(fn, "K", K));
+    const bool any = N > 0 && K > 0;
+    BL_TRY(need(fn, "w", w, any, 16));
+    BL_TRY(need(fn, "w_packed", w_packed, any, 16));
+    if (bad_count && !aligned(bad_count, 4))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: bad_count is not 4-byte aligned", fn);
+    if (!any && !bad_count) return ok();
+    return from_hip(bl::launch_pack(w, N, K, w_packed, bad_count, stream), fn);
+}
+
+bitlinear_status_t bitlinear_forward(const int8_t* x_q, const float* gamma, int64_t M, int64_t K,
+                                     const uint32_t* w_packed, int64_t N, float beta, float* y,
+                                     int32_t* acc, hipStream_t stream) {
+    return forward_impl("bitlinear_forward", x_q, gamma, M, K, w_packed, N, beta, y, acc,
+                        BITLINEAR_PATH_AUTO, stream);
+}
+
+bitlinear_status_t bitlinear_forward_path(const int8_t* x_q, const float* gamma, int64_t M,
+                                          int64_t K, const uint32_t* w_packed, int64_t N,
+                                          float beta, float* y, int32_t* acc, int path,
+                                          hipStream_t stream) {
+    return forward_impl("bitlinear_forward_path", x_q, gamma, M, K, w_packed, N, beta, y, acc,
+                        path, stream);
+}
+
+bitlinear_status_t bitlinear_silu_mul_quant(const float* gate, const float* up, int64_t M,
+                                            int64_t F, float* h, int8_t* h_q, float* gamma_h,
+                                            hipStream_t stream) {
+    const char* fn = "bitlinear_silu_mul_quant";
+    BL_TRY(check_rows(fn, "M", M, (1LL << 31) - 1));
+    BL_TRY(check_k(fn, "F", F));
+    const bool any = M > 0 && F > 0;
+    BL_TRY(need(fn, "gate", gate, any, 16));
+    BL_TRY(need(fn, "up", up, any, 16));
+    BL_TRY(need(fn, "h_q", h_q, any, 16));
+    BL_TRY(need(fn, "gamma_h", gamma_h, M > 0, 4));
+    if (h && !aligned(h, 16)) return fail(BITLINEAR_ERR_ALIGN, "%s: h is not 16-byte aligned", fn);
+    if (M == 0) return ok();
+    return from_hip(bl::launch_silu_mul_quant(gate, up, M, F, h, h_q, gamma_h, stream), fn);
+}
+
+const char* bitlinear_last_error(void) { return g_err; }
+
+int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Decode GEMV on the vector ALUs (M <= 4 tokens, HBM-bound).
+//
+// Ternary product (unite.ai BitNet.cpp article, 3. BitLinear-Betrieb;
+// datacamp MatMul-free article: products by -1, 0, +1 become negate, skip,
+// keep) with v_dot4_i32_i8 on the 2-bit codes c = w + 1: a code byte of 0, 1
+// or 2 turns each 4-wide dot product into a sum of selected and doubled
+// activations, and acc = sum c*q - sum q corrects the +1 offset once per
+// lane (the activation sum of a lane's K slice is shared by every row).
+//
+// A wave owns R consecutive weight rows.  Lane l streams the 16-byte units
+// (4 packed words = 64 weights) u = l, l+64, ... of each row, so one wave-wide
+// load covers 1 KB of a row contiguously.  The activation unit of the lane
+// (64 int8 per token) is loaded once per unit and reused by the R rows.  The
+// R x M lane partials are reduced across the wave with DPP row operations
+// (quad permutes and row rotations inside each 16-lane row) followed by four
+// v_readlane reads; the rescale is fused into the store.
+#include "device_common.h"
+#include "internal.h"
+
+namespace bl {
+namespace {
+
+constexpr int kGvThreads = 256;
+constexpr int kGvWaves = kGvThreads / kWave;
+
+// Sum over the 64 lanes of a wave; the result is wave-uniform.
+__device__ __forceinline__ int wave_reduce_dpp(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+template <int MR, int R>
+__global__ __launch_bounds__(kGvThreads) void gemv_valu_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
+    const uint32_t* __restrict__ wp, int N, float beta, float* __restrict__ y,
+    int32_t* __restrict__ acc_out) {
+    const int lane = threadIdx.x % kWave;
+    const int wv = threadIdx.x / kWave;
+    const int n0 = (blockIdx.x * kGvWaves + wv) * R;
+    if (n0 >= N) return;
+    const int WR = K >> 4;
+    const int units = (WR + 3) >> 2;
+    const bool aligned = (WR & 3) == 0;
+
+    int part[R][MR];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) part[r][m] = 0;
+    int spart[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) spart[m] = 0;
+
+    for (int u = lane; u < units; u += kWave) {
+        const int wb = 4 * u;
+        v4i a[MR][4];
+#pragma unroll
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (m < M && wb + s < WR)
+                    a[m][s] = *reinterpret_cast<const v4i*>(xq + (int64_t)m * K + 16 * (wb + s));
+                else
+                    a[m][s] = v4i{0, 0, 0, 0};
+                spart[m] = byte_sum16(a[m][s], spart[m]);
+            }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int n = n0 + r;
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+            if (n < N) {
+                const uint32_t* p = wp + (int64_t)n * WR + wb;
+                if (aligned) {
+                    v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+                    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+                } else {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) w[s] = (wb + s < WR) ? p[s] : 0u;
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const v4i c = unpack_codes(w[s]);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    int d = part[r][m];
+                    d = __builtin_amdgcn_sdot4(c.x, a[m][s].x, d, false);
+                    d = __builtin_amdgcn_sdot4(c.y, a[m][s].y, d, false);
+                    d = __builtin_amdgcn_sdot4(c.z, a[m][s].z, d, false);
+                    d = __builtin_amdgcn_sdot4(c.w, a[m][s].w, d, false);
+                    part[r][m] = d;
+                }
+            }
+        }
+    }
+
+    // lane r (< R) collects row n0 + r for every token
+    float yv[MR];
+    int av[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        yv[m] = 0.f;
+        av[m] = 0;
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        const float sc = (m < M) ? out_scale(beta, gamma[m]) : 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int tot = wave_reduce_dpp(part[r][m] - spart[m]);
+            if (lane == r) {
+                av[m] = tot;
+                yv[m] = (float)tot * sc;
+            }
+        }
+    }
+    const int n = n0 + lane;
+    if (lane < R && n < N) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            if (m < M) {
+                y[(int64_t)m * N + n] = yv[m];
+                if (acc_out) acc_out[(int64_t)m * N + n] = av[m];
+            }
+        }
+    }
+}
+
+template <int MR, int R>
+hipError_t launch_gv(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
+                     int N, float beta, float* y, int32_t* acc, hipStream_t s) {
+    const int rows_per_block = kGvWaves * R;
+    const int blocks = (N + rows_per_block - 1) / rows_per_block;
+    gemv_valu_kernel<MR, R><<<dim3(blocks), dim3(kGvThreads), 0, s>>>(xq, gamma, M, K, wp, N,
+                                                                      beta, y, acc);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_valu(const int8_t* xq, const float* gamma, int M, int K,
+                            const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
+                            hipStream_t s) {
+    if (M <= 1) return launch_gv<1, 8>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (M <= 2) return launch_gv<2, 8>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    return launch_gv<4, 4>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+}
+
+}  // namespace bl

@@ -1,0 +1,235 @@
+// Per-token absmax int8 quantisation kernels (unite.ai BitNet.cpp article,
+// Mathematische Grundlagen, 2. Aktivierungsquantisierung), the fused
+// RMSNorm + quantisation variant (datacamp MatMul-free article,
+// Kerncomponenten: RMS norm before quantisation), and the GLU glue
+// h = SiLU(gate) * up followed by the same quantisation (datacamp article,
+// MatMul-vrije GLU).
+//
+// One workgroup of 256 threads per token row.  A row is split into 16-element
+// chunks (K % 16 == 0) dealt round-robin to the threads, so each load and
+// each 16-byte code store is contiguous across the wave.  The first
+// kQuantCache chunks of every thread stay in registers between the absmax
+// pass and the quantisation pass, so rows up to 256 * 16 * kQuantCache
+// elements are read from HBM exactly once; longer rows re-read the remainder
+// (L2-resident by then).
+#include "device_common.h"
+#include "internal.h"
+
+namespace bl {
+namespace {
+
+constexpr int kQuantThreads = 256;
+constexpr int kQuantCache = 2;
+
+enum class Src { F32, BF16, SILU_MUL };
+
+struct RowSrc {
+    const void* a;  // x (fp32 / bf16) or gate (fp32)
+    const float* b; // up (SILU_MUL only)
+};
+
+// Load chunk c (16 elements) of row `row` (length K) as fp32.
+template <Src S>
+__device__ __forceinline__ void load_chunk(const RowSrc& src, int64_t row, int K, int c,
+                                           float v[16]) {
+    const int64_t base = row * (int64_t)K + (int64_t)c * 16;
+    if constexpr (S == Src::F32) {
+        const v4f* p = reinterpret_cast<const v4f*>(static_cast<const float*>(src.a) + base);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v4f t = __builtin_nontemporal_load(p + i);
+            v[4 * i + 0] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+        }
+    } else if constexpr (S == Src::BF16) {
+        const v4u* p = reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(src.a) + base);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            v4u t = __builtin_nontemporal_load(p + i);
+            uint32_t d[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j + 0] = __uint_as_float(d[j] << 16);          // exact widening
+                v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+            }
+        }
+    } else {
+        const float4* pg = reinterpret_cast<const float4*>(static_cast<const float*>(src.a) + base);
+        const float4* pu = reinterpret_cast<const float4*>(src.b + base);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float4 g = pg[i];
+            float4 u = pu[i];
+            float gg[4] = {g.x, g.y, g.z, g.w};
+            float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // silu(z) * up in float64, rounded once to fp32
+                double z = (double)gg[j];
+                double sl = z / (1.0 + exp(-z));
+                v[4 * i + j] = (float)(sl * (double)uu[j]);
+            }
+        }
+    }
+}
+
+// Block-wide reductions: max of a float and sum of a double.
+__device__ __forceinline__ void block_reduce(float& amax, double& ss, bool with_ss) {
+    __shared__ float s_max[kQuantThreads / kWave];
+    __shared__ double s_ss[kQuantThreads / kWave];
+    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+    amax = wave_max(amax);
+    if (with_ss) ss = wave_sum_d(ss);
+    if (lane == 0) {
+        s_max[wv] = amax;
+        s_ss[wv] = ss;
+    }
+    __syncthreads();
+    amax = s_max[0];
+    ss = s_ss[0];
+#pragma unroll
+    for (int i = 1; i < kQuantThreads / kWave; ++i) {
+        amax = fmaxf(amax, s_max[i]);
+        ss += s_ss[i];
+    }
+}
+
+__device__ __forceinline__ void store_codes(int8_t* q, int64_t row, int K, int c,
+                                            const float v[16], float gamma) {
+    uint32_t d[4];
+    if (gamma == 0.0f) {
+        d[0] = d[1] = d[2] = d[3] = 0u;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            d[j] = pack4(quant_code(v[4 * j], gamma), quant_code(v[4 * j + 1], gamma),
+                         quant_code(v[4 * j + 2], gamma), quant_code(v[4 * j + 3], gamma));
+    }
+    uint4* p = reinterpret_cast<uint4*>(q + row * (int64_t)K + (int64_t)c * 16);
+    *p = make_uint4(d[0], d[1], d[2], d[3]);
+}
+
+// RMS: gain applied before the absmax (u = g * x), sum of x^2 in float64.
+// H_OUT: also write the fp32 values being quantised (the SiLU*up product).
+template <Src S, bool RMS, bool H_OUT>
+__global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
+    RowSrc src, int K, const float* __restrict__ gain, float eps, float* __restrict__ h_out,
+    int8_t* __restrict__ q, float* __restrict__ gamma_out) {
+    const int64_t row = blockIdx.x;
+    const int nchunk = K / 16;
+    float cache[kQuantCache][16];
+    float amax = 0.0f;
+    double ss = 0.0;
+
+    auto prepare = [&](int c, float v[16]) {
+        load_chunk<S>(src, row, K, c, v);
+        if constexpr (RMS) {
+            const float4* pg = reinterpret_cast<const float4*>(gain + (int64_t)c * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float4 g = pg[i];
+                float gg[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float xv = v[4 * i + j];
+                    ss += (double)xv * (double)xv;
+                    v[4 * i + j] = gg[j] * xv;
+                }
+            }
+        }
+        if constexpr (H_OUT) {
+            float4* ph = reinterpret_cast<float4*>(h_out + row * (int64_t)K + (int64_t)c * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ph[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    };
+
+#pragma unroll
+    for (int i = 0; i < kQuantCache; ++i) {
+        int c = threadIdx.x + i * kQuantThreads;
+        if (c < nchunk) prepare(c, cache[i]);
+    }
+    for (int c = threadIdx.x + kQuantCache * kQuantThreads; c < nchunk; c += kQuantThreads) {
+        float v[16];
+        prepare(c, v);
+    }
+    block_reduce(amax, ss, RMS);
+
+    float gamma = amax;
+    if constexpr (RMS) {
+        double r = 1.0 / sqrt(ss / (double)K + (double)eps);
+        gamma = (float)(r * (double)amax);
+    }
+    if (threadIdx.x == 0) gamma_out[row] = gamma;
+
+#pragma unroll
+    for (int i = 0; i < kQuantCache; ++i) {
+        int c = threadIdx.x + i * kQuantThreads;
+        if (c < nchunk) store_codes(q, row, K, c, cache[i], amax);
+    }
+    for (int c = threadIdx.x + kQuantCache * kQuantThreads; c < nchunk; c += kQuantThreads) {
+        float v[16];
+        load_chunk<S>(src, row, K, c, v);
+        if constexpr (RMS) {
+            const float4* pg = reinterpret_cast<const float4*>(gain + (int64_t)c * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float4 g = pg[i];
+                v[4 * i + 0] *= g.x; v[4 * i + 1] *= g.y; v[4 * i + 2] *= g.z; v[4 * i + 3] *= g.w;
+            }
+        }
+        store_codes(q, row, K, c, v, amax);
+    }
+}
+
+// Rows with K == 0: gamma = 0 and nothing else to write.
+__global__ void zero_gamma_kernel(float* gamma, int64_t M) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < M) gamma[i] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, const float* gain,
+                            float eps, int8_t* q, float* gamma, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    if (K == 0) {
+        zero_gamma_kernel<<<dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s>>>(gamma, M);
+        return hipGetLastError();
+    }
+    RowSrc src{x, nullptr};
+    dim3 grid((unsigned)M), block(kQuantThreads);
+    const int k = (int)K;
+    if (bf16) {
+        if (gain)
+            quant_rows_kernel<Src::BF16, true, false><<<grid, block, 0, s>>>(src, k, gain, eps, nullptr, q, gamma);
+        else
+            quant_rows_kernel<Src::BF16, false, false><<<grid, block, 0, s>>>(src, k, nullptr, 0.f, nullptr, q, gamma);
+    } else {
+        if (gain)
+            quant_rows_kernel<Src::F32, true, false><<<grid, block, 0, s>>>(src, k, gain, eps, nullptr, q, gamma);
+        else
+            quant_rows_kernel<Src::F32, false, false><<<grid, block, 0, s>>>(src, k, nullptr, 0.f, nullptr, q, gamma);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_silu_mul_quant(const float* gate, const float* up, int64_t M, int64_t F,
+                                 float* h, int8_t* h_q, float* gamma, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    if (F == 0) {
+        zero_gamma_kernel<<<dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s>>>(gamma, M);
+        return hipGetLastError();
+    }
+    RowSrc src{gate, up};
+    dim3 grid((unsigned)M), block(kQuantThreads);
+    if (h)
+        quant_rows_kernel<Src::SILU_MUL, false, true><<<grid, block, 0, s>>>(src, (int)F, nullptr, 0.f, h, h_q, gamma);
+    else
+        quant_rows_kernel<Src::SILU_MUL, false, false><<<grid, block, 0, s>>>(src, (int)F, nullptr, 0.f, nullptr, h_q, gamma);
+    return hipGetLastError();
+}
+
+}  // namespace bl

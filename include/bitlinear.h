@@ -1,0 +1,159 @@
+/*
+ * bitlinear.h -- C ABI of the MI355X (gfx950) ternary BitLinear library.
+ *
+ * The layer (following "Microsofts Inference Framework bringt 1-Bit große
+ * Sprachmodelle auf lokale Geräte" (unite.ai), Mathematische Grundlagen,
+ * 2. Aktivierungsquantisierung and 3. BitLinear-Betrieb, and "MatMul-free
+ * language models" (datacamp.com), MatMul vervangen door ternaire
+ * bewerkingen / Kerncomponenten: MLGRU EN GLU):
+ *
+ *   gamma_m = max_k |x_mk|                       (per token)
+ *   q_mk    = clamp(rne(fl32(x_mk / gamma_m) * 128), -127, 127), 0 if gamma_m = 0
+ *   acc_mn  = sum_k w_nk * q_mk                  (w in {-1, 0, +1}, exact int32)
+ *   y_mn    = fl32(acc_mn) * (fl32(beta * gamma_m) / 128)
+ *
+ * Conventions shared by every entry point:
+ *  - Every pointer argument is a DEVICE pointer (memory from hipMalloc or a
+ *    torch CUDA/HIP tensor) unless stated otherwise.  Matrices are row-major
+ *    and contiguous.  The caller owns all memory; the library never
+ *    allocates, frees or retains it.
+ *  - All calls are asynchronous on `stream` (0 = the null stream).  The
+ *    returned status covers argument validation, which runs on the host
+ *    before anything is launched (nothing is written on a validation error),
+ *    and the launch itself.  A fault inside a kernel surfaces at the caller's
+ *    next synchronisation, as usual in HIP.
+ *  - Sizes are int64_t; M, N, K may be 0 (empty work).  K, the reduction
+ *    length, must be a multiple of 16 and at most 131072, so |acc| <= 127*K
+ *    < 2^24 and fl32(acc) is exact.
+ *  - Pointers to int8 / packed data and to the activations x must be 16-byte
+ *    aligned; float / int32 vectors must be 4-byte aligned.
+ *  - No C++ exception crosses the boundary.  On a non-OK status,
+ *    bitlinear_last_error() returns a message (thread-local).
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Packed-weight layout version; bumps whenever the layout below changes. */
+#define BITLINEAR_ABI_VERSION 1
+#define BITLINEAR_MAX_K 131072
+
+typedef enum {
+    BITLINEAR_OK = 0,
+    BITLINEAR_ERR_NULL = 1,   /* a required pointer is NULL                       */
+    BITLINEAR_ERR_SHAPE = 2,  /* negative size, K % 16 != 0, K > BITLINEAR_MAX_K   */
+    BITLINEAR_ERR_ALIGN = 3,  /* a pointer violates the alignment rule above        */
+    BITLINEAR_ERR_DTYPE = 4,  /* unknown bitlinear_dtype_t                          */
+    BITLINEAR_ERR_HIP = 5,    /* the HIP runtime reported an error at launch        */
+    BITLINEAR_ERR_VALUE = 6   /* an argument value outside its domain (path id,
+                                 non-finite beta, negative or non-finite eps)       */
+} bitlinear_status_t;
+
+typedef enum { BITLINEAR_F32 = 0, BITLINEAR_BF16 = 1 } bitlinear_dtype_t;
+
+/* Forward kernel choice for bitlinear_forward_path. */
+typedef enum {
+    BITLINEAR_PATH_AUTO = 0,    /* pick by M (what bitlinear_forward does)          */
+    BITLINEAR_PATH_GEMV = 1,    /* VALU dot4 GEMV, lanes reduced with DPP; M <= 4   */
+    BITLINEAR_PATH_SKINNY = 2,  /* int8 MFMA with M padded to 16-row tiles; M <= 64 */
+    BITLINEAR_PATH_GEMM = 3     /* LDS-tiled int8 MFMA GEMM; any M                  */
+} bitlinear_path_t;
+
+/*
+ * Per-token absmax int8 activation quantisation (unite.ai article,
+ * Mathematische Grundlagen, 2. Aktivierungsquantisierung; Qb = 2^(8-1) = 128,
+ * gamma = infinity norm of the token, codes clipped to [-127, 127], rounding
+ * to nearest with ties to even), optionally after RMSNorm (datacamp article,
+ * Kerncomponenten: the RMS norm that normalises activations before they are
+ * quantised).
+ *
+ *   x        [M][K] activations, fp32 or bf16 (x_dtype); bf16 is widened exactly.
+ *   rms_gain NULL: no normalisation.  Else fp32 [K] gain g of
+ *            RMSNorm(x) = g * x / sqrt(mean(x^2) + rms_eps).  The quantiser
+ *            divides by the absmax of its input, so the RMS factor cancels
+ *            from the codes: q is computed from u = fl32(g * x) and gamma_m =
+ *            fl32(r_m * max|u|) with r_m = 1/sqrt(mean_k x_mk^2 + eps)
+ *            evaluated in float64.
+ *   rms_eps  >= 0 and finite (ignored without rms_gain).
+ *   x_q      out [M][K] int8 codes.
+ *   gamma    out [M] fp32 per-token scale (0 for an all-zero token).
+ * Preconditions: finite inputs.
+ */
+bitlinear_status_t bitlinear_quant_act(const void* x, bitlinear_dtype_t x_dtype, int64_t M,
+                                       int64_t K, const float* rms_gain, float rms_eps,
+                                       int8_t* x_q, float* gamma, hipStream_t stream);
+
+/*
+ * Packs ternary weights (unite.ai article, Ternäres Gewichtssystem / Das
+ * Konzept: each weight is one of -1, 0, +1) at 2 bits each.
+ *
+ *   w        [N][K] int8, entries in {-1, 0, +1}.
+ *   w_packed out [N][K/16] uint32.  code = w + 1 (-1 -> 0, 0 -> 1, +1 -> 2);
+ *            weight k of row n sits in word n*(K/16) + k/16 at bit
+ *            8*b + 2*j where e = k % 16 = 4*j + b.  So (word >> 2j) & 0x03030303
+ *            holds the codes of weights 4j .. 4j+3 in bytes 0..3.  An entry
+ *            outside {-1, 0, +1} is stored as code 3 and counted.
+ *   bad_count optional device int32: set to the number of entries outside
+ *            {-1, 0, +1} (no host synchronisation).  NULL to skip.
+ */
+bitlinear_status_t bitlinear_pack_weights(const int8_t* w, int64_t N, int64_t K,
+                                          uint32_t* w_packed, int32_t* bad_count,
+                                          hipStream_t stream);
+
+/*
+ * BitLinear forward on quantised activations (unite.ai article, 3.
+ * BitLinear-Betrieb: ternary weights times quantised activations, rescaled by
+ * beta * gamma / Qb; datacamp article: the products become additions,
+ * subtractions and skips).
+ *
+ *   x_q, gamma  outputs of bitlinear_quant_act ([M][K] int8, [M] fp32).
+ *   w_packed    [N][K/16] from bitlinear_pack_weights (16-byte aligned).
+ *   beta        per-tensor fp32 weight scale (finite).
+ *   y           out [M][N] fp32.
+ *   acc         optional out [M][N] int32 accumulators; NULL to skip.
+ * The result does not depend on which kernel runs (bit-identical acc and y).
+ */
+bitlinear_status_t bitlinear_forward(const int8_t* x_q, const float* gamma, int64_t M, int64_t K,
+                                     const uint32_t* w_packed, int64_t N, float beta, float* y,
+                                     int32_t* acc, hipStream_t stream);
+
+/* bitlinear_forward with an explicit kernel (bitlinear_path_t).  A path that
+ * cannot take this M (GEMV: M > 4, SKINNY: M > 64) returns BITLINEAR_ERR_VALUE. */
+bitlinear_status_t bitlinear_forward_path(const int8_t* x_q, const float* gamma, int64_t M,
+                                          int64_t K, const uint32_t* w_packed, int64_t N,
+                                          float beta, float* y, int32_t* acc, int path,
+                                          hipStream_t stream);
+
+/*
+ * GLU glue of the MatMul-free channel mixer (datacamp article, Kerncomponenten:
+ * one projection passes through SiLU and multiplies the other elementwise;
+ * the product feeds the next BitLinear layer), followed by the per-token
+ * absmax quantisation of bitlinear_quant_act.
+ *
+ *   gate, up  [M][F] fp32 (outputs of the gate and up projections).
+ *   h         optional out [M][F] fp32: h = silu(gate) * up, evaluated in
+ *             float64 (silu(z) = z / (1 + e^-z)) and rounded once to fp32.
+ *             NULL to skip.
+ *   h_q       out [M][F] int8 codes of h; gamma_h out [M] fp32.
+ * F follows the rules of K (multiple of 16, at most 131072).
+ */
+bitlinear_status_t bitlinear_silu_mul_quant(const float* gate, const float* up, int64_t M,
+                                            int64_t F, float* h, int8_t* h_q, float* gamma_h,
+                                            hipStream_t stream);
+
+/* Text of the last non-OK status on this thread ("" if none). */
+const char* bitlinear_last_error(void);
+
+/* BITLINEAR_ABI_VERSION of the loaded library. */
+int bitlinear_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITLINEAR_H */

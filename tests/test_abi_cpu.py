@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/bitlinear.h, and rejects bad arguments with the documented
+status before anything is launched."""
+
+import ctypes
+import subprocess
+
+import pytest
+
+import bitlinear_rmsnorm_absmax_amd as bl
+from bitlinear_rmsnorm_absmax_amd import _lib
+
+F = ctypes.c_float
+FAKE = 0x10000  # a 16-byte aligned non-NULL address; never dereferenced on error paths
+
+
+def test_every_declared_symbol_is_exported():
+    declared = bl.declared_symbols()
+    assert set(declared) == {
+        "bitlinear_quant_act", "bitlinear_pack_weights", "bitlinear_forward",
+        "bitlinear_forward_path", "bitlinear_silu_mul_quant", "bitlinear_last_error",
+        "bitlinear_abi_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(bl.lib, name)
+
+
+def test_abi_version():
+    assert bl.abi_version() == 1
+
+
+def _fwd(xq=FAKE, g=FAKE, M=1, K=16, w=FAKE, N=1, beta=1.0, y=FAKE, acc=None, path=0):
+    return bl.lib.bitlinear_forward_path(xq, g, M, K, w, N, F(beta), y, acc, path, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(xq=None), bl.ERR_NULL, "x_q is NULL"),
+    (dict(g=None), bl.ERR_NULL, "gamma is NULL"),
+    (dict(w=None), bl.ERR_NULL, "w_packed is NULL"),
+    (dict(y=None), bl.ERR_NULL, "y is NULL"),
+    (dict(M=-1), bl.ERR_SHAPE, "M=-1"),
+    (dict(N=-5), bl.ERR_SHAPE, "N=-5"),
+    (dict(K=24), bl.ERR_SHAPE, "multiple of 16"),
+    (dict(K=131072 + 16), bl.ERR_SHAPE, "K=131088"),
+    (dict(xq=FAKE + 4), bl.ERR_ALIGN, "x_q is not 16-byte aligned"),
+    (dict(w=FAKE + 8), bl.ERR_ALIGN, "w_packed is not 16-byte aligned"),
+    (dict(y=FAKE + 2), bl.ERR_ALIGN, "y is not 4-byte aligned"),
+    (dict(acc=FAKE + 1), bl.ERR_ALIGN, "acc is not 4-byte aligned"),
+    (dict(path=7), bl.ERR_VALUE, "unknown path"),
+    (dict(path=-1), bl.ERR_VALUE, "unknown path"),
+    (dict(beta=float("inf")), bl.ERR_VALUE, "beta"),
+    (dict(beta=float("nan")), bl.ERR_VALUE, "beta"),
+    (dict(M=5, path=1), bl.ERR_VALUE, "GEMV path takes M <= 4"),
+    (dict(M=65, path=2), bl.ERR_VALUE, "skinny path takes M <= 64"),
+])
+def test_forward_rejects(kw, status, msg):
+    assert _fwd(**kw) == status
+    assert msg in bl.last_error()
+
+
+def test_forward_empty_work_is_ok_without_pointers():
+    assert _fwd(xq=None, g=None, w=None, y=None, M=0) == bl.OK
+    assert _fwd(xq=None, g=None, w=None, y=None, N=0) == bl.OK
+    assert bl.last_error() == ""
+    # plain entry point shares the validation
+    assert bl.lib.bitlinear_forward(None, None, 0, 16, None, 3, F(1.0), None, None, None) == bl.OK
+
+
+def _quant(x=FAKE, dt=0, M=1, K=16, gain=None, eps=1e-6, q=FAKE, g=FAKE):
+    return bl.lib.bitlinear_quant_act(x, dt, M, K, gain, F(eps), q, g, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(x=None), bl.ERR_NULL, "x is NULL"),
+    (dict(q=None), bl.ERR_NULL, "x_q is NULL"),
+    (dict(g=None), bl.ERR_NULL, "gamma is NULL"),
+    (dict(dt=2), bl.ERR_DTYPE, "unknown dtype"),
+    (dict(K=8), bl.ERR_SHAPE, "multiple of 16"),
+    (dict(M=-2), bl.ERR_SHAPE, "M=-2"),
+    (dict(x=FAKE + 4), bl.ERR_ALIGN, "x is not 16-byte aligned"),
+    (dict(gain=FAKE + 4), bl.ERR_ALIGN, "rms_gain is not 16-byte aligned"),
+    (dict(gain=FAKE, eps=-1.0), bl.ERR_VALUE, "rms_eps"),
+    (dict(gain=FAKE, eps=float("nan")), bl.ERR_VALUE, "rms_eps"),
+])
+def test_quant_rejects(kw, status, msg):
+    assert _quant(**kw) == status
+    assert msg in bl.last_error()
+
+
+def test_quant_empty_is_ok():
+    assert _quant(x=None, q=None, g=None, M=0) == bl.OK
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((None, 1, 16, FAKE, None), bl.ERR_NULL, "w is NULL"),
+    ((FAKE, 1, 16, None, None), bl.ERR_NULL, "w_packed is NULL"),
+    ((FAKE, 1, 40, FAKE, None), bl.ERR_SHAPE, "multiple of 16"),
+    ((FAKE, -1, 16, FAKE, None), bl.ERR_SHAPE, "N=-1"),
+    ((FAKE + 1, 1, 16, FAKE, None), bl.ERR_ALIGN, "w is not 16-byte aligned"),
+    ((FAKE, 1, 16, FAKE, FAKE + 2), bl.ERR_ALIGN, "bad_count"),
+])
+def test_pack_rejects(args, status, msg):
+    assert bl.lib.bitlinear_pack_weights(*args, None) == status
+    assert msg in bl.last_error()
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((None, FAKE, 1, 16, None, FAKE, FAKE), bl.ERR_NULL, "gate is NULL"),
+    ((FAKE, None, 1, 16, None, FAKE, FAKE), bl.ERR_NULL, "up is NULL"),
+    ((FAKE, FAKE, 1, 16, None, None, FAKE), bl.ERR_NULL, "h_q is NULL"),
+    ((FAKE, FAKE, 1, 16, None, FAKE, None), bl.ERR_NULL, "gamma_h is NULL"),
+    ((FAKE, FAKE, 1, 20, None, FAKE, FAKE), bl.ERR_SHAPE, "F=20"),
+    ((FAKE, FAKE, 1, 16, FAKE + 4, FAKE, FAKE), bl.ERR_ALIGN, "h is not 16-byte aligned"),
+])
+def test_silu_mul_quant_rejects(args, status, msg):
+    assert bl.lib.bitlinear_silu_mul_quant(*args, None) == status
+    assert msg in bl.last_error()
+
+
+def test_error_text_is_thread_local():
+    import threading
+    assert _fwd(M=-1) == bl.ERR_SHAPE
+    seen = {}
+
+    def other():
+        seen["before"] = bl.last_error()
+        _quant(dt=9)
+        seen["after"] = bl.last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["before"] == "" and "dtype" in seen["after"]
+    assert "M=-1" in bl.last_error()
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bl.quant_act(torch.zeros(2, 16))

@@ -1,0 +1,345 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bar: bit-exact int8 codes, gamma (no-norm path), packed words and int32
+accumulators; fp32 outputs within 1e-6 relative (y_ref = 0 forces y = 0).
+Every input comes from workloads.py; every expected value from oracle/.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from conftest import GOLDEN
+
+pytestmark = pytest.mark.gpu
+
+bl = pytest.importorskip("bitlinear_rmsnorm_absmax_amd")
+
+REL = 1e-6
+PATHS = {"gemv": bl.PATH_GEMV, "skinny": bl.PATH_SKINNY, "gemm": bl.PATH_GEMM, "auto": bl.PATH_AUTO}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to(dev)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def assert_y_close(y, y_ref):
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    err = np.abs(y - y_ref)
+    bad = err > REL * np.abs(y_ref)
+    assert not bad.any(), f"{bad.sum()} outputs beyond 1e-6 rel; worst {err[bad].max()}"
+
+
+def gpu_pack(w, dev):
+    packed, bad = bl.pack_weights(to_dev(w, dev))
+    return packed
+
+
+def run_forward(x_f32, w, beta, dev, path=bl.PATH_AUTO, rms=False):
+    """GPU quant + pack + forward; returns host arrays (q, gamma, y, acc)."""
+    xd = to_dev(x_f32, dev)
+    gain = torch.ones(x_f32.shape[1], dtype=torch.float32, device=dev) if rms else None
+    q, g = bl.quant_act(xd, gain)
+    wp = gpu_pack(w, dev)
+    y, acc = bl.forward(q, g, wp, beta, path=path, want_acc=True)
+    return host(q), host(g), host(y), host(acc)
+
+
+# ------------------------------------------------------------------ worked example
+
+def test_worked_example_on_gpu(dev):
+    gd = json.load(open(os.path.join(GOLDEN, "worked_4x4.json")))
+    # pad K = 4 -> 16 with zero activations and zero weights (changes nothing)
+    x = np.zeros((3, 16), np.float32)
+    x[:, :4] = gd["x"]
+    w = np.zeros((4, 16), np.int8)
+    w[:, :4] = gd["W"]
+    for name, path in PATHS.items():
+        q, g, y, acc = run_forward(x, w, gd["beta"], dev, path)
+        np.testing.assert_array_equal(q[:, :4], gd["q"])
+        np.testing.assert_array_equal(g, gd["gamma"])
+        np.testing.assert_array_equal(acc, gd["acc"], err_msg=name)
+        np.testing.assert_array_equal(y, np.array(gd["y"], np.float32), err_msg=name)
+
+
+# ------------------------------------------------------------------ quantisation
+
+QUANT_CASES = [
+    ("f32", 1, 2048, "normal_f32"), ("f32", 16, 4096, "normal_f32"), ("f32", 7, 1040, "normal_f32"),
+    ("f32", 3, 16, "normal_f32"), ("f32", 2, 131072, "normal_f32"), ("bf16", 5, 4096, "normal_bf16"),
+    ("f32", 9, 8192, "student_t3"), ("f32", 300, 4160, "normal_f32"), ("bf16", 33, 2576, "normal_bf16"),
+]
+
+
+@pytest.mark.parametrize("dt,M,K,act", QUANT_CASES)
+def test_quant_act_bit_exact(dev, dt, M, K, act):
+    x, _, _ = workloads.random_case(100 + M, M, 1, K, act=act)
+    x = x.copy()
+    x[0, :] = 0  # an all-zero token
+    if dt == "bf16":
+        xf = oracle.bf16_to_f32(x)
+        xd = to_dev(x, dev, torch.bfloat16)
+    else:
+        xf = x
+        xd = to_dev(x, dev)
+    q_ref, g_ref = oracle.quant_act(xf)
+    q, g = bl.quant_act(xd)
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(host(g), g_ref)
+
+
+@pytest.mark.parametrize("M,K,gain_kind", [(1, 2560, "unit"), (512, 2560, "unit"), (6, 1040, "rand"),
+                                           (3, 8192, "unit"), (2, 131072, "rand")])
+def test_rmsnorm_quant(dev, M, K, gain_kind):
+    x, _, _ = workloads.random_case(200 + M, M, 1, K)
+    rng = workloads.rng_for(201, M, K)
+    gain = np.ones(K, np.float32) if gain_kind == "unit" else \
+        rng.uniform(0.5, 2.0, K).astype(np.float32)
+    q_ref, g_ref = oracle.rmsnorm_quant_act(x, gain, 1e-6)
+    q, g = bl.quant_act(to_dev(x, dev), to_dev(gain, dev), 1e-6)
+    np.testing.assert_array_equal(host(q), q_ref)
+    assert_y_close(host(g), g_ref)
+
+
+def test_quant_empty_shapes(dev):
+    q, g = bl.quant_act(torch.zeros((0, 64), device=dev))
+    assert q.shape == (0, 64)
+    g = torch.full((3,), 5.0, device=dev)
+    q = torch.empty((3, 0), dtype=torch.int8, device=dev)
+    bl.quant_act(torch.zeros((3, 0), device=dev), out=(q, g))
+    assert not host(g).any()
+
+
+# ------------------------------------------------------------------ packing
+
+@pytest.mark.parametrize("N,K", [(1, 16), (33, 1040), (64, 4096), (100, 48), (7, 131072)])
+def test_pack_bit_exact(dev, N, K):
+    w = workloads.ternary(workloads.rng_for(300, N, K), N, K)
+    ref, bad_ref = oracle.pack(w)
+    packed, bad = bl.pack_weights(to_dev(w, dev))
+    np.testing.assert_array_equal(host(packed).view(np.uint32), ref)
+    assert int(host(bad)[0]) == bad_ref == 0
+
+
+def test_pack_counts_invalid(dev):
+    w = workloads.ternary(workloads.rng_for(301), 40, 64)
+    w[3, 5] = 2
+    w[39, 63] = -128
+    w[0, 0] = 100
+    ref, bad_ref = oracle.pack(w)
+    packed, bad = bl.pack_weights(to_dev(w, dev), check=False)
+    np.testing.assert_array_equal(host(packed).view(np.uint32), ref)
+    assert int(host(bad)[0]) == bad_ref == 3
+    with pytest.raises(ValueError, match="3 weight entries"):
+        bl.pack_weights(to_dev(w, dev))
+
+
+# ------------------------------------------------------------------ forward, small shapes
+
+FWD_CASES = []
+for _M in (1, 2, 3, 4):
+    for _N, _K in ((1, 16), (17, 48), (1000, 1040), (2048, 2048), (300, 4096)):
+        FWD_CASES.append(("gemv", _M, _N, _K))
+for _M in (1, 5, 16, 17, 33, 64):
+    for _N, _K in ((1, 16), (17, 48), (1000, 1040), (2048, 2048), (300, 4160)):
+        FWD_CASES.append(("skinny", _M, _N, _K))
+for _M in (1, 64, 100, 257):
+    for _N, _K in ((1, 16), (17, 48), (1000, 1040), (130, 2048), (300, 4160)):
+        FWD_CASES.append(("gemm", _M, _N, _K))
+for _M in (1, 8, 31, 40, 96):
+    FWD_CASES.append(("auto", _M, 777, 2112))
+
+
+@pytest.mark.parametrize("path,M,N,K", FWD_CASES)
+def test_forward_parity(dev, path, M, N, K):
+    x, w, beta = workloads.random_case(400 + M * 7 + N, M, N, K,
+                                       table=workloads.TERNARY_HALF_ZERO if N % 2 else
+                                       workloads.TERNARY_UNIFORM)
+    x = x.copy()
+    if M > 2:
+        x[1] = 0.0  # zero token: gamma = 0, y = 0
+    q, g, y, acc = run_forward(x, w, beta, dev, PATHS[path])
+    q_ref, g_ref = oracle.quant_act(x)
+    np.testing.assert_array_equal(q, q_ref)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, beta)
+    np.testing.assert_array_equal(acc, acc_ref)
+    assert_y_close(y, y_ref)
+
+
+def test_paths_agree_bitwise(dev):
+    x, w, beta = workloads.random_case(500, 4, 640, 4096)
+    outs = [run_forward(x, w, beta, dev, p) for p in (bl.PATH_GEMV, bl.PATH_SKINNY, bl.PATH_GEMM)]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o[3], outs[0][3])
+        np.testing.assert_array_equal(o[2], outs[0][2])
+
+
+def test_forward_extreme_values_and_max_k(dev):
+    K = 131072
+    q = np.full((2, K), 127, np.int8)
+    q[1] = -127
+    g = np.array([3.0, 0.5], np.float32)
+    w = np.ones((3, K), np.int8)
+    w[1] = -1
+    w[2, ::2] = 0
+    wp = gpu_pack(w, dev)
+    y_ref, acc_ref = oracle.forward(q, g, w, 0.02)
+    for p in (bl.PATH_GEMV, bl.PATH_SKINNY, bl.PATH_GEMM):
+        y, acc = bl.forward(to_dev(q, dev), to_dev(g, dev), wp, 0.02, path=p, want_acc=True)
+        np.testing.assert_array_equal(host(acc), acc_ref)
+        assert_y_close(host(y), y_ref)
+    assert acc_ref[0, 0] == 127 * K
+
+
+def test_forward_empty_and_k0(dev):
+    y = bl.forward(torch.zeros((0, 32), dtype=torch.int8, device=dev),
+                   torch.zeros((0,), device=dev),
+                   torch.zeros((5, 2), dtype=torch.int32, device=dev), 0.5)
+    assert y.shape == (0, 5)
+    y, acc = bl.forward(torch.zeros((3, 0), dtype=torch.int8, device=dev),
+                        torch.ones((3,), device=dev),
+                        torch.zeros((4, 0), dtype=torch.int32, device=dev), 0.5, want_acc=True)
+    assert not host(y).any() and not host(acc).any()
+
+
+def test_misaligned_tensor_is_rejected(dev):
+    buf = torch.zeros(64 + 1, dtype=torch.int8, device=dev)
+    xq = buf[1:].view(4, 16)
+    with pytest.raises(bl.BitLinearError) as ei:
+        bl.forward(xq, torch.ones(4, device=dev), torch.zeros((2, 1), dtype=torch.int32, device=dev), 1.0)
+    assert ei.value.status == bl.ERR_ALIGN
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _freivalds(acc, q, w, seed):
+    """acc @ v == q @ (w^T v) in exact int64 for a random integer vector v."""
+    v = workloads.rng_for(600, seed).integers(-3, 4, size=w.shape[0]).astype(np.int64)
+    u = np.zeros(w.shape[1], np.int64)
+    for r0 in range(0, w.shape[0], 2048):
+        u += v[r0:r0 + 2048] @ w[r0:r0 + 2048].astype(np.int64)
+    lhs = acc.astype(np.int64) @ v
+    rhs = q.astype(np.int64) @ u
+    np.testing.assert_array_equal(lhs, rhs)
+
+
+def _workload_case(wid, M):
+    wl = workloads.WORKLOADS[wid]
+    x = workloads.workload_activations(wid, M)
+    xf = oracle.bf16_to_f32(x) if wl.act == "normal_bf16" else x
+    return wl, x, xf
+
+
+@pytest.mark.parametrize("wid,M", [(1, 1), (2, 1), (2, 4), (2, 16), (5, 1), (5, 8), (5, 64)])
+def test_workload_full_parity(dev, wid, M):
+    wl, x, xf = _workload_case(wid, M)
+    w = workloads.workload_weights(wid)
+    beta = workloads.workload_beta(wid)
+    q, g, y, acc = run_forward(xf, w, beta, dev)
+    q_ref, g_ref = oracle.quant_act(xf)
+    np.testing.assert_array_equal(q, q_ref)
+    np.testing.assert_array_equal(g, g_ref)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, beta)
+    np.testing.assert_array_equal(acc, acc_ref)
+    assert_y_close(y, y_ref)
+    assert np.abs(acc).max() <= 127 * wl.K
+
+
+@pytest.mark.parametrize("wid,M,rows", [(3, 2048, 48), (5, 512, 24)])
+def test_workload_large_m_sampled(dev, wid, M, rows):
+    wl, x, xf = _workload_case(wid, M)
+    w = workloads.workload_weights(wid)
+    beta = workloads.workload_beta(wid)
+    xd = to_dev(x, dev, torch.bfloat16) if wl.act == "normal_bf16" else to_dev(x, dev)
+    q, g = bl.quant_act(xd)
+    wp = gpu_pack(w, dev)
+    y, acc = bl.forward(q, g, wp, beta, want_acc=True)
+    q, g, y, acc = host(q), host(g), host(y), host(acc)
+    q_ref, g_ref = oracle.quant_act(xf)
+    np.testing.assert_array_equal(q, q_ref)
+    np.testing.assert_array_equal(g, g_ref)
+    # sampled tokens, every output column, one by one through the oracle
+    ms = np.sort(workloads.rng_for(700, wid).choice(M, size=rows, replace=False))
+    ms[0], ms[-1] = 0, M - 1
+    y_ref, acc_ref = oracle.forward(q_ref[ms], g_ref[ms], w, beta)
+    np.testing.assert_array_equal(acc[ms], acc_ref)
+    assert_y_close(y[ms], y_ref)
+    # every output: exact integer checksum and the accumulator bound
+    _freivalds(acc, q_ref, w, wid)
+    assert np.abs(acc).max() <= 127 * wl.K
+    # every output: y within 1e-6 of acc * beta * gamma / 128 (float64)
+    assert_y_close(y, acc.astype(np.float64) * float(beta) * g_ref[:, None].astype(np.float64) / 128.0)
+
+
+# ------------------------------------------------------------------ GLU (workload 4)
+
+@pytest.mark.parametrize("M", [1, 512])
+def test_glu_stagewise(dev, M):
+    wl = workloads.WORKLOADS[4]
+    x = workloads.workload_activations(4, M)
+    wg, wu, wd = workloads.glu_weights()
+    betas = workloads.glu_betas()
+    gain = np.ones(wl.K, np.float32)
+    ref = oracle.glu(x, wg, wu, wd, betas, gain, wl.rms_eps)
+
+    packs = [gpu_pack(w, dev) for w in (wg, wu, wd)]
+    st = bl.glu(to_dev(x, dev), *packs, betas, to_dev(gain, dev), wl.rms_eps, stages=True)
+    st = {k: host(v) for k, v in st.items()}
+
+    np.testing.assert_array_equal(st["q"], ref["q"])
+    assert_y_close(st["gamma"], ref["gamma"])
+    for nm in ("gate", "up"):
+        np.testing.assert_array_equal(st[f"acc_{nm}"], ref[f"acc_{nm}"])
+    for nm in ("gate", "up"):
+        assert_y_close(st[f"y_{nm}"], ref[f"y_{nm}"])
+    # h: float64 SiLU*up rounded once to fp32 on both sides
+    assert_y_close(st["h"], ref["h64"])
+    n_h_diff = int((st["h"] != ref["h"]).sum())
+    # codes of h: equal to the oracle's except where the scaled value sits
+    # within rounding distance of a half-integer
+    t_ref = ref["h"].astype(np.float64) / ref["gamma_h"][:, None].astype(np.float64) * 128.0
+    dist = np.abs(t_ref - (np.floor(t_ref) + 0.5))
+    diff = st["h_q"].astype(np.int32) - ref["h_q"].astype(np.int32)
+    assert np.abs(diff).max() <= 1
+    assert (dist[diff != 0] < 1e-3).all()
+    assert_y_close(st["gamma_h"], ref["gamma_h"])
+    rows_same = (diff == 0).all(axis=1)
+    np.testing.assert_array_equal(st["acc_down"][rows_same], ref["acc_down"][rows_same])
+    if not rows_same.all():
+        nd = np.abs(diff).sum(axis=1)
+        assert (np.abs(st["acc_down"] - ref["acc_down"]).max(axis=1) <= nd).all()
+    print(f"GLU M={M}: h differs from fl32(h_ref) at {n_h_diff} entries, "
+          f"h_q codes differ at {int((diff != 0).sum())}")
+
+
+def test_glu_down_projection_on_oracle_codes(dev):
+    """The down projection (K = 6912) on the oracle's own requantised h."""
+    wl = workloads.WORKLOADS[4]
+    x = workloads.workload_activations(4, 512)
+    wg, wu, wd = workloads.glu_weights()
+    betas = workloads.glu_betas()
+    ref = oracle.glu(x, wg, wu, wd, betas, np.ones(wl.K, np.float32), wl.rms_eps)
+    y, acc = bl.forward(to_dev(ref["h_q"], dev), to_dev(ref["gamma_h"], dev), gpu_pack(wd, dev),
+                        betas[2], want_acc=True)
+    np.testing.assert_array_equal(host(acc), ref["acc_down"])
+    assert_y_close(host(y), ref["y"])
