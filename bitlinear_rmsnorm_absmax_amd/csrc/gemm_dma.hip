@@ -1,0 +1,250 @@
+// Prefill GEMM on int8 MFMA with an LDS ring fed by direct global->LDS loads
+// (K a multiple of 128).
+//
+// Arithmetic as in the other forward kernels (unite.ai BitNet.cpp article, 3.
+// BitLinear-Betrieb): v_mfma_i32_32x32x32_i8 on the 2-bit codes c = w + 1 and
+// acc = D - S_m, S_m the sum of the token's int8 activations.
+//
+// Pipeline: the activation tile (BM rows x 128 bytes) and packed weight tile
+// (BN columns x 8 words) of each K step are copied straight from global
+// memory into one of STAGES LDS buffers with global_load_lds_dwordx4, so the
+// copies occupy no registers and
+// STAGES-1 steps are in flight while one is multiplied.  Every wave issues the
+// same number of copies each step and waits for its own copies with an
+// explicit vmcnt; the barrier that follows makes the whole step visible and
+// also tells every wave that the buffer about to be refilled has been read.
+// Past the last step the copies re-read the last step into the free buffer,
+// so the counts stay uniform.  Each lane's 16-byte copy lands at
+// M0 + 16 * lane, so the global address of a lane is chosen to put the right
+// chunk at its swizzled LDS position.
+//
+// Layout and operand mapping follow gemm_mfma.hip: activation rows of 128
+// bytes with chunk c stored at c ^ ((row & 7) ^ ((row >> 3) & 1)); weight
+// columns of 32 bytes with halves swapped when bit 3 of the column is set;
+// MFMA kk (0..3) of lane half h covers packed word 4h + kk.  S_m is summed
+// from the activation fragments the waves already hold, the K range split
+// between the WN waves that share a row.
+#include "device_common.h"
+#include "internal.h"
+
+namespace bl {
+namespace {
+
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int BK = 128;
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int bswz(int col, int h) { return h ^ ((col >> 3) & 1); }
+
+// Copy 16 bytes per lane from global memory straight into LDS at
+// lds_wave_base + 16 * lane (the base is wave-uniform and goes to M0).
+// The builtin only exists in the device pass; the host pass compiles the
+// kernel to a launch stub and must not see it.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                     16, 0, 0);
+#endif
+}
+
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt any
+constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 0xF) << 8);
+}
+
+template <int WM, int WN, int TM, int TN, int STAGES>
+struct DCfg {
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int BM = WM * TM * 32;
+    static constexpr int BN = WN * TN * 32;
+    static constexpr int kABytes = BM * BK;        // activation bytes per stage
+    static constexpr int kBBytes = BN * 32;        // packed weight bytes per stage
+    static constexpr int kStageBytes = kABytes + kBBytes;
+    static constexpr int kAInstr = kABytes / 1024 / kWaves;  // 16-byte copies per wave per step
+    static constexpr int kBInstr = kBBytes / 1024 / kWaves;  // 16-byte copies per wave per step
+    static constexpr int kPerStep = kAInstr + kBInstr;
+    static_assert(kABytes % (1024 * kWaves) == 0, "activation copies divide the waves");
+    static_assert(kBBytes % (1024 * kWaves) == 0, "weight copies divide the waves");
+};
+
+template <int WM, int WN, int TM, int TN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M,
+                     int K, const uint32_t* __restrict__ wp, int N, float beta,
+                     float* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
+                     int tiles_total) {
+    using C = DCfg<WM, WN, TM, TN, STAGES>;
+    __shared__ __attribute__((aligned(16))) char lds[STAGES * C::kStageBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wv = tid / kWave;
+    const int wm = wv / WN, wn = wv % WN;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    int b = blockIdx.x;
+    const int full = (tiles_total / kXcds) * kXcds;
+    if (b < full) b = (b % kXcds) * (full / kXcds) + b / kXcds;
+    const int m0 = (b / tiles_n) * C::BM;
+    const int n0 = (b % tiles_n) * C::BN;
+    const int WR = K >> 4;
+    const int KT = K / BK;
+
+    // per-lane source offsets of this wave's copies at step 0 (32-bit, from
+    // the block's first row / column); rows and columns past the matrix are
+    // clamped onto its last row / column (their products are never stored)
+    const int8_t* abase = xq + (int64_t)m0 * K;
+    const uint32_t* bbase = wp + (int64_t)n0 * WR;
+    uint32_t aoff[C::kAInstr];
+#pragma unroll
+    for (int i = 0; i < C::kAInstr; ++i) {
+        const int q = wv * C::kAInstr + i;
+        const int row = 8 * q + lane / 8;
+        const int lchunk = (lane % 8) ^ swz(row);
+        aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + 16u * lchunk;
+    }
+    uint32_t boff[C::kBInstr];
+#pragma unroll
+    for (int i = 0; i < C::kBInstr; ++i) {
+        const int q = wv * C::kBInstr + i;
+        const int col = 32 * q + lane / 2;
+        const int lhalf = (lane % 2) ^ ((col >> 3) & 1);
+        boff[i] = (uint32_t)(min(n0 + col, N - 1) - n0) * (uint32_t)WR + 4u * lhalf;
+    }
+
+    auto issue = [&](int kt, int buf) {
+        char* stage = lds + buf * C::kStageBytes;
+        const int8_t* a_step = abase + (int64_t)kt * BK;
+        const uint32_t* b_step = bbase + (int64_t)kt * (BK / 16);
+#pragma unroll
+        for (int i = 0; i < C::kAInstr; ++i)
+            copy16_to_lds(a_step + aoff[i], stage + 1024 * (wv * C::kAInstr + i));
+#pragma unroll
+        for (int i = 0; i < C::kBInstr; ++i)
+            copy16_to_lds(b_step + boff[i], stage + C::kABytes + 1024 * (wv * C::kBInstr + i));
+    };
+
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[i][t] = v16i{};
+    int s_part[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) s_part[i] = 0;
+
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p) issue(min(p, KT - 1), p);
+
+    for (int kt = 0; kt < KT; ++kt) {
+        // this wave's copies of step kt are done (later steps may be in flight)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((STAGES - 2) * C::kPerStep, 0));
+        __builtin_amdgcn_s_barrier();
+        issue(min(kt + STAGES - 1, KT - 1), (kt + STAGES - 1) % STAGES);
+
+        const char* stage = lds + (kt % STAGES) * C::kStageBytes;
+        const v4i* As = reinterpret_cast<const v4i*>(stage);
+        const v4u* Bs = reinterpret_cast<const v4u*>(stage + C::kABytes);
+        // all LDS operand reads of the step first, so their latency overlaps
+        // the unpacking and the first MFMAs
+        v4u wq[TN];
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+            const int col = wn * TN * 32 + 32 * t + l32;
+            wq[t] = Bs[col * 2 + bswz(col, h)];
+        }
+        v4i af[4][TM];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int r = wm * TM * 32 + 32 * i + l32;
+                af[kk][i] = As[r * 8 + ((4 * h + kk) ^ swz(r))];
+            }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            v4i bf[TN];
+#pragma unroll
+            for (int t = 0; t < TN; ++t) bf[t] = unpack_codes(wq[t][kk]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                if (kk % WN == wn) s_part[i] = byte_sum16(af[kk][i], s_part[i]);
+#pragma unroll
+                for (int t = 0; t < TN; ++t)
+                    acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kk][i], bf[t], acc[i][t], 0, 0, 0);
+            }
+        }
+    }
+    // every copy (including the re-reads past the end) has landed before the
+    // LDS is reused below or released
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __syncthreads();
+
+    int* Sp = reinterpret_cast<int*>(lds);                   // [WN][BM]
+    float* Ssc = reinterpret_cast<float*>(lds) + WN * C::BM;  // [BM]
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int sv = s_part[i] + __shfl_xor(s_part[i], 32, kWave);
+        if (h == 0) Sp[wn * C::BM + wm * TM * 32 + 32 * i + l32] = sv;
+    }
+    for (int r = tid; r < C::BM; r += C::kThreads) {
+        const int row = m0 + r;
+        Ssc[r] = (row < M) ? out_scale(beta, gamma[row]) : 0.f;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int rl = wm * TM * 32 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+            const int row = m0 + rl;
+            if (row >= M) continue;
+            const float sc = Ssc[rl];
+            int sm = 0;
+#pragma unroll
+            for (int w = 0; w < WN; ++w) sm += Sp[w * C::BM + rl];
+#pragma unroll
+            for (int t = 0; t < TN; ++t) {
+                const int col = n0 + wn * TN * 32 + 32 * t + l32;
+                if (col >= N) continue;
+                const int a = acc[i][t][v] - sm;
+                const int64_t o = (int64_t)row * N + col;
+                y[o] = (float)a * sc;
+                if (acc_out) acc_out[o] = a;
+            }
+        }
+    }
+}
+
+template <int WM, int WN, int TM, int TN, int STAGES>
+hipError_t launch_dcfg(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
+                       int N, float beta, float* y, int32_t* acc, hipStream_t s) {
+    using C = DCfg<WM, WN, TM, TN, STAGES>;
+    const int tm = (M + C::BM - 1) / C::BM;
+    const int tn = (N + C::BN - 1) / C::BN;
+    const int64_t total = (int64_t)tm * tn;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemm_dma_kernel<WM, WN, TM, TN, STAGES><<<dim3((unsigned)total), dim3(C::kThreads), 0, s>>>(
+        xq, gamma, M, K, wp, N, beta, y, acc, tn, (int)total);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_dma_supports(int M, int K, int N) { return K % BK == 0 && K > 0 && M > 0 && N > 0; }
+
+hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
+                           const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
+                           hipStream_t s) {
+    const int64_t big_tiles = (int64_t)((M + 255) / 256) * ((N + 127) / 128);
+    if (M >= 256 && big_tiles >= 512)
+        return launch_dcfg<2, 2, 2, 4, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    return launch_dcfg<2, 2, 2, 2, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+}
+
+}  // namespace bl
