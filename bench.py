@@ -3,21 +3,22 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 
-A step is one pass of the path over one batch of synthetic input: per token
-count M of the workload, the activation quantisation (bitlinear_quant_act)
-followed by the ternary product with rescale (bitlinear_forward); for the GLU
-workload the whole RMSNorm+quant -> gate -> up -> SiLU*up+requant -> down
-chain.  Weight packing is offline and outside the step.
+A step is one pass of the path over one batch of synthetic input: for every
+token count M of the workload, the activation quantisation
+(bitlinear_quant_act) followed by the ternary product with rescale
+(bitlinear_forward); for the GLU workload the whole RMSNorm+quant -> gate ->
+up -> SiLU*up+requant -> down chain.  Weight packing is offline and outside
+the step.
 
-Inputs are seeded synthetic draws (workloads.py) resident in HBM before the
+Inputs are seeded synthetic draws (workloads.py), resident in HBM before the
 timed region.  The packed weights rotate through at least 512 MB of copies so
 that consecutive steps cannot be served from the 256 MB Infinity Cache.
-Timed steps are replays of HIP graphs (one per weight copy) so host launch
-overhead does not pace the GPU; a second pass launches the same steps eagerly
-with HIP events around every kernel call on its stream to obtain each
-kernel's average duration for the roofline figure.
+Timed steps are replays of HIP graphs (one per weight copy), so host launch
+overhead does not pace the GPU.  Per-call kernel durations come from a second
+pass that launches each call of the step back to back `steps` times between
+two HIP events on its stream; the dominant forward call gives the roofline.
 
-Prints ONE JSON line (rank 0, N=1).
+Prints ONE JSON line.
 """
 
 from __future__ import annotations
@@ -57,6 +58,58 @@ def parse():
     return ap.parse_args()
 
 
+def forward_kernel(M: int, K: int) -> str:
+    """Kernel that bitlinear_forward picks for M (the library's dispatch)."""
+    if M <= 4:
+        return "gemv_valu_kernel"
+    if M <= 32:
+        return "skinny_mfma_kernel"
+    return "gemm_dma_kernel" if K % 128 == 0 else "gemm_mfma_kernel"
+
+
+# ----------------------------------------------------------------------------- timers
+
+class RunAll:
+    """Runs every call; records how often each call occurs per step."""
+
+    def __init__(self):
+        self.calls = {}
+        self.info = {}
+
+    def __call__(self, name, M=0, N=0, K=0, wbytes=0):
+        self.calls[name] = self.calls.get(name, 0) + 1
+        if wbytes:
+            # algorithmic bytes of one forward launch: packed W + x_q + gamma + y
+            self.info[name] = dict(alg_bytes=wbytes + M * K + 4 * M + 4 * M * N,
+                                   ops=2 * M * N * K, wbytes=wbytes, M=M, N=N, K=K,
+                                   kernel=forward_kernel(M, K))
+        return True
+
+
+class RunOne:
+    """Runs only the call `name`; the first run records the start event."""
+
+    def __init__(self, torch, name):
+        self.torch = torch
+        self.name = name
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
+        self.started = False
+
+    def __call__(self, name, *a, **kw):
+        if name != self.name:
+            return False
+        if not self.started:
+            self.e0.record(self.torch.cuda.current_stream())
+            self.started = True
+        return True
+
+    def avg_us(self, launches):
+        self.e1.record(self.torch.cuda.current_stream())
+        self.torch.cuda.synchronize()
+        return self.e0.elapsed_time(self.e1) * 1e3 / launches
+
+
 # ----------------------------------------------------------------------------- plan
 
 class Layer:
@@ -74,12 +127,11 @@ class Layer:
 
 
 def build_plan(args, torch, bl, dev):
-    """Returns (ops, meta): ops(step_idx, timer) launches one step."""
+    """Returns (ops, meta, keepalive): ops(step_idx, timer) launches one step."""
     wid = args.workload
     wl = workloads.WORKLOADS[wid]
     rotate = not args.no_rotate
     lib = bl.lib
-    F32, BF16 = bl.F32, bl.BF16
 
     def stream():
         return torch.cuda.current_stream(dev).cuda_stream
@@ -102,34 +154,37 @@ def build_plan(args, torch, bl, dev):
             bufs.append(dict(
                 M=M, x=x, q=torch.empty((M, D), dtype=torch.int8, device=dev),
                 g=torch.empty(M, device=dev), yg=torch.empty((M, Fh), device=dev),
-                yu=torch.empty((M, Fh), device=dev), hq=torch.empty((M, Fh), dtype=torch.int8, device=dev),
+                yu=torch.empty((M, Fh), device=dev),
+                hq=torch.empty((M, Fh), dtype=torch.int8, device=dev),
                 gh=torch.empty(M, device=dev), y=torch.empty((M, D), device=dev)))
 
-        def ops(step, timer):
+        def ops(step, run):
             c = step % ncopy
             for b in bufs:
                 M = b["M"]
-                with timer("quant_act_rms"):
-                    check(lib.bitlinear_quant_act(b["x"].data_ptr(), F32, M, D, gain.data_ptr(),
-                                                  wl.rms_eps, b["q"].data_ptr(), b["g"].data_ptr(), stream()))
-                for L, out in ((layers[0], b["yg"]), (layers[1], b["yu"])):
-                    with timer(f"forward_M{M}", L.wbytes, M, L.N, L.K):
+                if run(f"quant_act_rms_M{M}"):
+                    check(lib.bitlinear_quant_act(b["x"].data_ptr(), bl.F32, M, D, gain.data_ptr(),
+                                                  wl.rms_eps, b["q"].data_ptr(), b["g"].data_ptr(),
+                                                  stream()))
+                for nm, L, out in (("gate", layers[0], b["yg"]), ("up", layers[1], b["yu"])):
+                    if run(f"forward_{nm}_M{M}", M, L.N, L.K, L.wbytes):
                         check(lib.bitlinear_forward(b["q"].data_ptr(), b["g"].data_ptr(), M, D,
                                                     L.copies[c].data_ptr(), Fh, L.beta,
                                                     out.data_ptr(), None, stream()))
-                with timer("silu_mul_quant"):
+                if run(f"silu_mul_quant_M{M}"):
                     check(lib.bitlinear_silu_mul_quant(b["yg"].data_ptr(), b["yu"].data_ptr(), M, Fh,
                                                        None, b["hq"].data_ptr(), b["gh"].data_ptr(),
                                                        stream()))
                 L = layers[2]
-                with timer(f"forward_M{M}", L.wbytes, M, L.N, L.K):
+                if run(f"forward_down_M{M}", M, L.N, L.K, L.wbytes):
                     check(lib.bitlinear_forward(b["hq"].data_ptr(), b["gh"].data_ptr(), M, Fh,
                                                 L.copies[c].data_ptr(), D, L.beta, b["y"].data_ptr(),
                                                 None, stream()))
 
         meta.update(weight_bytes_per_step=sum(L.wbytes for L in layers) * len(wl.ms),
-                    weight_copies=ncopy, ops_per_step=sum(2 * M * (2 * D * Fh + Fh * D) for M in wl.ms))
-        return ops, meta, (layers, bufs)
+                    weight_copies=ncopy,
+                    ops_per_step=sum(2 * M * (2 * D * Fh + Fh * D) for M in wl.ms))
+        return ops, meta, (layers, bufs, gain)
 
     w = workloads.workload_weights(wid)
     L = Layer(torch, bl, dev, w, workloads.workload_beta(wid), rotate)
@@ -138,79 +193,26 @@ def build_plan(args, torch, bl, dev):
     for M in wl.ms:
         xa = workloads.workload_activations(wid, M)
         if wl.act == "normal_bf16":
-            x = torch.from_numpy(xa).to(dev).view(torch.bfloat16)
-            dt = BF16
+            x, dt = torch.from_numpy(xa).to(dev).view(torch.bfloat16), bl.BF16
         else:
-            x = torch.from_numpy(xa).to(dev)
-            dt = F32
+            x, dt = torch.from_numpy(xa).to(dev), bl.F32
         bufs.append(dict(M=M, x=x, dt=dt, q=torch.empty((M, K), dtype=torch.int8, device=dev),
                          g=torch.empty(M, device=dev), y=torch.empty((M, N), device=dev)))
 
-    def ops(step, timer):
+    def ops(step, run):
         wptr = L.copies[step % len(L.copies)].data_ptr()
         for b in bufs:
             M = b["M"]
-            with timer("quant_act"):
+            if run(f"quant_act_M{M}"):
                 check(lib.bitlinear_quant_act(b["x"].data_ptr(), b["dt"], M, K, None, 0.0,
                                               b["q"].data_ptr(), b["g"].data_ptr(), stream()))
-            with timer(f"forward_M{M}", L.wbytes, M, N, K):
+            if run(f"forward_M{M}", M, N, K, L.wbytes):
                 check(lib.bitlinear_forward(b["q"].data_ptr(), b["g"].data_ptr(), M, K, wptr, N,
                                             L.beta, b["y"].data_ptr(), None, stream()))
 
     meta.update(weight_bytes_per_step=L.wbytes * len(wl.ms), weight_copies=len(L.copies),
                 ops_per_step=sum(2 * M * N * K for M in wl.ms))
     return ops, meta, (L, bufs)
-
-
-# ----------------------------------------------------------------------------- timing
-
-class NullTimer:
-    def __call__(self, name, *a):
-        return self
-
-    def __enter__(self):
-        return self
-
-    def __exit__(self, *a):
-        return False
-
-
-class EventTimer:
-    """HIP events on the launching stream around every call."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pending = []
-        self.info = {}
-
-    def __call__(self, name, wbytes=0, M=0, N=0, K=0):
-        self._name = name
-        if wbytes:
-            # algorithmic bytes of one forward launch: packed W + x_q + gamma + y
-            self.info[name] = dict(alg_bytes=wbytes + M * K + 4 * M + 4 * M * N,
-                                   ops=2 * M * N * K, wbytes=wbytes)
-        return self
-
-    def __enter__(self):
-        s = self.torch.cuda.current_stream()
-        self._e0 = self.torch.cuda.Event(enable_timing=True)
-        self._e0.record(s)
-        return self
-
-    def __exit__(self, *a):
-        e1 = self.torch.cuda.Event(enable_timing=True)
-        e1.record(self.torch.cuda.current_stream())
-        self.pending.append((self._name, self._e0, e1))
-        return False
-
-    def summary(self):
-        self.torch.cuda.synchronize()
-        out = {}
-        for name, e0, e1 in self.pending:
-            d = out.setdefault(name, [])
-            d.append(e0.elapsed_time(e1) * 1e3)  # us
-        return {k: dict(n=len(v), avg_us=float(np.mean(v)), med_us=float(np.median(v)),
-                        total_us=float(np.sum(v)), **self.info.get(k, {})) for k, v in out.items()}
 
 
 # ----------------------------------------------------------------------------- traffic
@@ -224,16 +226,16 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_name: str):
-    """HBM bytes per launch of the dominant kernel from a committed counter
-    summary (profiles/traffic_<workload>.md), only if it was taken on the
-    current kernel sources."""
+def read_traffic(workload_name: str, call: str):
+    """HBM bytes per launch of `call` from the committed counter summary
+    profiles/traffic_<workload>.md, only if it was taken on the current kernel
+    sources (else None)."""
     path = os.path.join(PROFILES, f"traffic_{workload_name}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_src = re.search(r"source_digest:\s*(\w+)", text)
-    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_val = re.search(rf"traffic_bytes_per_launch\[{re.escape(call)}\]:\s*([0-9.eE+]+)", text)
     if not m_src or not m_val or m_src.group(1) != kernel_source_digest():
         return None
     return float(m_val.group(1))
@@ -265,14 +267,13 @@ def cpu_baseline(args, seconds: float):
         for M in wl.ms:
             x = workloads.workload_activations(wid, M)
             xs.append(oracle.bf16_to_f32(x) if wl.act == "normal_bf16" else x)
-        wbytes = w.size // 4 * len(wl.ms)
         rows = w.shape[0]
         # large workloads: a bounded slice of output rows (same K, same M sweep)
-        est = sum(x.shape[0] for x in xs) * w.size * 1e-9  # ~1 ns per MAC and thread
+        est = sum(x.shape[0] for x in xs) * w.size * 1.5e-9  # ~1.5 ns per MAC and thread
         if est / max(oracle.num_threads(), 1) > seconds:
             rows = max(64, int(rows * seconds * oracle.num_threads() / est / 3))
             w = np.ascontiguousarray(w[:rows])
-            wbytes = w.size // 4 * len(wl.ms)
+        wbytes = w.size // 4 * len(wl.ms)
 
         def step():
             for x in xs:
@@ -310,23 +311,21 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     ops, meta, keep = build_plan(args, torch, bl, dev)
+    rec = RunAll()
+    ops(0, rec)  # first launch of every kernel; records the calls of a step
     torch.cuda.synchronize()
     print(f"# workload {meta['workload']}: M={meta['M']} K={meta['K']} N={meta['N']}, "
           f"{meta['weight_copies']} weight copies", file=sys.stderr, flush=True)
 
     ncopy = meta["weight_copies"]
-    null = NullTimer()
     graphs = None
     if not args.eager:
-        # one graph per weight copy; step i replays graph i % ncopy
-        ops(0, null)  # first eager launch initialises every kernel
-        torch.cuda.synchronize()
         graphs = []
         s = torch.cuda.Stream(device=dev)
         for c in range(ncopy):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=s):
-                ops(c, null)
+                ops(c, RunAll())
             graphs.append(g)
         torch.cuda.synchronize()
 
@@ -334,63 +333,59 @@ def main():
         if graphs is not None:
             graphs[i % ncopy].replay()
         else:
-            ops(i, null)
+            ops(i, RunAll())
 
     for i in range(args.warmup):
         run(i)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
         run(args.warmup + i)
     e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
-    print(f"# timed {args.steps} steps: {ms_step * 1e3:.2f} us/step (wall {wall * 1e3 / args.steps:.2f})",
-          file=sys.stderr, flush=True)
+    print(f"# timed {args.steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
-    # per-kernel durations: the same steps launched eagerly, events on the stream
-    timer = EventTimer(torch)
-    for i in range(args.steps):
-        ops(args.warmup + i, timer)
-    kern = timer.summary()
+    # per-call durations: each call launched back to back `steps` times
+    kern = {}
+    for name, per_step in rec.calls.items():
+        t = RunOne(torch, name)
+        for i in range(args.steps):
+            ops(args.warmup + i, t)
+        kern[name] = dict(avg_us=t.avg_us(args.steps * per_step), per_step=per_step,
+                          **rec.info.get(name, {}))
     print("# per-call GPU time (us): " + ", ".join(f"{k} {v['avg_us']:.2f}" for k, v in kern.items()),
           file=sys.stderr, flush=True)
 
-    fwd = {k: v for k, v in kern.items() if k.startswith("forward_")}
-    dom_name = max(fwd, key=lambda k: fwd[k]["total_us"])
-    # roofline over every forward launch of the step (same kernel family)
-    alg = sum(v["alg_bytes"] * v["n"] for v in fwd.values())
-    dur = sum(v["total_us"] for v in fwd.values())
-    achieved = alg / (dur * 1e-6) / 1e9
-    wl = workloads.WORKLOADS[args.workload]
-    mfma_bound = max(wl.ms) >= 512
-    value = meta["weight_bytes_per_step"] / (ms_step * 1e-3) / 1e9
-    traffic = read_traffic(meta["workload"])
-    roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                kernel="bitlinear_forward (" + ", ".join(sorted(fwd)) + ")",
-                avg_launch_us=round(dur / sum(v["n"] for v in fwd.values()), 3))
-    if mfma_bound:
-        ops_all = sum(v["ops"] * v["n"] for v in fwd.values())
-        tops = ops_all / (dur * 1e-6) / 1e12
+    fwd = {k: v for k, v in kern.items() if "alg_bytes" in v}
+    dom = max(fwd, key=lambda k: fwd[k]["avg_us"] * fwd[k]["per_step"])
+    d = fwd[dom]
+    traffic = read_traffic(meta["workload"], dom)
+    if d["M"] >= 512:
+        tops = d["ops"] / (d["avg_us"] * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(tops, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
-                    frac=round(tops / INT8_PEAK_TOPS, 4), traffic=traffic,
-                    kernel="bitlinear_forward (" + ", ".join(sorted(fwd)) + ")",
-                    avg_launch_us=round(dur / sum(v["n"] for v in fwd.values()), 3))
+                    frac=round(tops / INT8_PEAK_TOPS, 4), traffic=traffic)
+    else:
+        gbs = d["alg_bytes"] / (d["avg_us"] * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic)
+    roof.update(call=dom, kernel=d["kernel"], avg_launch_us=round(d["avg_us"], 3),
+                alg_bytes_per_launch=d["alg_bytes"], ops_per_launch=d["ops"])
 
-    cpu = None
-    if args.cpu_seconds > 0:
-        cpu = cpu_baseline(args, args.cpu_seconds)
+    cpu = cpu_baseline(args, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
-    per_call = {k: dict(avg_us=round(v["avg_us"], 3),
-                        **({"packed_w_GBs": round(v["wbytes"] / (v["avg_us"] * 1e-6) / 1e9, 1),
-                            "int8_eq_TOPS": round(v["ops"] / (v["avg_us"] * 1e-6) / 1e12, 2)}
-                           if "wbytes" in v else {}))
-                for k, v in kern.items()}
+    value = meta["weight_bytes_per_step"] / (ms_step * 1e-3) / 1e9
+    per_call = {}
+    for k, v in kern.items():
+        e = dict(avg_us=round(v["avg_us"], 3), per_step=v["per_step"])
+        if "alg_bytes" in v:
+            e.update(kernel=v["kernel"],
+                     packed_w_GBs=round(v["wbytes"] / (v["avg_us"] * 1e-6) / 1e9, 1),
+                     alg_GBs=round(v["alg_bytes"] / (v["avg_us"] * 1e-6) / 1e9, 1),
+                     int8_eq_TOPS=round(v["ops"] / (v["avg_us"] * 1e-6) / 1e12, 2))
+        per_call[k] = e
     line = {
         "metric": "BitLinear ternary GEMV/GEMM: packed-W GB/s (% HBM peak), int8-eq TOPS",
         "value": round(value, 2),

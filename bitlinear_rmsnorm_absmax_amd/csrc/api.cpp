@@ -90,7 +90,8 @@ bitlinear_status_t forward_impl(const char* fn, const int8_t* x_q, const float* 
     if (!any_out) return ok();
     if (K == 0) return from_hip(bl::launch_fill_zero(y, acc, M * N, stream), fn);
 
-    if (path == BITLINEAR_PATH_AUTO) path = (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
+    if (path == BITLINEAR_PATH_AUTO)
+        path = (M <= 4) ? BITLINEAR_PATH_GEMV : (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
     const int m = (int)M, n = (int)N, k = (int)K;
     hipError_t e;
     switch (path) {

@@ -39,12 +39,14 @@ __global__ __launch_bounds__(kGvThreads) void gemv_valu_kernel(
     const uint32_t* __restrict__ wp, int N, float beta, float* __restrict__ y,
     int32_t* __restrict__ acc_out) {
     const int lane = threadIdx.x % kWave;
-    const int wv = threadIdx.x / kWave;
-    const int n0 = (blockIdx.x * kGvWaves + wv) * R;
-    if (n0 >= N) return;
+    // wave index made scalar so row addressing stays on the SALU
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n0 = (blockIdx.x * kGvWaves + wv) * R;  // waves past N load and store nothing
     const int WR = K >> 4;
     const int units = (WR + 3) >> 2;
     const bool aligned = (WR & 3) == 0;
+    const bool full = aligned && n0 + R <= N;
+    const uint32_t* wrow = wp + (int64_t)n0 * WR;  // first weight row of the wave
 
     int part[R][MR];
 #pragma unroll
@@ -57,6 +59,32 @@ __global__ __launch_bounds__(kGvThreads) void gemv_valu_kernel(
 
     for (int u = lane; u < units; u += kWave) {
         const int wb = 4 * u;
+        // weight loads first: R rows x 16 bytes, rows WR words apart
+        uint32_t w[R][4];
+        if (full) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const v4u v = __builtin_nontemporal_load(
+                    reinterpret_cast<const v4u*>(wrow + (uint32_t)(r * WR + wb)));
+                w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) w[r][s] = 0u;
+                if (n0 + r < N) {
+                    const uint32_t* p = wrow + (uint32_t)(r * WR + wb);
+                    if (aligned) {
+                        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+                        w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
+                    } else {
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) w[r][s] = (wb + s < WR) ? p[s] : 0u;
+                    }
+                }
+            }
+        }
         v4i a[MR][4];
 #pragma unroll
         for (int m = 0; m < MR; ++m)
@@ -70,21 +98,9 @@ __global__ __launch_bounds__(kGvThreads) void gemv_valu_kernel(
             }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int n = n0 + r;
-            uint32_t w[4] = {0u, 0u, 0u, 0u};
-            if (n < N) {
-                const uint32_t* p = wp + (int64_t)n * WR + wb;
-                if (aligned) {
-                    v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-                    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-                } else {
-#pragma unroll
-                    for (int s = 0; s < 4; ++s) w[s] = (wb + s < WR) ? p[s] : 0u;
-                }
-            }
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const v4i c = unpack_codes(w[s]);
+                const v4i c = unpack_codes(w[r][s]);
 #pragma unroll
                 for (int m = 0; m < MR; ++m) {
                     int d = part[r][m];
@@ -145,8 +161,8 @@ hipError_t launch_gv(const int8_t* xq, const float* gamma, int M, int K, const u
 hipError_t launch_gemv_valu(const int8_t* xq, const float* gamma, int M, int K,
                             const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                             hipStream_t s) {
-    if (M <= 1) return launch_gv<1, 8>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    if (M <= 2) return launch_gv<2, 8>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (M <= 1) return launch_gv<1, 4>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (M <= 2) return launch_gv<2, 4>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     return launch_gv<4, 4>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
 

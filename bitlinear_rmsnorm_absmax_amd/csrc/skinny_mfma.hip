@@ -39,7 +39,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_mfma_kernel(
     __shared__ int red[WAVES][MT * NT][4][kWave];
 
     const int lane = threadIdx.x % kWave;
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int j = lane & 15;  // A row / B column within a 16-tile
     const int g = lane >> 4;  // K block of the lane inside one MFMA
     const int WR = K >> 4;    // packed words per weight row
