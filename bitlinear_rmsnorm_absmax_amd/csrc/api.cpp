@@ -91,7 +91,7 @@ bitlinear_status_t forward_impl(const char* fn, const int8_t* x_q, const float* 
     if (K == 0) return from_hip(bl::launch_fill_zero(y, acc, M * N, stream), fn);
 
     if (path == BITLINEAR_PATH_AUTO)
-        path = (M <= 4) ? BITLINEAR_PATH_GEMV : (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
+        path = (M <= 2) ? BITLINEAR_PATH_GEMV : (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
     const int m = (int)M, n = (int)N, k = (int)K;
     hipError_t e;
     switch (path) {

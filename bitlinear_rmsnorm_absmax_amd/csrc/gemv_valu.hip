@@ -9,7 +9,8 @@
 //
 // A wave owns R consecutive weight rows.  Lane l streams the 16-byte units
 // (4 packed words = 64 weights) u = l, l+64, ... of each row, so one wave-wide
-// load covers 1 KB of a row contiguously.  The activation unit of the lane
+// load covers 1 KB of a row contiguously; the loads of all R rows are issued
+// before the first dot product.  The activation unit of the lane
 // (64 int8 per token) is loaded once per unit and reused by the R rows.  The
 // R x M lane partials are reduced across the wave with DPP row operations
 // (quad permutes and row rotations inside each 16-lane row) followed by four
@@ -33,7 +34,7 @@ __device__ __forceinline__ int wave_reduce_dpp(int v) {
            __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
-template <int MR, int R>
+template <int MR, int R, int U>
 __global__ __launch_bounds__(kGvThreads) void gemv_valu_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
     const uint32_t* __restrict__ wp, int N, float beta, float* __restrict__ y,
@@ -57,58 +58,68 @@ __global__ __launch_bounds__(kGvThreads) void gemv_valu_kernel(
 #pragma unroll
     for (int m = 0; m < MR; ++m) spart[m] = 0;
 
-    for (int u = lane; u < units; u += kWave) {
-        const int wb = 4 * u;
-        // weight loads first: R rows x 16 bytes, rows WR words apart
-        uint32_t w[R][4];
-        if (full) {
+    // U units per lane are loaded together (all U*R weight loads in flight
+    // before the first dot product); longer rows loop over such batches
+    for (int ub = lane; ub < units; ub += U * kWave) {
+        uint32_t w[U][R][4];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const v4u v = __builtin_nontemporal_load(
-                    reinterpret_cast<const v4u*>(wrow + (uint32_t)(r * WR + wb)));
-                w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
-            }
-        } else {
+        for (int i = 0; i < U; ++i) {
+            const int wb = 4 * (ub + i * kWave);
+            const bool live = ub + i * kWave < units;
+            if (full && live) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
+                for (int r = 0; r < R; ++r) {
+                    const v4u v = __builtin_nontemporal_load(
+                        reinterpret_cast<const v4u*>(wrow + (uint32_t)(r * WR + wb)));
+                    w[i][r][0] = v.x; w[i][r][1] = v.y; w[i][r][2] = v.z; w[i][r][3] = v.w;
+                }
+            } else {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) w[r][s] = 0u;
-                if (n0 + r < N) {
-                    const uint32_t* p = wrow + (uint32_t)(r * WR + wb);
-                    if (aligned) {
-                        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
-                        w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
-                    } else {
+                for (int r = 0; r < R; ++r) {
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) w[r][s] = (wb + s < WR) ? p[s] : 0u;
+                    for (int s = 0; s < 4; ++s) w[i][r][s] = 0u;
+                    if (live && n0 + r < N) {
+                        const uint32_t* p = wrow + (uint32_t)(r * WR + wb);
+                        if (aligned) {
+                            const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+                            w[i][r][0] = v.x; w[i][r][1] = v.y; w[i][r][2] = v.z; w[i][r][3] = v.w;
+                        } else {
+#pragma unroll
+                            for (int s = 0; s < 4; ++s) w[i][r][s] = (wb + s < WR) ? p[s] : 0u;
+                        }
                     }
                 }
             }
         }
-        v4i a[MR][4];
 #pragma unroll
-        for (int m = 0; m < MR; ++m)
+        for (int i = 0; i < U; ++i) {
+            const int wb = 4 * (ub + i * kWave);
+            const bool live = ub + i * kWave < units;
+            v4i a[MR][4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                if (m < M && wb + s < WR)
-                    a[m][s] = *reinterpret_cast<const v4i*>(xq + (int64_t)m * K + 16 * (wb + s));
-                else
-                    a[m][s] = v4i{0, 0, 0, 0};
-                spart[m] = byte_sum16(a[m][s], spart[m]);
-            }
+            for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+                for (int s = 0; s < 4; ++s) {
+                    if (live && m < M && wb + s < WR)
+                        a[m][s] = *reinterpret_cast<const v4i*>(xq + (int64_t)m * K + 16 * (wb + s));
+                    else
+                        a[m][s] = v4i{0, 0, 0, 0};
+                    spart[m] = byte_sum16(a[m][s], spart[m]);
+                }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const v4i c = unpack_codes(w[r][s]);
+            for (int r = 0; r < R; ++r) {
 #pragma unroll
-                for (int m = 0; m < MR; ++m) {
-                    int d = part[r][m];
-                    d = __builtin_amdgcn_sdot4(c.x, a[m][s].x, d, false);
-                    d = __builtin_amdgcn_sdot4(c.y, a[m][s].y, d, false);
-                    d = __builtin_amdgcn_sdot4(c.z, a[m][s].z, d, false);
-                    d = __builtin_amdgcn_sdot4(c.w, a[m][s].w, d, false);
-                    part[r][m] = d;
+                for (int s = 0; s < 4; ++s) {
+                    const v4i c = unpack_codes(w[i][r][s]);
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) {
+                        int d = part[r][m];
+                        d = __builtin_amdgcn_sdot4(c.x, a[m][s].x, d, false);
+                        d = __builtin_amdgcn_sdot4(c.y, a[m][s].y, d, false);
+                        d = __builtin_amdgcn_sdot4(c.z, a[m][s].z, d, false);
+                        d = __builtin_amdgcn_sdot4(c.w, a[m][s].w, d, false);
+                        part[r][m] = d;
+                    }
                 }
             }
         }
@@ -151,8 +162,10 @@ hipError_t launch_gv(const int8_t* xq, const float* gamma, int M, int K, const u
                      int N, float beta, float* y, int32_t* acc, hipStream_t s) {
     const int rows_per_block = kGvWaves * R;
     const int blocks = (N + rows_per_block - 1) / rows_per_block;
-    gemv_valu_kernel<MR, R><<<dim3(blocks), dim3(kGvThreads), 0, s>>>(xq, gamma, M, K, wp, N,
-                                                                      beta, y, acc);
+    // one unit per lane in flight per row (batching two units per lane measured
+    // slower at K = 8192: fewer waves fit and each waits longer)
+    gemv_valu_kernel<MR, R, 1><<<dim3(blocks), dim3(kGvThreads), 0, s>>>(xq, gamma, M, K, wp, N,
+                                                                         beta, y, acc);
     return hipGetLastError();
 }
 

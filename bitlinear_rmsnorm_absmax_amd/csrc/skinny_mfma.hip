@@ -157,9 +157,11 @@ hipError_t launch_mt_nt(const int8_t* xq, const float* gamma, int M, int K, cons
 template <int MT>
 hipError_t launch_mt(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
                      int N, float beta, float* y, int32_t* acc, hipStream_t s) {
-    // 8 waves split K when there are at least 16 chunks of 256, else 4
-    const int nchunks = (K / 16 + 15) / 16;
-    if (nchunks >= 16) return launch_mt_nt<MT, 1, 8>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    // measured on K = 4096 / 8192 decode shapes: up to 4 tokens, 4 waves split
+    // K and a wave owns one column tile; 5..16 tokens, 2 waves split K and a
+    // wave owns two column tiles (the activation rows are then re-read from L2
+    // half as often per weight byte)
+    if (MT == 1 && M > 4) return launch_mt_nt<MT, 2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     return launch_mt_nt<MT, 1, 4>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
 
