@@ -15,8 +15,9 @@ timed region.  The packed weights rotate through at least 512 MB of copies so
 that consecutive steps cannot be served from the 256 MB Infinity Cache.
 Timed steps are replays of HIP graphs (one per weight copy), so host launch
 overhead does not pace the GPU.  Per-call kernel durations come from a second
-pass that launches each call of the step back to back `steps` times between
-two HIP events on its stream; the dominant forward call gives the roofline.
+pass: for each call of the step, a HIP graph of that call alone, once per
+weight copy, replayed between two HIP events on the stream the kernels run on;
+the dominant forward call gives the roofline.
 
 Prints ONE JSON line.
 """
@@ -42,6 +43,7 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published
 ROTATE_BYTES = 512 * 10 ** 6   # twice the Infinity Cache
+COPY_BYTES = 256 * 2 ** 20     # calibration copy of the traffic counters
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -55,6 +57,13 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--traffic-probe", metavar="JSON",
+                    help="launch every call of one step once, then a plain copy kernel of "
+                         f"{COPY_BYTES} bytes, write the launch order to JSON and exit "
+                         "(run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--traffic-write", nargs=3, metavar=("JSON", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn the two counter runs of --traffic-probe into "
+                         "profiles/traffic_<workload>.md")
     return ap.parse_args()
 
 
@@ -241,6 +250,103 @@ def read_traffic(workload_name: str, call: str):
     return float(m_val.group(1))
 
 
+def traffic_probe(args, torch, ops, dev):
+    """One eager step (every call once, in step order), then the calibration
+    copy: an elementwise kernel that reads COPY_BYTES and writes COPY_BYTES."""
+    src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    seq = []
+    ops(0, lambda name, *a, **kw: seq.append(name) or True)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    with open(args.traffic_probe, "w") as f:
+        json.dump(dict(workload=workloads.WORKLOADS[args.workload].name, calls=seq,
+                       copy_bytes=COPY_BYTES, copy_kernel="neg"), f)
+
+
+def _counter_rows(d: str, counter: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {files}")
+    per = {}
+    with open(files[0]) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            did = int(r["Dispatch_Id"])
+            name, v = per.get(did, (r["Kernel_Name"], 0.0))
+            per[did] = (name, v + float(r["Counter_Value"]))
+    return [per[k] for k in sorted(per)]
+
+
+def traffic_write(args):
+    """profiles/traffic_<workload>.md from the FETCH_SIZE and WRITE_SIZE runs of
+    --traffic-probe: the last dispatches of each run are the probe's step and
+    its copy; the counters (KiB per dispatch) are scaled by what they read for
+    the copy of known size."""
+    probe_json, fdir, wdir = args.traffic_write
+    probe = json.load(open(probe_json))
+    calls = probe["calls"]
+
+    def pick(rows):
+        """(library dispatches of the probe's step, the calibration copy)"""
+        copies = [i for i, (name, _) in enumerate(rows) if "neg" in name]
+        if not copies:
+            raise SystemExit("counter run holds no calibration copy")
+        lib = [r for r in rows[:copies[-1]] if "bl::" in r[0]][-len(calls):]
+        if len(lib) != len(calls):
+            raise SystemExit(f"counter run holds {len(lib)} library dispatches, "
+                             f"the probe made {len(calls)}")
+        for call, (name, _) in zip(calls, lib):
+            want = "quant_rows" if call.startswith(("quant", "silu")) else "_kernel"
+            if want not in name or (call.startswith("forward") and "quant_rows" in name):
+                raise SystemExit(f"dispatch {name} does not match call {call}")
+        return lib, rows[copies[-1]]
+
+    fr, fcopy = pick(_counter_rows(fdir, "FETCH_SIZE"))
+    wr, wcopy = pick(_counter_rows(wdir, "WRITE_SIZE"))
+    cb = probe["copy_bytes"]
+    f_scale = cb / (fcopy[1] * 1024)
+    w_scale = cb / (wcopy[1] * 1024)
+    wl = next(w for w in workloads.WORKLOADS.values() if w.name == probe["workload"])
+    lines = [f"# HBM traffic per launch: {wl.name}", "",
+             "Counters: rocprofv3 `--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE` (KiB per dispatch), "
+             "each in its own run of the probe; commands (from the repository root, "
+             "`cd /tmp && export TMPDIR=/tmp` first):", "",
+             "```",
+             f"python3 bench.py --workload {args.workload} --traffic-probe gpurun_out/probe.json",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- "
+             f"python3 bench.py --workload {args.workload} --traffic-probe gpurun_out/probe.json",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
+             f"python3 bench.py --workload {args.workload} --traffic-probe gpurun_out/probe.json",
+             f"python3 bench.py --workload {args.workload} --traffic-write gpurun_out/probe.json "
+             "gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             "```", "",
+             f"Calibration: an elementwise negation of {cb} bytes (reads {cb}, writes {cb}) "
+             f"reads FETCH_SIZE {fcopy[1]:.0f} KiB and WRITE_SIZE {wcopy[1]:.0f} KiB; "
+             f"scale factors {f_scale:.4f} (fetch) and {w_scale:.4f} (write).", "",
+             "| call | kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled bytes |",
+             "|---|---|---:|---:|---:|"]
+    vals = []
+    for call, (fk, fv), (wk, wv) in zip(calls, fr, wr):
+        if fk != wk:
+            raise SystemExit(f"dispatch mismatch between the runs: {fk} / {wk}")
+        b = fv * 1024 * f_scale + wv * 1024 * w_scale
+        short = fk.replace("(anonymous namespace)::", "").replace("void ", "")
+        short = short[:short.index(">(") + 1] if ">(" in short else short.split("(")[0]
+        lines.append(f"| {call} | `{short}` | {fv:.0f} | {wv:.0f} | {b:.4g} |")
+        vals.append((call, b))
+    lines += ["", f"source_digest: {kernel_source_digest()}", ""]
+    lines += [f"traffic_bytes_per_launch[{c}]: {b:.6g}" for c, b in vals]
+    path = os.path.join(PROFILES, f"traffic_{wl.name}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(path)
+
+
 # ----------------------------------------------------------------------------- cpu baseline
 
 def cpu_baseline(args, seconds: float):
@@ -297,6 +403,9 @@ def cpu_baseline(args, seconds: float):
 
 def main():
     args = parse()
+    if args.traffic_write:
+        traffic_write(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is a "
               "single-GPU kernel set and this build launches no multi-GPU run.", file=sys.stderr)
@@ -310,7 +419,12 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.traffic_probe:
+        args.no_rotate = True
     ops, meta, keep = build_plan(args, torch, bl, dev)
+    if args.traffic_probe:
+        traffic_probe(args, torch, ops, dev)
+        return
     rec = RunAll()
     ops(0, rec)  # first launch of every kernel; records the calls of a step
     torch.cuda.synchronize()
@@ -348,14 +462,31 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     print(f"# timed {args.steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
-    # per-call durations: each call launched back to back `steps` times
+    # per-call durations: each call launched back to back, one launch per
+    # weight copy, replayed from one HIP graph (eager: from the host)
     kern = {}
     for name, per_step in rec.calls.items():
-        t = RunOne(torch, name)
-        for i in range(args.steps):
-            ops(args.warmup + i, t)
-        kern[name] = dict(avg_us=t.avg_us(args.steps * per_step), per_step=per_step,
-                          **rec.info.get(name, {}))
+        if graphs is None:
+            t = RunOne(torch, name)
+            for i in range(args.steps):
+                ops(args.warmup + i, t)
+            avg = t.avg_us(args.steps * per_step)
+        else:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for c in range(ncopy):
+                    ops(c, lambda n, *a, **kw: n == name)
+            reps = max(1, math.ceil(args.steps / ncopy))
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            avg = e0.elapsed_time(e1) * 1e3 / (reps * ncopy * per_step)
+            del g
+        kern[name] = dict(avg_us=avg, per_step=per_step, **rec.info.get(name, {}))
     print("# per-call GPU time (us): " + ", ".join(f"{k} {v['avg_us']:.2f}" for k, v in kern.items()),
           file=sys.stderr, flush=True)
 
