@@ -26,11 +26,10 @@
 // between the WN waves that share a row.
 #include "device_common.h"
 #include "internal.h"
+#include "mfma_epilogue.h"
 
 namespace bl {
 namespace {
-
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 constexpr int BK = 128;
 constexpr int kXcds = 8;
@@ -82,7 +81,7 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wv = tid / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wv / WN, wn = wv % WN;
     const int l32 = lane & 31, h = lane >> 5;
 
@@ -184,41 +183,18 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __syncthreads();
 
-    int* Sp = reinterpret_cast<int*>(lds);                   // [WN][BM]
-    float* Ssc = reinterpret_cast<float*>(lds) + WN * C::BM;  // [BM]
+    int* Sp = reinterpret_cast<int*>(lds);  // [WN][BM] partial row sums
+    int* S = Sp + WN * C::BM;                // [BM]
+    float* Ssc = reinterpret_cast<float*>(S + C::BM);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int sv = s_part[i] + __shfl_xor(s_part[i], 32, kWave);
         if (h == 0) Sp[wn * C::BM + wm * TM * 32 + 32 * i + l32] = sv;
     }
-    for (int r = tid; r < C::BM; r += C::kThreads) {
-        const int row = m0 + r;
-        Ssc[r] = (row < M) ? out_scale(beta, gamma[row]) : 0.f;
-    }
     __syncthreads();
-
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rl = wm * TM * 32 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-            const int row = m0 + rl;
-            if (row >= M) continue;
-            const float sc = Ssc[rl];
-            int sm = 0;
-#pragma unroll
-            for (int w = 0; w < WN; ++w) sm += Sp[w * C::BM + rl];
-#pragma unroll
-            for (int t = 0; t < TN; ++t) {
-                const int col = n0 + wn * TN * 32 + 32 * t + l32;
-                if (col >= N) continue;
-                const int a = acc[i][t][v] - sm;
-                const int64_t o = (int64_t)row * N + col;
-                y[o] = (float)a * sc;
-                if (acc_out) acc_out[o] = a;
-            }
-        }
-    }
+    epilogue_tables(Sp, WN, C::BM, m0, M, gamma, beta, S, Ssc, tid, C::kThreads);
+    __syncthreads();
+    store_tiles<TM, TN>(acc, S, Ssc, wm * TM * 32, wn * TN * 32, m0, n0, M, N, y, acc_out, lane);
 }
 
 template <int WM, int WN, int TM, int TN, int STAGES>

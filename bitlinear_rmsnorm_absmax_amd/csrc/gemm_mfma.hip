@@ -44,6 +44,7 @@
 // plain load path; edge tiles clamp addresses and zero-fill what lies outside.
 #include "device_common.h"
 #include "internal.h"
+#include "mfma_epilogue.h"
 
 namespace bl {
 namespace {
@@ -161,7 +162,6 @@ __device__ __forceinline__ void store_step(const Stage<WM, WN>& st, v4i* As, v4u
         *reinterpret_cast<v2u*>(dst) = v2u{st.b.x, st.b.y};
 }
 
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ void mma_step(const v4i* As, const v4u* Bs, v16i (&acc)[TM][TN],
                                          int wm, int wn, int l32, int h) {
@@ -259,27 +259,7 @@ __device__ __forceinline__ void gemm_tile(const int8_t* __restrict__ xq,
     }
     __syncthreads();
 
-    // epilogue: lane (l32, h) holds column l32 and rows 8*(v/4) + 4h + v%4
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rl = wm * TM * 32 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-            const int row = m0 + rl;
-            if (EDGE && row >= M) continue;
-            const float sc = Ssc[rl];
-            const int sm = Ssum[rl];
-#pragma unroll
-            for (int t = 0; t < TN; ++t) {
-                const int col = n0 + wn * TN * 32 + 32 * t + l32;
-                if (EDGE && col >= N) continue;
-                const int a = acc[i][t][v] - sm;
-                const int64_t o = (int64_t)row * N + col;
-                y[o] = (float)a * sc;
-                if (acc_out) acc_out[o] = a;
-            }
-        }
-    }
+    store_tiles<TM, TN>(acc, Ssum, Ssc, wm * TM * 32, wn * TN * 32, m0, n0, M, N, y, acc_out, lane);
 }
 
 template <int WM, int WN>

@@ -32,6 +32,13 @@ hipError_t launch_skinny_mfma(const int8_t* xq, const float* gamma, int M, int K
                               const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                               hipStream_t s);
 
+// Decode product with the activation block staged in LDS (5 <= M <= 16,
+// K % 256 == 0); decode_lds_supports() tells whether a shape fits.
+bool decode_lds_supports(int M, int K, int N);
+hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
+                             const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
+                             hipStream_t s);
+
 // Path 3: LDS-tiled int8 MFMA GEMM.  The LDS-ring variant needs K % 128 == 0.
 bool gemm_dma_supports(int M, int K, int N);
 hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,

@@ -170,6 +170,10 @@ hipError_t launch_mt(const int8_t* xq, const float* gamma, int M, int K, const u
 hipError_t launch_skinny_mfma(const int8_t* xq, const float* gamma, int M, int K,
                               const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                               hipStream_t s) {
+    // 5..16 tokens: the LDS-staged kernel (measured faster on every decode
+    // shape from K = 2560 to 8192); 1..4 tokens and other K keep this kernel
+    if (M >= 5 && decode_lds_supports(M, K, N))
+        return launch_decode_lds(xq, gamma, M, K, wp, N, beta, y, acc, s);
     switch ((M + 15) / 16) {
         case 1: return launch_mt<1>(xq, gamma, M, K, wp, N, beta, y, acc, s);
         case 2: return launch_mt<2>(xq, gamma, M, K, wp, N, beta, y, acc, s);

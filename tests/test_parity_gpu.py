@@ -186,6 +186,43 @@ def test_forward_parity(dev, path, M, N, K):
     assert_y_close(y, y_ref)
 
 
+# The skinny path sends 5..16 tokens with K % 256 == 0 to the LDS-staged decode
+# kernel.  Cases cover its four workgroup widths (column tiles of 16: < 320,
+# >= 320, >= 640, >= 1280 tiles), ragged N, the largest K whose activation
+# block fits in LDS at 16 tokens (9216), and a zero token.
+DECODE_LDS_CASES = [(5, 1000, 256), (7, 5200, 512), (12, 10300, 1024), (16, 20500, 768),
+                    (16, 333, 9216), (9, 2570, 2560), (13, 40, 4096), (6, 17, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", DECODE_LDS_CASES)
+def test_decode_lds_parity(dev, M, N, K):
+    x, w, beta = workloads.random_case(700 + M + N, M, N, K, table=workloads.TERNARY_HALF_ZERO)
+    x = x.copy()
+    x[1] = 0.0
+    q, g, y, acc = run_forward(x, w, beta, dev, bl.PATH_SKINNY)
+    q_ref, g_ref = oracle.quant_act(x)
+    np.testing.assert_array_equal(q, q_ref)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, beta)
+    np.testing.assert_array_equal(acc, acc_ref)
+    assert_y_close(y, y_ref)
+
+
+def test_decode_lds_extreme_codes(dev):
+    M, N, K = 16, 700, 9216
+    q = np.full((M, K), 127, np.int8)
+    q[1::2] = -127
+    w = np.ones((N, K), np.int8)
+    w[1::3] = -1
+    g = np.linspace(0.5, 2.0, M).astype(np.float32)
+    packed, _ = bl.pack_weights(to_dev(w, dev))
+    y, acc = bl.forward(to_dev(q, dev), to_dev(g, dev), packed, 0.03, path=bl.PATH_SKINNY,
+                        want_acc=True)
+    y_ref, acc_ref = oracle.forward(q, g, w, np.float32(0.03))
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    assert np.abs(acc_ref).max() == 127 * K
+    assert_y_close(host(y), y_ref)
+
+
 def test_paths_agree_bitwise(dev):
     x, w, beta = workloads.random_case(500, 4, 640, 4096)
     outs = [run_forward(x, w, beta, dev, p) for p in (bl.PATH_GEMV, bl.PATH_SKINNY, bl.PATH_GEMM)]
