@@ -52,6 +52,7 @@ def _load() -> ctypes.CDLL:
             "oracle_accumulate": [_c_p, _i64, _i64, _c_p, _i64, _c_p],
             "oracle_rescale": [_c_p, _c_p, _i64, _i64, ctypes.c_float, _c_p],
             "oracle_silu_mul": [_c_p, _c_p, _i64, _c_p],
+            "oracle_ternarize": [_c_p, _i64, _i64, _c_p],
             "oracle_num_threads": [],
         }
         for name, args in sig.items():
@@ -60,6 +61,7 @@ def _load() -> ctypes.CDLL:
         lib.oracle_pack.restype = ctypes.c_int64
         lib.oracle_accumulate.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_ternarize.restype = ctypes.c_double
         for name in ("oracle_bf16_to_f32", "oracle_quant_act", "oracle_rmsnorm_quant_act",
                      "oracle_rmsnorm_quant_act_literal", "oracle_unpack", "oracle_rescale",
                      "oracle_silu_mul"):
@@ -123,6 +125,16 @@ def pack(w: np.ndarray) -> Tuple[np.ndarray, int]:
     out = np.empty((N, K // 16), dtype=np.uint32)
     bad = _load().oracle_pack(_p(w), N, K, _p(out))
     return out, int(bad)
+
+
+def ternarize(W: np.ndarray) -> Tuple[np.ndarray, float]:
+    """fp32 weights [N][K] -> (ternary int8 [N][K], beta as a Python float =
+    the float64 mean |W|); absmean rule of the datacamp article."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    w = np.empty((N, K), dtype=np.int8)
+    beta = _load().oracle_ternarize(_p(W), N, K, _p(w))
+    return w, float(beta)
 
 
 def unpack(packed: np.ndarray, K: int) -> np.ndarray:

@@ -209,3 +209,21 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* [D] absmean ternarisation: the mean absolute value in double, rows then
+ * columns in index order; then each entry against half of it. */
+double oracle_ternarize(const float* W, int64_t N, int64_t K, int8_t* w) {
+    double total = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double row = 0.0;
+        for (int64_t k = 0; k < K; ++k) row += fabs((double)W[n * K + k]);
+        total += row;
+    }
+    const double beta = (N > 0 && K > 0) ? total / ((double)N * (double)K) : 0.0;
+    const double half = beta * 0.5;
+    for (int64_t i = 0; i < N * K; ++i) {
+        const double v = (double)W[i];
+        w[i] = (int8_t)((v > half && beta > 0.0) ? 1 : (v < -half && beta > 0.0) ? -1 : 0);
+    }
+    return beta;
+}

@@ -12,8 +12,8 @@
  *       2. Aktivierungsquantisierung and 3. BitLinear-Betrieb; section
  *       "Ternäres Gewichtssystem / Das Konzept".
  *   [D] "MatMul-free language models" (datacamp.com, Dutch), sections
- *       "MatMul vervangen door ternaire bewerkingen" and
- *       "Kerncomponenten: MLGRU EN GLU".
+ *       "MatMul vervangen door ternaire bewerkingen" (also the absmean
+ *       ternarisation) and "Kerncomponenten: MLGRU EN GLU".
  *
  * Parity status: every function below is pinned by the CPU tests except the
  * float64 SiLU evaluation, whose transcendental is checked only through
@@ -62,6 +62,15 @@ void oracle_rescale(const int32_t* acc, const float* gamma, int64_t M, int64_t N
 
 /* h[i] = silu(gate[i]) * up[i] in float64 ([D] MatMul-vrije GLU). */
 void oracle_silu_mul(const float* gate, const float* up, int64_t n, double* h);
+
+/* Absmean ternarisation ([D] MatMul vervangen door ternaire bewerkingen: the
+ * weight matrix is scaled by its mean absolute value and every entry rounded
+ * to the nearest of -1, 0, 1).  beta64 = (sum over rows n, then over k, of
+ * |W[n][k]|, accumulated in double in index order) / (N*K).  Entry code:
+ * +1 if W > beta64/2, -1 if W < -beta64/2, else 0, compared exactly in double,
+ * which is round-half-even of W/beta64 clipped to [-1, 1] (a tie |W| = beta/2
+ * rounds to 0).  beta64 = 0 gives all zeros.  Returns beta64. */
+double oracle_ternarize(const float* W, int64_t N, int64_t K, int8_t* w);
 
 /* Number of OpenMP threads the accumulate loop runs on. */
 int oracle_num_threads(void);

@@ -363,3 +363,69 @@ def test_glu_with_identity_down_projection_tracks_h():
     # zero up-projection kills the block
     st0 = oracle.glu(x, wg, np.zeros_like(wu), eye, (0.02, 0.03, 1.0), np.ones(D, np.float32))
     assert not st0["y"].any() and not st0["h_q"].any()
+
+
+# ---------------------------------------------------------------- absmean ternarisation
+
+def test_ternarize_worked_example():
+    g = _golden("ternarize_2x16.json")
+    W = np.array(g["W"], dtype=np.float32)
+    w, beta = oracle.ternarize(W)
+    assert beta == g["beta"]
+    np.testing.assert_array_equal(w, np.array(g["codes"], dtype=np.int8))
+
+
+def test_ternarize_recovers_a_scaled_ternary_matrix():
+    # W = a * T with T ternary: beta = a * nnz / (N K) (exact here: dyadic a,
+    # N K a power of two) and every nonzero satisfies |W| = a > beta / 2
+    rng = workloads.rng_for(900, 1)
+    T = workloads.ternary(rng, 64, 256, workloads.TERNARY_UNIFORM)
+    a = 0.375
+    w, beta = oracle.ternarize(T.astype(np.float32) * np.float32(a))
+    np.testing.assert_array_equal(w, T)
+    assert Fraction(beta) == Fraction(3, 8) * Fraction(int(np.count_nonzero(T)), 64 * 256)
+
+
+def test_ternarize_scale_and_sign_symmetries():
+    rng = workloads.rng_for(900, 2)
+    W = rng.standard_normal((48, 320)).astype(np.float32)
+    w, beta = oracle.ternarize(W)
+    w2, beta2 = oracle.ternarize(W * np.float32(8.0))
+    np.testing.assert_array_equal(w2, w)
+    assert beta2 == 8.0 * beta  # power-of-two scaling is exact in every partial sum
+    wn, betan = oracle.ternarize(-W)
+    np.testing.assert_array_equal(wn, -w)
+    assert betan == beta
+
+
+def test_ternarize_ties_clip_and_zero():
+    # sum |W| = 8 over 8 entries: beta = 1, half = 0.5; the three entries of
+    # magnitude 0.5 are ties and go to 0, 1.5 and 3.0 clip to +-1
+    W = np.array([[0.5, -0.5, 0.625, -1.5, 3.0, 0.0, 1.375, -0.5]], np.float32)
+    w, beta = oracle.ternarize(W)
+    assert beta == 1.0
+    np.testing.assert_array_equal(w[0], [0, 0, 1, -1, 1, 0, 1, 0])
+    # one ulp above the tie rounds away from zero
+    W2 = W.copy()
+    W2[0, 0] = np.nextafter(np.float32(0.5), np.float32(1.0))
+    W2[0, 2] = np.float32(0.625) - (W2[0, 0] - np.float32(0.5))  # same ulp: sum |W| stays 8
+    w2, beta2 = oracle.ternarize(W2)
+    assert beta2 == 1.0 and w2[0, 0] == 1
+    z, bz = oracle.ternarize(np.zeros((3, 32), np.float32))
+    assert bz == 0.0 and not z.any()
+
+
+def test_ternarize_against_exact_rational_mean():
+    # beta against the exactly rounded mean (math.fsum); the oracle's ordered
+    # double sum may differ from it only by rounding, and every code must agree
+    # with the exact threshold except entries within that rounding of it
+    rng = workloads.rng_for(900, 3)
+    W = (rng.standard_normal((37, 416)) * 0.02).astype(np.float32)
+    w, beta = oracle.ternarize(W)
+    exact = math.fsum(abs(float(v)) for v in W.ravel()) / W.size
+    assert abs(beta - exact) <= 1e-12 * exact
+    d = W.astype(np.float64)
+    ref = np.where(d > exact / 2, 1, np.where(d < -exact / 2, -1, 0))
+    near = np.abs(np.abs(d) - exact / 2) <= 1e-12 * exact
+    np.testing.assert_array_equal(w[~near], ref[~near])
+    assert 0.25 < np.count_nonzero(w) / w.size < 0.75
