@@ -129,7 +129,8 @@ def pack(w: np.ndarray) -> Tuple[np.ndarray, int]:
 
 def ternarize(W: np.ndarray) -> Tuple[np.ndarray, float]:
     """fp32 weights [N][K] -> (ternary int8 [N][K], beta as a Python float =
-    the float64 mean |W|); absmean rule of the datacamp article."""
+    the float64 mean |W|, pairwise-summed); absmean rule of the datacamp
+    article."""
     W = _c(W, np.float32)
     N, K = W.shape
     w = np.empty((N, K), dtype=np.int8)

@@ -210,18 +210,23 @@ int oracle_num_threads(void) {
 #endif
 }
 
-/* [D] absmean ternarisation: the mean absolute value in double, rows then
- * columns in index order; then each entry against half of it. */
+/* Pairwise sum of |x[a..b)| in double: a run of one entry is its value; a
+ * longer run splits after the largest power of two below its length. */
+static double pairwise_abs(const float* x, int64_t a, int64_t b) {
+    const int64_t n = b - a;
+    if (n == 1) return fabs((double)x[a]);
+    int64_t p = 1;
+    while (p * 2 < n) p *= 2;
+    return pairwise_abs(x, a, a + p) + pairwise_abs(x, a + p, b);
+}
+
+/* [D] absmean ternarisation: the mean absolute value (pairwise double sum of
+ * the row-major entries, divided by N*K); then each entry against half of it. */
 double oracle_ternarize(const float* W, int64_t N, int64_t K, int8_t* w) {
-    double total = 0.0;
-    for (int64_t n = 0; n < N; ++n) {
-        double row = 0.0;
-        for (int64_t k = 0; k < K; ++k) row += fabs((double)W[n * K + k]);
-        total += row;
-    }
-    const double beta = (N > 0 && K > 0) ? total / ((double)N * (double)K) : 0.0;
+    const int64_t total_n = N * K;
+    const double beta = total_n > 0 ? pairwise_abs(W, 0, total_n) / ((double)N * (double)K) : 0.0;
     const double half = beta * 0.5;
-    for (int64_t i = 0; i < N * K; ++i) {
+    for (int64_t i = 0; i < total_n; ++i) {
         const double v = (double)W[i];
         w[i] = (int8_t)((v > half && beta > 0.0) ? 1 : (v < -half && beta > 0.0) ? -1 : 0);
     }

@@ -65,11 +65,12 @@ void oracle_silu_mul(const float* gate, const float* up, int64_t n, double* h);
 
 /* Absmean ternarisation ([D] MatMul vervangen door ternaire bewerkingen: the
  * weight matrix is scaled by its mean absolute value and every entry rounded
- * to the nearest of -1, 0, 1).  beta64 = (sum over rows n, then over k, of
- * |W[n][k]|, accumulated in double in index order) / (N*K).  Entry code:
- * +1 if W > beta64/2, -1 if W < -beta64/2, else 0, compared exactly in double,
- * which is round-half-even of W/beta64 clipped to [-1, 1] (a tie |W| = beta/2
- * rounds to 0).  beta64 = 0 gives all zeros.  Returns beta64. */
+ * to the nearest of -1, 0, 1).  beta64 = S / (N*K) with S the pairwise sum in
+ * double of |W| over the row-major entries (a run splits after the largest
+ * power of two below its length).  Entry code: +1 if W > beta64/2, -1 if
+ * W < -beta64/2, else 0, compared exactly in double, which is
+ * round-half-even of W/beta64 clipped to [-1, 1] (a tie |W| = beta/2 rounds
+ * to 0).  beta64 = 0 gives all zeros.  Returns beta64. */
 double oracle_ternarize(const float* W, int64_t N, int64_t K, int8_t* w);
 
 /* Number of OpenMP threads the accumulate loop runs on. */

@@ -429,3 +429,17 @@ def test_ternarize_against_exact_rational_mean():
     near = np.abs(np.abs(d) - exact / 2) <= 1e-12 * exact
     np.testing.assert_array_equal(w[~near], ref[~near])
     assert 0.25 < np.count_nonzero(w) / w.size < 0.75
+
+
+def test_ternarize_sum_is_pairwise():
+    # |W| = [1, 2^-53 x 4, 0, 0, 0]: adding left to right every 1 + 2^-53 ties
+    # back to 1 (sum 1); the pairwise tree adds the small terms first:
+    # ((1 + 2^-53) + (2^-53 + 2^-53)) + ((2^-53 + 0) + 0) = (1 + 2^-52) + 2^-53,
+    # a tie between 1 + 2^-52 and 1 + 2^-51 that goes to the even 1 + 2^-51,
+    # which is also the exact sum
+    e = 2.0 ** -53
+    W = np.array([[1.0, e, -e, e, -e, 0.0, 0.0, 0.0] * 4], np.float32)  # K = 32, 4 copies
+    _, beta = oracle.ternarize(W)
+    block = 1.0 + 2.0 ** -51   # pairwise sum of one group of 8, exact
+    assert beta == (4 * block) / 32  # the four equal group sums add exactly
+    assert beta != 4.0 / 32
