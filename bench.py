@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--op", choices=("layer", "ternarize"), default="layer",
+                    help="layer: the BitLinear step (default); ternarize: absmean "
+                         "ternarisation + packing of fp32 weights of the workload's shape")
     ap.add_argument("--traffic-probe", metavar="JSON",
                     help="launch every call of one step once, then a plain copy kernel of "
                          f"{COPY_BYTES} bytes, write the launch order to JSON and exit "
@@ -399,6 +402,74 @@ def cpu_baseline(args, seconds: float):
                 sample=f"{n} x ({desc}), M={list(wl.ms)}, {el:.1f} s")
 
 
+# ----------------------------------------------------------------------------- ternarize
+
+def bench_ternarize(args, torch, bl, dev):
+    """bitlinear_ternarize on seeded fp32 weights N(0, 0.02^2) of the workload's
+    [N][K]: one call per step (row sums, ordered total, codes + packing)."""
+    wl = workloads.WORKLOADS[args.workload]
+    N, K = wl.N, wl.K
+    W = (workloads.rng_for(args.workload, 30).standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wd = torch.from_numpy(W).to(dev)
+    packed = torch.empty((N, K // 16), dtype=torch.int32, device=dev)
+    beta = torch.empty((1,), dtype=torch.float32, device=dev)
+    beta64 = torch.empty((1,), dtype=torch.float64, device=dev)
+
+    def call():
+        st = bl.lib.bitlinear_ternarize(Wd.data_ptr(), N, K, packed.data_ptr(), None,
+                                        beta.data_ptr(), beta64.data_ptr(),
+                                        torch.cuda.current_stream(dev).cuda_stream)
+        if st != 0:
+            raise RuntimeError(bl.last_error())
+
+    call()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    alg = 8 * N * K + N * K // 4   # W read twice (row sums, codes) + packed words written
+    gbs = alg / (us * 1e-6) / 1e9
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < args.cpu_seconds / 2 or n == 0:
+            oracle.ternarize(W)
+            n += 1
+        el = time.perf_counter() - t0
+        cpu = dict(value=round(4 * N * K * n / el / 1e9, 4), unit="fp32-W GB/s", cores=1,
+                   kind="oracle", sample=f"{n} x oracle.ternarize on [{N}][{K}], {el:.1f} s")
+    line = {
+        "metric": "absmean ternarisation + packing: fp32-W GB/s",
+        "value": round(4 * N * K / (us * 1e-6) / 1e9, 2),
+        "unit": "fp32-W GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"ternarize_{wl.name}", "N": N, "K": K,
+                   "timing": "hip_graph_per_step"},
+        "roofline": dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None,
+                         call="bitlinear_ternarize", avg_launch_us=round(us, 3),
+                         alg_bytes_per_launch=alg),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -419,6 +490,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.op == "ternarize":
+        bench_ternarize(args, torch, bl, dev)
+        return
     if args.traffic_probe:
         args.no_rotate = True
     ops, meta, keep = build_plan(args, torch, bl, dev)

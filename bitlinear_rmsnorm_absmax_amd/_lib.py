@@ -33,6 +33,7 @@ _SIGNATURES = {
     "bitlinear_forward": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _vp],
     "bitlinear_forward_path": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, ctypes.c_int, _vp],
     "bitlinear_silu_mul_quant": [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp],
+    "bitlinear_ternarize": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "bitlinear_last_error": [],
     "bitlinear_abi_version": [],
 }
@@ -166,6 +167,21 @@ def silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, want_h: bool = False):
     _check(lib.bitlinear_silu_mul_quant(gate.data_ptr(), up.data_ptr(), M, F, _ptr(h),
                                         h_q.data_ptr(), g.data_ptr(), _stream(gate)))
     return (h_q, g, h) if want_h else (h_q, g)
+
+
+def ternarize(W: torch.Tensor, want_codes: bool = False):
+    """Absmean ternarisation of fp32 weights [N][K] -> (packed int32 [N][K/16],
+    beta fp32 [1], beta64 float64 [1][, codes int8 [N][K]]), all on W's device."""
+    _dev(W, "W", (torch.float32,))
+    N, K = W.shape
+    dev = W.device
+    packed = torch.empty((N, K // 16), dtype=torch.int32, device=dev)
+    beta = torch.empty((1,), dtype=torch.float32, device=dev)
+    beta64 = torch.empty((1,), dtype=torch.float64, device=dev)
+    codes = torch.empty((N, K), dtype=torch.int8, device=dev) if want_codes else None
+    _check(lib.bitlinear_ternarize(W.data_ptr(), N, K, packed.data_ptr(), _ptr(codes),
+                                   beta.data_ptr(), beta64.data_ptr(), _stream(W)))
+    return (packed, beta, beta64, codes) if want_codes else (packed, beta, beta64)
 
 
 def bitlinear(x: torch.Tensor, w_packed: torch.Tensor, beta: float,

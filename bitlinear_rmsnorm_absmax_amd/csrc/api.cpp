@@ -180,6 +180,28 @@ bitlinear_status_t bitlinear_silu_mul_quant(const float* gate, const float* up, 
     return from_hip(bl::launch_silu_mul_quant(gate, up, M, F, h, h_q, gamma_h, stream), fn);
 }
 
+bitlinear_status_t bitlinear_ternarize(const float* W, int64_t N, int64_t K, uint32_t* w_packed,
+                                       int8_t* w_ternary, float* beta, double* beta64,
+                                       hipStream_t stream) {
+    const char* fn = "bitlinear_ternarize";
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    BL_TRY(check_k(fn, "K", K));
+    if (K != 0 && K < 32)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld must be 0 or >= 32", fn, (long long)K);
+    const bool any = N > 0 && K > 0;
+    if (any && N * (K / 16) > (1LL << 40))
+        return fail(BITLINEAR_ERR_SHAPE, "%s: N*K/16 exceeds 2^40", fn);
+    BL_TRY(need(fn, "W", W, any, 16));
+    BL_TRY(need(fn, "w_packed", w_packed, any, 16));
+    BL_TRY(need(fn, "beta", beta, true, 4));
+    BL_TRY(need(fn, "beta64", beta64, true, 8));
+    if (w_ternary && !aligned(w_ternary, 16))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: w_ternary is not 16-byte aligned", fn);
+    return from_hip(bl::launch_ternarize(W, any ? N : 0, any ? K : 0, w_packed, w_ternary, beta,
+                                         beta64, stream),
+                    fn);
+}
+
 const char* bitlinear_last_error(void) { return g_err; }
 
 int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }

@@ -41,6 +41,11 @@ hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
 
 // Path 3: LDS-tiled int8 MFMA GEMM.  The LDS-ring variant needs K % 128 == 0.
 bool gemm_dma_supports(int M, int K, int N);
+
+// Absmean ternarisation + packing (three stream-ordered launches; the packed
+// buffer holds the per-row sums in between, so K >= 32).
+hipError_t launch_ternarize(const float* W, int64_t N, int64_t K, uint32_t* packed, int8_t* codes,
+                            float* beta32, double* beta64, hipStream_t s);
 hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
                            const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                            hipStream_t s);

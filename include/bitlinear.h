@@ -147,6 +147,37 @@ bitlinear_status_t bitlinear_silu_mul_quant(const float* gate, const float* up, 
                                             int64_t F, float* h, int8_t* h_q, float* gamma_h,
                                             hipStream_t stream);
 
+/*
+ * bitlinear_ternarize -- absmean ternarisation of full-precision weights,
+ * then packing (datacamp article "MatMul-free language models", section
+ * "MatMul vervangen door ternaire bewerkingen": the weight matrix is scaled
+ * by its mean absolute value and every entry rounded to the nearest of -1, 0,
+ * 1).  The step before bitlinear_pack_weights for weights that are not yet
+ * ternary.
+ *
+ *   beta64 = S / (N*K), S = pairwise sum in double of |W| over the
+ *            row-major entries (a run of entries splits after the largest
+ *            power of two below its length)
+ *   code   = +1 if W > beta64/2, -1 if W < -beta64/2, else 0 (compared
+ *            exactly in double: round-half-even of W/beta64 clipped to
+ *            [-1, 1]; |W| = beta64/2 gives 0; beta64 = 0 gives all zeros)
+ *
+ * W          device fp32 [N][K] row-major, 16-byte aligned, finite.
+ * w_packed   device uint32 [N][K/16] out, the codes packed as by
+ *            bitlinear_pack_weights.  While the call runs it also holds the
+ *            partial sums (about N*K/8 bytes), hence K >= 32.
+ * w_ternary  device int8 [N][K] out (the codes), 16-byte aligned; may be NULL.
+ * beta       device fp32 [1] out: fl32(beta64), the scale bitlinear_forward takes.
+ * beta64     device double [1] out: the mean itself.
+ * N, K       N >= 0; K == 0 or (K >= 32 and K % 16 == 0), K <= BITLINEAR_MAX_K;
+ *            N*K == 0 writes beta = beta64 = 0 and nothing else.
+ * Cost: W is read twice (sum, then codes).  3 + ceil(log64(N*K/4096))
+ * launches on `stream`; none allocates.
+ */
+bitlinear_status_t bitlinear_ternarize(const float* W, int64_t N, int64_t K, uint32_t* w_packed,
+                                       int8_t* w_ternary, float* beta, double* beta64,
+                                       hipStream_t stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 const char* bitlinear_last_error(void);
 

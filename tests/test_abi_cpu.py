@@ -18,8 +18,8 @@ def test_every_declared_symbol_is_exported():
     declared = bl.declared_symbols()
     assert set(declared) == {
         "bitlinear_quant_act", "bitlinear_pack_weights", "bitlinear_forward",
-        "bitlinear_forward_path", "bitlinear_silu_mul_quant", "bitlinear_last_error",
-        "bitlinear_abi_version"}
+        "bitlinear_forward_path", "bitlinear_silu_mul_quant", "bitlinear_ternarize",
+        "bitlinear_last_error", "bitlinear_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -141,3 +141,27 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError, match="GPU tensor"):
         bl.quant_act(torch.zeros(2, 16))
+
+
+def _tern(W=FAKE, N=1, K=32, packed=FAKE, codes=None, beta=FAKE, beta64=FAKE):
+    return bl.lib.bitlinear_ternarize(W, N, K, packed, codes, beta, beta64, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(W=None), bl.ERR_NULL, "W is NULL"),
+    (dict(packed=None), bl.ERR_NULL, "w_packed is NULL"),
+    (dict(beta=None), bl.ERR_NULL, "beta is NULL"),
+    (dict(beta64=None), bl.ERR_NULL, "beta64 is NULL"),
+    (dict(beta=None, N=0), bl.ERR_NULL, "beta is NULL"),
+    (dict(K=16), bl.ERR_SHAPE, "must be 0 or >= 32"),
+    (dict(K=40), bl.ERR_SHAPE, "multiple of 16"),
+    (dict(K=131072 + 16), bl.ERR_SHAPE, "K=131088"),
+    (dict(N=-3), bl.ERR_SHAPE, "N=-3"),
+    (dict(W=FAKE + 4), bl.ERR_ALIGN, "W is not 16-byte aligned"),
+    (dict(packed=FAKE + 8), bl.ERR_ALIGN, "w_packed is not 16-byte aligned"),
+    (dict(codes=FAKE + 4), bl.ERR_ALIGN, "w_ternary is not 16-byte aligned"),
+    (dict(beta64=FAKE + 4), bl.ERR_ALIGN, "beta64 is not 8-byte aligned"),
+])
+def test_ternarize_rejects(kw, status, msg):
+    assert _tern(**kw) == status
+    assert msg in bl.last_error()

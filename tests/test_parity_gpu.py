@@ -380,3 +380,69 @@ def test_glu_down_projection_on_oracle_codes(dev):
                         betas[2], want_acc=True)
     np.testing.assert_array_equal(host(acc), ref["acc_down"])
     assert_y_close(host(y), ref["y"])
+
+
+# ------------------------------------------------------------------ absmean ternarisation
+
+def _ternarize_check(W, dev):
+    Wd = to_dev(W, dev)
+    packed, beta, beta64, codes = bl.ternarize(Wd, want_codes=True)
+    w_ref, b_ref = oracle.ternarize(W)
+    assert float(host(beta64)[0]) == b_ref                       # same ordered double sum
+    assert host(beta)[0] == np.float32(b_ref)
+    np.testing.assert_array_equal(host(codes), w_ref)
+    ref_packed, bad = oracle.pack(w_ref)
+    assert bad == 0
+    np.testing.assert_array_equal(host(packed).view(np.uint32), ref_packed)
+    return w_ref, b_ref, packed, beta
+
+
+@pytest.mark.parametrize("N,K,dist", [
+    # 1 to 3 level passes of the pairwise reduction; (65, 64) is the first size
+    # with a level pass (65 groups of 64), (1, 80) the smallest scratch margin
+    (1, 32, "normal"), (1, 80, "normal"), (65, 64, "normal"), (37, 48, "normal"),
+    (100, 4096, "normal"), (33, 112, "student_t3"),
+    (2570, 2560, "normal"), (11008, 4096, "normal"), (64, 256, "scaled_ternary")])
+def test_ternarize_parity(dev, N, K, dist):
+    rng = workloads.rng_for(950, N, K)
+    if dist == "normal":
+        W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    elif dist == "student_t3":
+        W = (rng.standard_t(3, (N, K)) * 0.05).astype(np.float32)
+    else:
+        T = workloads.ternary(rng, N, K, workloads.TERNARY_HALF_ZERO)
+        W = T.astype(np.float32) * np.float32(0.75)
+    w_ref, _, _, _ = _ternarize_check(W, dev)
+    if dist == "scaled_ternary":
+        np.testing.assert_array_equal(w_ref, T)
+
+
+def test_ternarize_ties_on_gpu(dev):
+    # the hand-derived 2 x 16 example, repeated along K (same mean): ties at beta/2 -> 0
+    g = json.load(open(os.path.join(GOLDEN, "ternarize_2x16.json")))
+    W = np.concatenate([np.array(g["W"], np.float32)] * 2, axis=1)
+    w_ref, b_ref, _, _ = _ternarize_check(W, dev)
+    assert b_ref == g["beta"]
+    np.testing.assert_array_equal(w_ref, np.concatenate([np.array(g["codes"], np.int8)] * 2, axis=1))
+
+
+def test_ternarize_empty(dev):
+    for shape in ((0, 64), (5, 0)):
+        W = torch.zeros(shape, dtype=torch.float32, device=dev)
+        packed, beta, beta64 = bl.ternarize(W)
+        assert float(host(beta)[0]) == 0.0 and float(host(beta64)[0]) == 0.0
+
+
+def test_ternarize_then_forward(dev):
+    # fp weights -> ternary + beta on the GPU -> the layer, against the oracle chain
+    rng = workloads.rng_for(951, 1)
+    N, K, M = 640, 2048, 6
+    W = (rng.standard_normal((N, K)) * 0.03).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w_ref, b_ref, packed, beta = _ternarize_check(W, dev)
+    q, g = bl.quant_act(to_dev(x, dev))
+    y, acc = bl.forward(q, g, packed, float(host(beta)[0]), want_acc=True)
+    q_ref, g_ref = oracle.quant_act(x)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w_ref, np.float32(b_ref))
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    assert_y_close(host(y), y_ref)
