@@ -74,6 +74,8 @@ def forward_kernel(M: int, K: int) -> str:
     """Kernel that bitlinear_forward picks for M (the library's dispatch)."""
     if M <= 2:
         return "gemv_valu_kernel"
+    if 5 <= M <= 16 and K % 256 == 0 and ((M * K + 1023) // 1024) * 1024 + 16384 <= 160 * 1024:
+        return "decode_lds_kernel"
     if M <= 32:
         return "skinny_mfma_kernel"
     return "gemm_dma_kernel" if K % 128 == 0 else "gemm_mfma_kernel"
