@@ -53,6 +53,9 @@ def _load() -> ctypes.CDLL:
             "oracle_rescale": [_c_p, _c_p, _i64, _i64, ctypes.c_float, _c_p],
             "oracle_silu_mul": [_c_p, _c_p, _i64, _c_p],
             "oracle_ternarize": [_c_p, _i64, _i64, _c_p],
+            "oracle_binarize": [_c_p, _i64, _i64, _c_p],
+            "oracle_pack1": [_c_p, _i64, _i64, _c_p],
+            "oracle_unpack1": [_c_p, _i64, _i64, _c_p],
             "oracle_num_threads": [],
         }
         for name, args in sig.items():
@@ -62,6 +65,9 @@ def _load() -> ctypes.CDLL:
         lib.oracle_accumulate.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_ternarize.restype = ctypes.c_double
+        lib.oracle_binarize.restype = ctypes.c_double
+        lib.oracle_pack1.restype = ctypes.c_int64
+        lib.oracle_unpack1.restype = None
         for name in ("oracle_bf16_to_f32", "oracle_quant_act", "oracle_rmsnorm_quant_act",
                      "oracle_rmsnorm_quant_act_literal", "oracle_unpack", "oracle_rescale",
                      "oracle_silu_mul"):
@@ -136,6 +142,35 @@ def ternarize(W: np.ndarray) -> Tuple[np.ndarray, float]:
     w = np.empty((N, K), dtype=np.int8)
     beta = _load().oracle_ternarize(_p(W), N, K, _p(w))
     return w, float(beta)
+
+
+def binarize(W: np.ndarray) -> Tuple[np.ndarray, float]:
+    """fp32 weights [N][K] -> (+-1 int8 [N][K], alpha = float64 mean of W);
+    Sign(W - alpha) with Sign(0) = -1 (unite.ai article, weight binarisation)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    w = np.empty((N, K), dtype=np.int8)
+    alpha = _load().oracle_binarize(_p(W), N, K, _p(w))
+    return w, float(alpha)
+
+
+def pack1(w: np.ndarray) -> Tuple[np.ndarray, int]:
+    """+-1 int8 [N][K] (K % 32 == 0) -> (uint32 [N][K/32], #entries not +-1)."""
+    w = _c(w, np.int8)
+    N, K = w.shape
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    out = np.empty((N, K // 32), dtype=np.uint32)
+    bad = _load().oracle_pack1(_p(w), N, K, _p(out))
+    return out, int(bad)
+
+
+def unpack1(packed: np.ndarray, K: int) -> np.ndarray:
+    packed = _c(packed, np.uint32)
+    N = packed.shape[0]
+    w = np.empty((N, K), dtype=np.int8)
+    _load().oracle_unpack1(_p(packed), N, K, _p(w))
+    return w
 
 
 def unpack(packed: np.ndarray, K: int) -> np.ndarray:

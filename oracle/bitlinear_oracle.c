@@ -232,3 +232,52 @@ double oracle_ternarize(const float* W, int64_t N, int64_t K, int8_t* w) {
     }
     return beta;
 }
+
+/* Pairwise sum of x[a..b) in double, split as in pairwise_abs. */
+static double pairwise_signed(const float* x, int64_t a, int64_t b) {
+    const int64_t n = b - a;
+    if (n == 1) return (double)x[a];
+    int64_t p = 1;
+    while (p * 2 < n) p *= 2;
+    return pairwise_signed(x, a, a + p) + pairwise_signed(x, a + p, b);
+}
+
+/* [U] 1. Gewichtsbinarisierung: centre on the mean, then the sign (+1 only
+ * for a strictly positive difference). */
+double oracle_binarize(const float* W, int64_t N, int64_t K, int8_t* w) {
+    const int64_t total_n = N * K;
+    const double alpha = total_n > 0 ? pairwise_signed(W, 0, total_n) / ((double)N * (double)K) : 0.0;
+    for (int64_t i = 0; i < total_n; ++i) w[i] = (int8_t)(((double)W[i] > alpha) ? 1 : -1);
+    return alpha;
+}
+
+int64_t oracle_pack1(const int8_t* w, int64_t N, int64_t K, uint32_t* packed) {
+    int64_t bad = 0;
+    const int64_t words = K / 32;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t q = 0; q < words; ++q) {
+            uint32_t word = 0;
+            for (int e = 0; e < 32; ++e) {
+                const int8_t v = w[n * K + 32 * q + e];
+                uint32_t bit = 0;
+                if (v == 1) bit = 1;
+                else if (v != -1) ++bad;
+                const int j = e / 4, b = e % 4;
+                word |= bit << (8 * b + j);
+            }
+            packed[n * words + q] = word;
+        }
+    return bad;
+}
+
+void oracle_unpack1(const uint32_t* packed, int64_t N, int64_t K, int8_t* w) {
+    const int64_t words = K / 32;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t q = 0; q < words; ++q) {
+            const uint32_t word = packed[n * words + q];
+            for (int e = 0; e < 32; ++e) {
+                const int j = e / 4, b = e % 4;
+                w[n * K + 32 * q + e] = (int8_t)(((word >> (8 * b + j)) & 1u) ? 1 : -1);
+            }
+        }
+}

@@ -73,6 +73,21 @@ void oracle_silu_mul(const float* gate, const float* up, int64_t n, double* h);
  * to 0).  beta64 = 0 gives all zeros.  Returns beta64. */
 double oracle_ternarize(const float* W, int64_t N, int64_t K, int8_t* w);
 
+/* Weight binarisation ([U] Mathematische Grundlagen, 1. Gewichtsbinarisierung:
+ * W_f = Sign(W - alpha) with alpha the mean of the weights and Sign(v) = +1 for
+ * v > 0, else -1).  alpha64 = pairwise double sum of W (row-major, as in
+ * oracle_ternarize) / (N*K); code = +1 if W > alpha64 (exact comparison in
+ * double), else -1, so W == alpha64 gives -1.  Returns alpha64. */
+double oracle_binarize(const float* W, int64_t N, int64_t K, int8_t* w);
+
+/* 1-bit packing of +-1 weights: word n*(K/32) + k/32 holds entry e = k mod 32
+ * = 4j + b (j = e / 4, b = e mod 4) at bit 8b + j as (w + 1) / 2, so
+ * (word >> j) & 0x01010101 gives the bits of entries 4j .. 4j+3 in bytes
+ * 0 .. 3.  K % 32 == 0.  Returns the number of entries not in {-1, +1}
+ * (packed as 0 bits). */
+int64_t oracle_pack1(const int8_t* w, int64_t N, int64_t K, uint32_t* packed);
+void oracle_unpack1(const uint32_t* packed, int64_t N, int64_t K, int8_t* w);
+
 /* Number of OpenMP threads the accumulate loop runs on. */
 int oracle_num_threads(void);
 

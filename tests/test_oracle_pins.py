@@ -443,3 +443,62 @@ def test_ternarize_sum_is_pairwise():
     block = 1.0 + 2.0 ** -51   # pairwise sum of one group of 8, exact
     assert beta == (4 * block) / 32  # the four equal group sums add exactly
     assert beta != 4.0 / 32
+
+
+# ---------------------------------------------------------------- 1-bit weights
+
+def test_binarize_worked_example():
+    g = _golden("binarize_2x32.json")
+    W = np.array(g["W"], dtype=np.float32)
+    w, alpha = oracle.binarize(W)
+    assert alpha == g["alpha"] == 0.25
+    np.testing.assert_array_equal(w, np.array(g["codes"], dtype=np.int8))
+    packed, bad = oracle.pack1(w)
+    assert bad == 0
+    np.testing.assert_array_equal(packed, np.array(g["packed"], dtype=np.uint32))
+    np.testing.assert_array_equal(oracle.unpack1(packed, 32), w)
+
+
+def test_pack1_bit_positions_and_round_trip():
+    # entry e = 4j + b at bit 8b + j: a single +1 at e lights exactly that bit
+    for e in range(32):
+        w = -np.ones((1, 32), np.int8)
+        w[0, e] = 1
+        packed, _ = oracle.pack1(w)
+        assert int(packed[0, 0]) == 1 << (8 * (e % 4) + e // 4)
+    rng = workloads.rng_for(910, 1)
+    w = np.where(rng.random((9, 96)) < 0.5, 1, -1).astype(np.int8)
+    packed, bad = oracle.pack1(w)
+    assert bad == 0
+    np.testing.assert_array_equal(oracle.unpack1(packed, 96), w)
+    w[3, 7] = 0
+    assert oracle.pack1(w)[1] == 1
+
+
+def test_binarize_shift_and_sign_symmetries():
+    rng = workloads.rng_for(910, 2)
+    # dyadic entries on a grid of 2^-10: every partial sum is exact
+    W = (rng.integers(-4096, 4096, (32, 64)) / 1024.0).astype(np.float32)  # N K = 2^11
+    w, alpha = oracle.binarize(W)
+    assert Fraction(alpha) == Fraction(int((W.astype(np.float64) * 1024).sum()), 1024 * W.size)
+    w2, alpha2 = oracle.binarize(W + np.float32(0.5))
+    np.testing.assert_array_equal(w2, w)
+    assert alpha2 == alpha + 0.5
+    wn, alphan = oracle.binarize(-W)
+    assert alphan == -alpha
+    tie = W.astype(np.float64) == alpha
+    np.testing.assert_array_equal(wn[~tie], -w[~tie])
+    assert (wn[tie] == -1).all() and (w[tie] == -1).all()
+
+
+def test_binary_weights_closed_form():
+    # with w in {-1, +1}: acc = 2 * sum_{w = +1} q - sum q
+    rng = workloads.rng_for(910, 3)
+    q = rng.integers(-127, 128, (3, 64)).astype(np.int8)
+    w = np.where(rng.random((5, 64)) < 0.5, 1, -1).astype(np.int8)
+    acc = oracle.accumulate(q, w)
+    S = q.astype(np.int64).sum(axis=1)
+    for m in range(3):
+        for n in range(5):
+            pos = q[m].astype(np.int64)[w[n] == 1].sum()
+            assert acc[m, n] == 2 * pos - S[m]
