@@ -57,9 +57,11 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
-    ap.add_argument("--op", choices=("layer", "ternarize"), default="layer",
+    ap.add_argument("--op", choices=("layer", "ternarize", "binary"), default="layer",
                     help="layer: the BitLinear step (default); ternarize: absmean "
-                         "ternarisation + packing of fp32 weights of the workload's shape")
+                         "ternarisation + packing of fp32 weights of the workload's shape; "
+                         "binary: the step on 1-bit Sign(W - alpha) weights "
+                         "(bitlinear_quant_act + bitlinear_forward1 per token count)")
     ap.add_argument("--traffic-probe", metavar="JSON",
                     help="launch every call of one step once, then a plain copy kernel of "
                          f"{COPY_BYTES} bytes, write the launch order to JSON and exit "
@@ -472,6 +474,96 @@ def bench_ternarize(args, torch, bl, dev):
     print(json.dumps(line), flush=True)
 
 
+# ----------------------------------------------------------------------------- 1-bit step
+
+def bench_binary(args, torch, bl, dev):
+    """The decode step of the workload on 1-bit weights: seeded fp32 W
+    N(0.003, 0.02^2) binarised on the GPU (Sign(W - alpha), beta = mean |W|),
+    then per token count quant + bitlinear_forward1; weights rotate through
+    >= 512 MB of copies; steps are HIP graph replays."""
+    wl = workloads.WORKLOADS[args.workload]
+    N, K = wl.N, wl.K
+    W = (workloads.rng_for(args.workload, 31).standard_normal((N, K)) * 0.02 + 0.003).astype(np.float32)
+    packed1, _, _, _, beta, _ = bl.binarize(torch.from_numpy(W).to(dev))
+    beta = float(beta.item())
+    del W
+    wbytes = N * K // 8
+    copies = [packed1] + [packed1.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / wbytes)) - 1)]
+    bufs = []
+    for M in [m for m in wl.ms if m <= 16]:   # decode token counts; more tokens take the 2-bit path
+        x = torch.from_numpy(workloads.workload_activations(args.workload, M)).to(dev)
+        bufs.append(dict(M=M, x=x, q=torch.empty((M, K), dtype=torch.int8, device=dev),
+                         g=torch.empty(M, device=dev), y=torch.empty((M, N), device=dev)))
+    lib = bl.lib
+
+    def stream():
+        return torch.cuda.current_stream(dev).cuda_stream
+
+    def ops(step, only=None):
+        w = copies[step % len(copies)].data_ptr()
+        for b in bufs:
+            M = b["M"]
+            if only in (None, f"quant_act_M{M}"):
+                assert lib.bitlinear_quant_act(b["x"].data_ptr(), bl.F32, M, K, None, 0.0,
+                                               b["q"].data_ptr(), b["g"].data_ptr(), stream()) == 0
+            if only in (None, f"forward1_M{M}"):
+                assert lib.bitlinear_forward1(b["q"].data_ptr(), b["g"].data_ptr(), M, K, w, N, beta,
+                                              b["y"].data_ptr(), None, stream()) == 0
+
+    def graph(only=None):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream(device=dev)
+        with torch.cuda.graph(g, stream=s):
+            for c in range(len(copies)):
+                ops(c, only)
+        return g
+
+    def time_graph(g, per_replay):
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, math.ceil(args.steps / len(copies)))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * per_replay)
+
+    ops(0)
+    torch.cuda.synchronize()
+    us_step = time_graph(graph(), len(copies))
+    per_call = {}
+    for b in bufs:
+        M = b["M"]
+        for name in (f"quant_act_M{M}", f"forward1_M{M}"):
+            per_call[name] = dict(avg_us=round(time_graph(graph(name), len(copies)), 3))
+        alg = wbytes + M * K + 4 * M + 4 * M * N
+        per_call[f"forward1_M{M}"].update(alg_bytes=alg, packed_w_GBs=round(
+            wbytes / (per_call[f"forward1_M{M}"]["avg_us"] * 1e-6) / 1e9, 1))
+    dom = max((k for k in per_call if k.startswith("forward1")), key=lambda k: per_call[k]["avg_us"])
+    d = per_call[dom]
+    gbs = d["alg_bytes"] / (d["avg_us"] * 1e-6) / 1e9
+    line = {
+        "metric": "BitLinear 1-bit weights: packed-W GB/s",
+        "value": round(wbytes * len(bufs) / (us_step * 1e-6) / 1e9, 2),
+        "unit": "packed-W GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_step * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"binary_{wl.name}", "M": [b["M"] for b in bufs], "K": K, "N": N,
+                   "weight_copies": len(copies), "timing": "hip_graph_per_step"},
+        "roofline": dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, call=dom,
+                         kernel="decode_lds_kernel" if int(dom.split("M")[-1]) >= 5 else "gemv1_kernel",
+                         avg_launch_us=d["avg_us"],
+                         alg_bytes_per_launch=d["alg_bytes"]),
+        "cpu_baseline": None,
+        "per_call": per_call,
+    }
+    print(json.dumps(line), flush=True)
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -494,6 +586,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.op == "ternarize":
         bench_ternarize(args, torch, bl, dev)
+        return
+    if args.op == "binary":
+        bench_binary(args, torch, bl, dev)
         return
     if args.traffic_probe:
         args.no_rotate = True

@@ -34,6 +34,9 @@ _SIGNATURES = {
     "bitlinear_forward_path": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, ctypes.c_int, _vp],
     "bitlinear_silu_mul_quant": [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp],
     "bitlinear_ternarize": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
+    "bitlinear_binarize": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "bitlinear_pack_weights1": [_vp, _i64, _i64, _vp, _vp, _vp],
+    "bitlinear_forward1": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _vp],
     "bitlinear_last_error": [],
     "bitlinear_abi_version": [],
 }
@@ -182,6 +185,54 @@ def ternarize(W: torch.Tensor, want_codes: bool = False):
     _check(lib.bitlinear_ternarize(W.data_ptr(), N, K, packed.data_ptr(), _ptr(codes),
                                    beta.data_ptr(), beta64.data_ptr(), _stream(W)))
     return (packed, beta, beta64, codes) if want_codes else (packed, beta, beta64)
+
+
+def binarize(W: torch.Tensor):
+    """Sign(W - alpha) of fp32 weights [N][K] -> (packed1 int32 [N][K/32],
+    codes int8 [N][K], alpha fp32 [1], alpha64 float64 [1], beta fp32 [1],
+    beta64 float64 [1]) on W's device (beta = mean |W|)."""
+    _dev(W, "W", (torch.float32,))
+    N, K = W.shape
+    dev = W.device
+    packed1 = torch.empty((N, K // 32), dtype=torch.int32, device=dev)
+    codes = torch.empty((N, K), dtype=torch.int8, device=dev)
+    sc = [torch.empty((1,), dtype=t, device=dev)
+          for t in (torch.float32, torch.float64, torch.float32, torch.float64)]
+    _check(lib.bitlinear_binarize(W.data_ptr(), N, K, packed1.data_ptr(), codes.data_ptr(),
+                                  *(t.data_ptr() for t in sc), _stream(W)))
+    return (packed1, codes, *sc)
+
+
+def pack_weights1(w: torch.Tensor, check: bool = True):
+    """+-1 int8 [N][K] -> (1-bit packed int32 [N][K/32], bad-count int32 [1])."""
+    _dev(w, "w", (torch.int8,))
+    N, K = w.shape
+    packed1 = torch.empty((N, K // 32), dtype=torch.int32, device=w.device)
+    bad = torch.zeros((1,), dtype=torch.int32, device=w.device)
+    _check(lib.bitlinear_pack_weights1(w.data_ptr(), N, K, packed1.data_ptr(), bad.data_ptr(),
+                                       _stream(w)))
+    if check:
+        n_bad = int(bad.item())
+        if n_bad:
+            raise ValueError(f"{n_bad} weight entries are not -1 or +1")
+    return packed1, bad
+
+
+def forward1(x_q: torch.Tensor, gamma: torch.Tensor, w_packed1: torch.Tensor, beta: float,
+             want_acc: bool = False):
+    """BitLinear on 1-bit weights -> y [M][N] (and acc with ``want_acc``)."""
+    _dev(x_q, "x_q", (torch.int8,))
+    _dev(gamma, "gamma", (torch.float32,))
+    _dev(w_packed1, "w_packed1", (torch.int32, torch.uint32))
+    M, K = x_q.shape
+    N = w_packed1.shape[0]
+    if w_packed1.shape[1] * 32 != K:
+        raise ValueError(f"w_packed1 has {w_packed1.shape[1]} words per row, K={K} needs {K // 32}")
+    y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device) if want_acc else None
+    _check(lib.bitlinear_forward1(x_q.data_ptr(), gamma.data_ptr(), M, K, w_packed1.data_ptr(), N,
+                                  float(beta), y.data_ptr(), _ptr(acc), _stream(x_q)))
+    return (y, acc) if want_acc else y
 
 
 def bitlinear(x: torch.Tensor, w_packed: torch.Tensor, beta: float,

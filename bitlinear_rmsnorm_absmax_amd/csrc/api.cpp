@@ -202,6 +202,76 @@ bitlinear_status_t bitlinear_ternarize(const float* W, int64_t N, int64_t K, uin
                     fn);
 }
 
+bitlinear_status_t bitlinear_binarize(const float* W, int64_t N, int64_t K, uint32_t* w_packed1,
+                                      int8_t* w_codes, float* alpha, double* alpha64, float* beta,
+                                      double* beta64, hipStream_t stream) {
+    const char* fn = "bitlinear_binarize";
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    if (K < 0 || K % 32 != 0 || K > BITLINEAR_MAX_K)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld must be in [0, %d] and a multiple of 32", fn,
+                    (long long)K, BITLINEAR_MAX_K);
+    const bool any = N > 0 && K > 0;
+    if (any && N * (K / 32) > (1LL << 40))
+        return fail(BITLINEAR_ERR_SHAPE, "%s: N*K/32 exceeds 2^40", fn);
+    BL_TRY(need(fn, "W", W, any, 16));
+    BL_TRY(need(fn, "w_packed1", w_packed1, any, 4));
+    BL_TRY(need(fn, "w_codes", w_codes, any, 16));
+    BL_TRY(need(fn, "alpha", alpha, true, 4));
+    BL_TRY(need(fn, "alpha64", alpha64, true, 8));
+    BL_TRY(need(fn, "beta", beta, true, 4));
+    BL_TRY(need(fn, "beta64", beta64, true, 8));
+    if (any) {  // both partial-sum arrays must fit their halves of the code buffer
+        const int64_t L = N * K;
+        if ((int64_t)bl::pairwise_scratch_bytes(L, 256) > ((L / 2) & ~(int64_t)15))
+            return fail(BITLINEAR_ERR_SHAPE, "%s: N*K=%lld too small for the scratch", fn,
+                        (long long)L);
+    }
+    return from_hip(bl::launch_binarize(W, any ? N : 0, any ? K : 0, w_packed1, w_codes, alpha64,
+                                        alpha, beta64, beta, stream),
+                    fn);
+}
+
+bitlinear_status_t bitlinear_pack_weights1(const int8_t* w, int64_t N, int64_t K,
+                                           uint32_t* w_packed1, int32_t* bad_count,
+                                           hipStream_t stream) {
+    const char* fn = "bitlinear_pack_weights1";
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    if (K < 0 || K % 32 != 0 || K > BITLINEAR_MAX_K)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld must be in [0, %d] and a multiple of 32", fn,
+                    (long long)K, BITLINEAR_MAX_K);
+    const bool any = N > 0 && K > 0;
+    BL_TRY(need(fn, "w", w, any, 16));
+    BL_TRY(need(fn, "w_packed1", w_packed1, any, 4));
+    if (bad_count && !aligned(bad_count, 4))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: bad_count is not 4-byte aligned", fn);
+    if (!any && !bad_count) return ok();
+    return from_hip(bl::launch_pack1(w, any ? N : 0, any ? K : 0, w_packed1, bad_count, stream), fn);
+}
+
+bitlinear_status_t bitlinear_forward1(const int8_t* x_q, const float* gamma, int64_t M, int64_t K,
+                                      const uint32_t* w_packed1, int64_t N, float beta, float* y,
+                                      int32_t* acc, hipStream_t stream) {
+    const char* fn = "bitlinear_forward1";
+    BL_TRY(check_rows(fn, "M", M, (1LL << 31) - 1));
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    if (K < 0 || K % 64 != 0 || K > BITLINEAR_MAX_K)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld must be in [0, %d] and a multiple of 64", fn,
+                    (long long)K, BITLINEAR_MAX_K);
+    if (!std::isfinite(beta)) return fail(BITLINEAR_ERR_VALUE, "%s: beta is not finite", fn);
+    const bool any_out = M > 0 && N > 0;
+    const bool any_in = any_out && K > 0;
+    BL_TRY(need(fn, "x_q", x_q, any_in, 16));
+    BL_TRY(need(fn, "gamma", gamma, any_in, 4));
+    BL_TRY(need(fn, "w_packed1", w_packed1, any_in, 8));
+    BL_TRY(need(fn, "y", y, any_out, 4));
+    if (acc && !aligned(acc, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: acc is not 4-byte aligned", fn);
+    if (!any_out) return ok();
+    if (K == 0) return from_hip(bl::launch_fill_zero(y, acc, M * N, stream), fn);
+    return from_hip(bl::launch_forward1(x_q, gamma, (int)M, (int)K, w_packed1, (int)N, beta, y, acc,
+                                        stream),
+                    fn);
+}
+
 const char* bitlinear_last_error(void) { return g_err; }
 
 int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }

@@ -1,5 +1,5 @@
 // Decode product for a few tokens (5 <= M <= 16) on int8 MFMA, activations
-// staged in LDS.
+// staged in LDS; 2-bit ternary weights, or 1-bit weights (ONEBIT).
 //
 // Arithmetic as in the skinny kernel (unite.ai BitNet.cpp article, 3.
 // BitLinear-Betrieb; datacamp MatMul-free article): v_mfma_i32_16x16x64_i8 on
@@ -33,6 +33,7 @@ namespace {
 constexpr int kDecWaves = 8;
 constexpr int kDecMaxBatch = 16;   // 256-K chunks whose weight loads a wave keeps in flight
 constexpr int kDecLdsMax = 160 * 1024;
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -41,7 +42,11 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave_ba
 #endif
 }
 
-template <int CT, int NTW>
+// ONEBIT: 1-bit weights ([N][K/32], entry 4j + b of a word at bit 8b + j):
+// lane (j, g) loads words 8c + 2g, 8c + 2g + 1 of chunk c (the same 64 K
+// positions as the 2-bit words 16c + 4g .. +3), MFMA s takes bits 4(s%2) ..
+// +3 of word s/2, and acc = 2 D - S.
+template <int CT, int NTW, bool ONEBIT>
 __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
     const uint32_t* __restrict__ wp, int N, float beta, float* __restrict__ y,
@@ -56,7 +61,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int cg = wv % CG, kp = wv / CG;
     const int j = lane & 15, g = lane >> 4;
-    const int WR = K >> 4;          // packed words per weight row = 16-byte pieces per activation row
+    const int WR = K >> 4;          // 16-byte pieces per activation row (= 2-bit words per row)
+    const int WRW = ONEBIT ? (K >> 5) : WR;  // weight words per row
     const int nchunks = K >> 8;
     const int n_base = blockIdx.x * (16 * CT) + cg * 16 * NTW;
 
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const uint32_t* wrow[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
-        wrow[t] = wp + (int64_t)min(n_base + 16 * t + j, N - 1) * WR + 4 * g;
+        wrow[t] = wp + (int64_t)min(n_base + 16 * t + j, N - 1) * WRW + (ONEBIT ? 2 : 4) * g;
     // A-operand row of lane j; rows past M repeat row M-1 (never stored)
     const int arow = min(j, M - 1);
     const char* arow_p = As + arow * K;
@@ -92,14 +98,21 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     bool staged = false;
     for (int cb = c_begin; cb < c_end; cb += kDecMaxBatch) {
         const int nb = min(kDecMaxBatch, c_end - cb);  // wave-uniform
-        v4u bw[kDecMaxBatch][NTW];
+        v4u bw[kDecMaxBatch][NTW];  // ONEBIT: .x, .y hold the two words
 #pragma unroll
         for (int i = 0; i < kDecMaxBatch; ++i)
 #pragma unroll
             for (int t = 0; t < NTW; ++t)
-                if (i < nb)
-                    bw[i][t] = __builtin_nontemporal_load(
-                        reinterpret_cast<const v4u*>(wrow[t] + 16 * (cb + i)));
+                if (i < nb) {
+                    if constexpr (ONEBIT) {
+                        const v2u w2 = __builtin_nontemporal_load(
+                            reinterpret_cast<const v2u*>(wrow[t] + 8 * (cb + i)));
+                        bw[i][t] = v4u{w2.x, w2.y, 0u, 0u};
+                    } else {
+                        bw[i][t] = __builtin_nontemporal_load(
+                            reinterpret_cast<const v4u*>(wrow[t] + 16 * (cb + i)));
+                    }
+                }
         if (!staged) {
             stage_activations();
             __syncthreads();  // also waits for this wave's weight loads
@@ -114,9 +127,18 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
                     const int p = 16 * c + 4 * g + s;
                     const v4i a = *reinterpret_cast<const v4i*>(arow_p + 16 * (p ^ axor));
 #pragma unroll
-                    for (int t = 0; t < NTW; ++t)
-                        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_codes(bw[i][t][s]),
-                                                                       acc[t], 0, 0, 0);
+                    for (int t = 0; t < NTW; ++t) {
+                        v4i b;
+                        if constexpr (ONEBIT) {
+                            const uint32_t w = bw[i][t][s >> 1];
+                            const int j0 = 4 * (s & 1);
+                            b = v4i{(int)((w >> j0) & 0x01010101u), (int)((w >> (j0 + 1)) & 0x01010101u),
+                                    (int)((w >> (j0 + 2)) & 0x01010101u), (int)((w >> (j0 + 3)) & 0x01010101u)};
+                        } else {
+                            b = unpack_codes(bw[i][t][s]);
+                        }
+                        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
+                    }
                     accS = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, ones, accS, 0, 0, 0);
                 }
             }
@@ -132,7 +154,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     for (int t = 0; t < NTW; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            red[((wv * NTW + t) * 4 + v) * kWave + lane] = acc[t][v] - accS[v];
+            red[((wv * NTW + t) * 4 + v) * kWave + lane] = (ONEBIT ? 2 * acc[t][v] : acc[t][v]) - accS[v];
     __syncthreads();
     if (kp == 0) {
 #pragma unroll
@@ -161,21 +183,35 @@ size_t decode_lds_bytes(int M, int K, int ntw) {
     return (size_t)decode_a_bytes(M, K) + (size_t)kDecWaves * ntw * 4 * kWave * 4;
 }
 
-template <int CT, int NTW>
+template <int CT, int NTW, bool ONEBIT>
 hipError_t launch_ct(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
                      float beta, float* y, int32_t* acc, hipStream_t s) {
     static bool attr_set = false;  // per-kernel opt-in to more than 64 KB of dynamic LDS
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW>),
+            reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, ONEBIT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int blocks = (N + 16 * CT - 1) / (16 * CT);
-    decode_lds_kernel<CT, NTW><<<dim3(blocks), dim3(kDecWaves * kWave), decode_lds_bytes(M, K, NTW),
-                                 s>>>(xq, gamma, M, K, wp, N, beta, y, acc, decode_a_bytes(M, K));
+    decode_lds_kernel<CT, NTW, ONEBIT><<<dim3(blocks), dim3(kDecWaves * kWave),
+                                         decode_lds_bytes(M, K, NTW), s>>>(
+        xq, gamma, M, K, wp, N, beta, y, acc, decode_a_bytes(M, K));
     return hipGetLastError();
+}
+
+template <bool ONEBIT>
+hipError_t launch_widths(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
+                         int N, float beta, float* y, int32_t* acc, hipStream_t s) {
+    // widest workgroup that still leaves >= 160 workgroups (measured on
+    // N = 2560 .. 28672, K = 2560 .. 8192): fewer, wider groups copy the
+    // activation block fewer times, too few leave CUs idle
+    const int tiles = (N + 15) / 16;
+    if (tiles >= 8 * 160) return launch_ct<8, 2, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (tiles >= 4 * 160) return launch_ct<4, 2, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (tiles >= 2 * 160) return launch_ct<2, 1, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    return launch_ct<1, 1, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
 
 }  // namespace
@@ -188,14 +224,13 @@ bool decode_lds_supports(int M, int K, int N) {
 hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
                              const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                              hipStream_t s) {
-    // widest workgroup that still leaves >= 160 workgroups (measured on
-    // N = 2560 .. 28672, K = 2560 .. 8192): fewer, wider groups copy the
-    // activation block fewer times, too few leave CUs idle
-    const int tiles = (N + 15) / 16;
-    if (tiles >= 8 * 160) return launch_ct<8, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    if (tiles >= 4 * 160) return launch_ct<4, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    if (tiles >= 2 * 160) return launch_ct<2, 1>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    return launch_ct<1, 1>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    return launch_widths<false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+}
+
+hipError_t launch_decode_lds1(const int8_t* xq, const float* gamma, int M, int K,
+                              const uint32_t* wp1, int N, float beta, float* y, int32_t* acc,
+                              hipStream_t s) {
+    return launch_widths<true>(xq, gamma, M, K, wp1, N, beta, y, acc, s);
 }
 
 }  // namespace bl

@@ -38,12 +38,34 @@ bool decode_lds_supports(int M, int K, int N);
 hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
                              const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                              hipStream_t s);
+// Same kernel on 1-bit weights [N][K/32].
+hipError_t launch_decode_lds1(const int8_t* xq, const float* gamma, int M, int K,
+                              const uint32_t* wp1, int N, float beta, float* y, int32_t* acc,
+                              hipStream_t s);
 
 // Path 3: LDS-tiled int8 MFMA GEMM.  The LDS-ring variant needs K % 128 == 0.
 bool gemm_dma_supports(int M, int K, int N);
 
-// Absmean ternarisation + packing (three stream-ordered launches; the packed
-// buffer holds the per-row sums in between, so K >= 32).
+// Pairwise double mean of |W| (abs_values) or W over L = N*K entries, leaf
+// groups of `group` (64 or 256) entries; scratch of pairwise_scratch_bytes().
+hipError_t launch_pairwise_mean(const float* W, int64_t L, int64_t N, int64_t K, bool abs_values,
+                                int group, double* scratch, double* mean64, float* mean32,
+                                hipStream_t s);
+size_t pairwise_scratch_bytes(int64_t L, int group);
+
+// 1-bit weights: binarisation Sign(W - alpha) + packing (the partial sums live
+// in the int8 code output), packing of +-1 weights, and the decode product
+// (groups of up to four tokens per pass over the weights; K % 64 == 0).
+hipError_t launch_binarize(const float* W, int64_t N, int64_t K, uint32_t* packed1, int8_t* codes,
+                           double* alpha64, float* alpha32, double* beta64, float* beta32,
+                           hipStream_t s);
+hipError_t launch_pack1(const int8_t* w, int64_t N, int64_t K, uint32_t* packed1, int* bad_count,
+                        hipStream_t s);
+hipError_t launch_forward1(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
+                           int N, float beta, float* y, int32_t* acc, hipStream_t s);
+
+// Absmean ternarisation + packing (stream-ordered launches; the packed buffer
+// holds the partial sums in between, so K >= 32).
 hipError_t launch_ternarize(const float* W, int64_t N, int64_t K, uint32_t* packed, int8_t* codes,
                             float* beta32, double* beta64, hipStream_t s);
 hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,

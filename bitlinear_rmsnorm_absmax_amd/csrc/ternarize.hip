@@ -22,6 +22,8 @@
 //      bit 8b + 2j, the layout of bitlinear_pack_weights).
 // The partial sums live in the packed output buffer (about N*K/8 bytes of
 // its N*K/4), ping-ponging between two regions; step 3 overwrites them.
+// launch_pairwise_mean is also the mean of the weight binarisation (signed
+// entries, 256-entry leaf groups: the same tree, a quarter of the scratch).
 #include "device_common.h"
 #include "internal.h"
 
@@ -34,26 +36,31 @@ __device__ __forceinline__ double xor_pair_sum(double v, int mask) {
     return v + __shfl_xor(v, mask, kWave);
 }
 
-// Pass 1: group g = entries [64g, 64g + 64) of the flat matrix (zero past L).
-__global__ __launch_bounds__(kTernBlock) void abs_group_sums_kernel(const float* __restrict__ W,
-                                                                    int64_t L, int64_t groups,
-                                                                    double* __restrict__ out) {
+// Pass 1: group g = entries [G g, G g + G) of the flat matrix (zero past L),
+// G = 64 (16 lanes per group) or 256 (the whole wave); ABS: |W| else W.
+template <int G, bool ABS>
+__global__ __launch_bounds__(kTernBlock) void group_sums_leaf_kernel(const float* __restrict__ W,
+                                                                     int64_t L, int64_t groups,
+                                                                     double* __restrict__ out) {
+    constexpr int kLanes = G / 4;  // lanes per group
     const int lane = threadIdx.x % kWave;
     const int64_t wave = ((int64_t)blockIdx.x * kTernBlock + threadIdx.x) / kWave;
-    const int64_t base = wave * 1024;  // 16 groups per wave
+    const int64_t base = wave * 1024;  // 1024 / G groups per wave
     if (base >= L) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t e = base + 256 * i + 4 * lane;  // entries e .. e+3, group e / 64
+        const int64_t e = base + 256 * i + 4 * lane;  // entries e .. e+3, group e / G
         v4f v = v4f{0.f, 0.f, 0.f, 0.f};
         if (e < L) v = *reinterpret_cast<const v4f*>(W + e);  // L % 16 == 0: all four or none
-        double s = (fabs((double)v.x) + fabs((double)v.y)) + (fabs((double)v.z) + fabs((double)v.w));
-        s = xor_pair_sum(s, 1);
-        s = xor_pair_sum(s, 2);
-        s = xor_pair_sum(s, 4);
-        s = xor_pair_sum(s, 8);
-        const int64_t g = e / 64;
-        if ((lane & 15) == 0 && g < groups) out[g] = s;
+        double s;
+        if constexpr (ABS)
+            s = (fabs((double)v.x) + fabs((double)v.y)) + (fabs((double)v.z) + fabs((double)v.w));
+        else
+            s = ((double)v.x + (double)v.y) + ((double)v.z + (double)v.w);
+#pragma unroll
+        for (int m = 1; m < kLanes; m <<= 1) s = xor_pair_sum(s, m);
+        const int64_t g = e / G;
+        if ((lane % kLanes) == 0 && g < groups) out[g] = s;
     }
 }
 
@@ -127,21 +134,26 @@ int64_t waves_to_blocks(int64_t waves) { return (waves * kWave + kTernBlock - 1)
 
 }  // namespace
 
-hipError_t launch_ternarize(const float* W, int64_t N, int64_t K, uint32_t* packed, int8_t* codes,
-                            float* beta32, double* beta64, hipStream_t s) {
-    if (N == 0 || K == 0) {  // empty matrix: beta = 0, nothing else written
-        finish_kernel<<<dim3(1), dim3(kWave), 0, s>>>(nullptr, 0, 0, 0, beta64, beta32);
+hipError_t launch_pairwise_mean(const float* W, int64_t L, int64_t N, int64_t K, bool abs_values,
+                                int group, double* scratch, double* mean64, float* mean32,
+                                hipStream_t s) {
+    if (L == 0) {
+        finish_kernel<<<dim3(1), dim3(kWave), 0, s>>>(nullptr, 0, 0, 0, mean64, mean32);
         return hipGetLastError();
     }
-    const int64_t L = N * K;
-    int64_t n = (L + 63) / 64;  // group sums after the leaf pass
-    // region A: n doubles at the start of the packed buffer; region B (at most
-    // n/64 + 1 doubles) right after.  Level passes run only while n > 64, i.e.
-    // L > 4096, where 8 * (n + n/64 + 1) bytes stay below the buffer's L/4.
-    double* a = reinterpret_cast<double*>(packed);
+    int64_t n = (L + group - 1) / group;  // group sums after the leaf pass
+    // region A: n doubles at `scratch`; region B (at most n/64 + 1 doubles)
+    // right after; level passes run only while n > 64
+    double* a = scratch;
     double* b = a + n;
-    abs_group_sums_kernel<<<dim3((unsigned)waves_to_blocks((L + 1023) / 1024)), dim3(kTernBlock), 0,
-                            s>>>(W, L, n, a);
+    const dim3 leaf_grid((unsigned)waves_to_blocks((L + 1023) / 1024));
+    if (group == 64) {
+        if (abs_values) group_sums_leaf_kernel<64, true><<<leaf_grid, dim3(kTernBlock), 0, s>>>(W, L, n, a);
+        else group_sums_leaf_kernel<64, false><<<leaf_grid, dim3(kTernBlock), 0, s>>>(W, L, n, a);
+    } else {
+        if (abs_values) group_sums_leaf_kernel<256, true><<<leaf_grid, dim3(kTernBlock), 0, s>>>(W, L, n, a);
+        else group_sums_leaf_kernel<256, false><<<leaf_grid, dim3(kTernBlock), 0, s>>>(W, L, n, a);
+    }
     double* src = a;
     double* dst = b;
     while (n > 64) {
@@ -153,7 +165,22 @@ hipError_t launch_ternarize(const float* W, int64_t N, int64_t K, uint32_t* pack
         src = dst;
         dst = t;
     }
-    finish_kernel<<<dim3(1), dim3(kWave), 0, s>>>(src, n, N, K, beta64, beta32);
+    finish_kernel<<<dim3(1), dim3(kWave), 0, s>>>(src, n, N, K, mean64, mean32);
+    return hipGetLastError();
+}
+
+size_t pairwise_scratch_bytes(int64_t L, int group) {
+    const int64_t n = (L + group - 1) / group;
+    return (size_t)8 * (size_t)(n + (n > 64 ? (n + 63) / 64 : 0));
+}
+
+hipError_t launch_ternarize(const float* W, int64_t N, int64_t K, uint32_t* packed, int8_t* codes,
+                            float* beta32, double* beta64, hipStream_t s) {
+    const int64_t L = N * K;
+    // the partial sums (about L/8 bytes) live in the packed buffer (L/4 bytes)
+    hipError_t e = launch_pairwise_mean(W, L, N, K, true, 64, reinterpret_cast<double*>(packed),
+                                        beta64, beta32, s);
+    if (e != hipSuccess || L == 0) return e;
     const int64_t words = L / 16;
     ternarize_pack_kernel<<<dim3((unsigned)((words + kTernBlock - 1) / kTernBlock)),
                             dim3(kTernBlock), 0, s>>>(W, words, beta64, packed, codes);

@@ -178,6 +178,59 @@ bitlinear_status_t bitlinear_ternarize(const float* W, int64_t N, int64_t K, uin
                                        int8_t* w_ternary, float* beta, double* beta64,
                                        hipStream_t stream);
 
+/*
+ * 1-bit weights (unite.ai article "Microsofts Inference Framework bringt 1-Bit
+ * große Sprachmodelle auf lokale Geräte", section "Mathematische Grundlagen",
+ * 1. Gewichtsbinarisierung: W_f = Sign(W - alpha), alpha the mean of the
+ * weights, Sign(v) = +1 for v > 0 and -1 otherwise).
+ *
+ * 1-bit packed layout: uint32 [N][K/32]; word n*(K/32) + k/32 holds entry
+ * e = k mod 32 = 4j + b at bit 8b + j as (w + 1) / 2 (so +1 -> 1, -1 -> 0).
+ * The +-1 codes are also valid ternary codes: bitlinear_pack_weights turns
+ * them into the 2-bit layout for bitlinear_forward (the path for many tokens).
+ */
+
+/*
+ * bitlinear_binarize -- alpha64 = pairwise double sum of W over the row-major
+ * entries (as in bitlinear_ternarize) / (N*K); code = +1 if W > alpha64
+ * (exact comparison in double), else -1 (W == alpha64 gives -1).  Also the
+ * scale beta64 = mean |W| (the absmean of bitlinear_ternarize).
+ *
+ * W          device fp32 [N][K] row-major, 16-byte aligned, finite.
+ * w_packed1  device uint32 [N][K/32] out (1-bit layout), 4-byte aligned.
+ * w_codes    device int8 [N][K] out, the +-1 codes, 16-byte aligned.  While
+ *            the call runs it also holds the partial sums of both means.
+ * alpha, beta      device fp32 [1] out: fl32(alpha64), fl32(beta64).
+ * alpha64, beta64  device double [1] out.
+ * N, K       N >= 0; K % 32 == 0, K <= BITLINEAR_MAX_K; N*K == 0 writes the
+ *            four scalars as 0 and nothing else.
+ */
+bitlinear_status_t bitlinear_binarize(const float* W, int64_t N, int64_t K, uint32_t* w_packed1,
+                                      int8_t* w_codes, float* alpha, double* alpha64, float* beta,
+                                      double* beta64, hipStream_t stream);
+
+/*
+ * bitlinear_pack_weights1 -- +-1 int8 weights [N][K] (device, 16-byte aligned,
+ * K % 32 == 0) -> the 1-bit layout [N][K/32].  bad_count (optional device
+ * int32) receives the number of entries that are not +-1 (packed as -1).
+ */
+bitlinear_status_t bitlinear_pack_weights1(const int8_t* w, int64_t N, int64_t K,
+                                           uint32_t* w_packed1, int32_t* bad_count,
+                                           hipStream_t stream);
+
+/*
+ * bitlinear_forward1 -- bitlinear_forward on 1-bit weights: acc_mn =
+ * sum_k w_nk q_mk with w in {-1, +1}, y = fl32(acc) * (fl32(beta * gamma_m)/128).
+ * Arguments as for bitlinear_forward; w_packed1 is [N][K/32] in the 1-bit
+ * layout (8-byte aligned) and K % 64 == 0.  A decode product: 5..16 tokens
+ * (K % 256 == 0, activations fitting in LDS) run on int8 MFMA, other counts
+ * on the vector ALUs with one pass over the weights per four tokens; for many
+ * tokens pack the codes for bitlinear_forward.
+ */
+bitlinear_status_t bitlinear_forward1(const int8_t* x_q, const float* gamma, int64_t M, int64_t K,
+                                      const uint32_t* w_packed1, int64_t N, float beta, float* y,
+                                      int32_t* acc, hipStream_t stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 const char* bitlinear_last_error(void);
 

@@ -19,6 +19,7 @@ def test_every_declared_symbol_is_exported():
     assert set(declared) == {
         "bitlinear_quant_act", "bitlinear_pack_weights", "bitlinear_forward",
         "bitlinear_forward_path", "bitlinear_silu_mul_quant", "bitlinear_ternarize",
+        "bitlinear_binarize", "bitlinear_pack_weights1", "bitlinear_forward1",
         "bitlinear_last_error", "bitlinear_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -164,4 +165,53 @@ def _tern(W=FAKE, N=1, K=32, packed=FAKE, codes=None, beta=FAKE, beta64=FAKE):
 ])
 def test_ternarize_rejects(kw, status, msg):
     assert _tern(**kw) == status
+    assert msg in bl.last_error()
+
+
+def _bin(W=FAKE, N=1, K=64, p1=FAKE, codes=FAKE, a=FAKE, a64=FAKE, b=FAKE, b64=FAKE):
+    return bl.lib.bitlinear_binarize(W, N, K, p1, codes, a, a64, b, b64, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(W=None), bl.ERR_NULL, "W is NULL"),
+    (dict(codes=None), bl.ERR_NULL, "w_codes is NULL"),
+    (dict(p1=None), bl.ERR_NULL, "w_packed1 is NULL"),
+    (dict(a64=None, N=0), bl.ERR_NULL, "alpha64 is NULL"),
+    (dict(b=None), bl.ERR_NULL, "beta is NULL"),
+    (dict(K=48), bl.ERR_SHAPE, "multiple of 32"),
+    (dict(codes=FAKE + 8), bl.ERR_ALIGN, "w_codes is not 16-byte aligned"),
+    (dict(a64=FAKE + 4), bl.ERR_ALIGN, "alpha64 is not 8-byte aligned"),
+])
+def test_binarize_rejects(kw, status, msg):
+    assert _bin(**kw) == status
+    assert msg in bl.last_error()
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((None, 1, 32, FAKE, None), bl.ERR_NULL, "w is NULL"),
+    ((FAKE, 1, 32, None, None), bl.ERR_NULL, "w_packed1 is NULL"),
+    ((FAKE, 1, 16, FAKE, None), bl.ERR_SHAPE, "multiple of 32"),
+    ((FAKE + 4, 1, 32, FAKE, None), bl.ERR_ALIGN, "w is not 16-byte aligned"),
+    ((FAKE, 1, 32, FAKE, FAKE + 1), bl.ERR_ALIGN, "bad_count"),
+])
+def test_pack1_rejects(args, status, msg):
+    assert bl.lib.bitlinear_pack_weights1(*args, None) == status
+    assert msg in bl.last_error()
+
+
+def _fwd1(xq=FAKE, g=FAKE, M=1, K=64, w=FAKE, N=1, beta=1.0, y=FAKE, acc=None):
+    return bl.lib.bitlinear_forward1(xq, g, M, K, w, N, F(beta), y, acc, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(xq=None), bl.ERR_NULL, "x_q is NULL"),
+    (dict(w=None), bl.ERR_NULL, "w_packed1 is NULL"),
+    (dict(y=None), bl.ERR_NULL, "y is NULL"),
+    (dict(K=32), bl.ERR_SHAPE, "multiple of 64"),
+    (dict(beta=float("inf")), bl.ERR_VALUE, "beta is not finite"),
+    (dict(w=FAKE + 4), bl.ERR_ALIGN, "w_packed1 is not 8-byte aligned"),
+    (dict(M=-1), bl.ERR_SHAPE, "M=-1"),
+])
+def test_forward1_rejects(kw, status, msg):
+    assert _fwd1(**kw) == status
     assert msg in bl.last_error()

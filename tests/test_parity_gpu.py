@@ -446,3 +446,87 @@ def test_ternarize_then_forward(dev):
     y_ref, acc_ref = oracle.forward(q_ref, g_ref, w_ref, np.float32(b_ref))
     np.testing.assert_array_equal(host(acc), acc_ref)
     assert_y_close(host(y), y_ref)
+
+
+
+# ------------------------------------------------------------------ 1-bit weights
+
+def _binarize_check(W, dev):
+    packed1, codes, alpha, alpha64, beta, beta64 = bl.binarize(to_dev(W, dev))
+    w_ref, a_ref = oracle.binarize(W)
+    _, b_ref = oracle.ternarize(W)                 # beta = the absmean of the same tree
+    assert float(host(alpha64)[0]) == a_ref
+    assert host(alpha)[0] == np.float32(a_ref)
+    assert float(host(beta64)[0]) == b_ref
+    assert host(beta)[0] == np.float32(b_ref)
+    np.testing.assert_array_equal(host(codes), w_ref)
+    p_ref, bad = oracle.pack1(w_ref)
+    assert bad == 0
+    np.testing.assert_array_equal(host(packed1).view(np.uint32), p_ref)
+    return w_ref, packed1, codes, float(host(beta)[0])
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (3, 96), (257, 512), (1000, 4096), (11008, 4096)])
+def test_binarize_parity(dev, N, K):
+    rng = workloads.rng_for(960, N, K)
+    W = (rng.standard_normal((N, K)) * 0.02 + 0.003).astype(np.float32)
+    _binarize_check(W, dev)
+
+
+def test_binarize_ties_on_gpu(dev):
+    g = json.load(open(os.path.join(GOLDEN, "binarize_2x32.json")))
+    W = np.array(g["W"], np.float32)
+    w_ref, packed1, _, _ = _binarize_check(W, dev)
+    np.testing.assert_array_equal(w_ref, np.array(g["codes"], np.int8))
+    np.testing.assert_array_equal(host(packed1).view(np.uint32), np.array(g["packed"], np.uint32))
+
+
+def test_pack_weights1_parity(dev):
+    rng = workloads.rng_for(961, 1)
+    w = np.where(rng.random((300, 640)) < 0.5, 1, -1).astype(np.int8)
+    packed1, _ = bl.pack_weights1(to_dev(w, dev))
+    np.testing.assert_array_equal(host(packed1).view(np.uint32), oracle.pack1(w)[0])
+    w[5, 9] = 0
+    w[7, 1] = 2
+    _, bad = bl.pack_weights1(to_dev(w, dev), check=False)
+    assert int(host(bad)[0]) == 2
+
+
+# 1..4 tokens and K % 256 != 0: vector-ALU kernel; 5..16 tokens with K % 256 == 0:
+# the LDS-staged MFMA kernel in its 1-bit form (all four workgroup widths);
+# 17 and 20 tokens: several vector-ALU passes
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (2, 17, 192), (3, 1000, 4096), (4, 333, 2560),
+                                   (5, 640, 1024), (9, 100, 64), (1, 11008, 4096),
+                                   (7, 5200, 512), (12, 10300, 1024), (16, 20500, 768),
+                                   (16, 333, 8192), (17, 200, 512), (20, 96, 320)])
+def test_forward1_parity(dev, M, N, K):
+    rng = workloads.rng_for(962, M, N, K)
+    w = np.where(rng.random((N, K)) < 0.5, 1, -1).astype(np.int8)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    if M > 2:
+        x[1] = 0.0
+    q, g = bl.quant_act(to_dev(x, dev))
+    packed1, _ = bl.pack_weights1(to_dev(w, dev))
+    y, acc = bl.forward1(q, g, packed1, 0.02, want_acc=True)
+    q_ref, g_ref = oracle.quant_act(x)
+    np.testing.assert_array_equal(host(q), q_ref)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, np.float32(0.02))
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    assert_y_close(host(y), y_ref)
+
+
+def test_binarize_then_both_forward_paths(dev):
+    # fp weights -> +-1 codes on the GPU -> the 1-bit decode product and the
+    # 2-bit path (codes packed by bitlinear_pack_weights) agree bit for bit
+    rng = workloads.rng_for(963, 1)
+    N, K, M = 700, 2048, 3
+    W = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    w_ref, packed1, codes, beta = _binarize_check(W, dev)
+    q, g = bl.quant_act(to_dev(rng.standard_normal((M, K)).astype(np.float32), dev))
+    y1, acc1 = bl.forward1(q, g, packed1, beta, want_acc=True)
+    packed2, _ = bl.pack_weights(codes)
+    y2, acc2 = bl.forward(q, g, packed2, beta, want_acc=True)
+    np.testing.assert_array_equal(host(acc1), host(acc2))
+    np.testing.assert_array_equal(host(y1), host(y2))
+    y_ref, acc_ref = oracle.forward(host(q), host(g), w_ref, np.float32(beta))
+    np.testing.assert_array_equal(host(acc1), acc_ref)
