@@ -486,6 +486,7 @@ def bench_binary(args, torch, bl, dev):
     W = (workloads.rng_for(args.workload, 31).standard_normal((N, K)) * 0.02 + 0.003).astype(np.float32)
     packed1, _, _, _, beta, _ = bl.binarize(torch.from_numpy(W).to(dev))
     beta = float(beta.item())
+    cpu = binary_cpu_baseline(args, W, beta, args.cpu_seconds) if args.cpu_seconds > 0 else None
     del W
     wbytes = N * K // 8
     copies = [packed1] + [packed1.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / wbytes)) - 1)]
@@ -558,10 +559,38 @@ def bench_binary(args, torch, bl, dev):
                          kernel="decode_lds_kernel" if int(dom.split("M")[-1]) >= 5 else "gemv1_kernel",
                          avg_launch_us=d["avg_us"],
                          alg_bytes_per_launch=d["alg_bytes"]),
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
         "per_call": per_call,
     }
     print(json.dumps(line), flush=True)
+
+
+def binary_cpu_baseline(args, W, beta, seconds):
+    """The oracle's quantisation + product on the oracle's own binarisation of
+    the same W, whole decode steps over a bounded slice of output rows."""
+    import oracle
+    wl = workloads.WORKLOADS[args.workload]
+    ms = [m for m in wl.ms if m <= 16]
+    xs = [workloads.workload_activations(args.workload, M) for M in ms]
+    est = sum(ms) * W.size * 1.5e-9
+    rows = W.shape[0]
+    if est / max(oracle.num_threads(), 1) > seconds:
+        rows = max(64, int(rows * seconds * oracle.num_threads() / est / 3))
+    w, _ = oracle.binarize(np.ascontiguousarray(W[:rows]))
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for x in xs:
+            q, g = oracle.quant_act(x)
+            oracle.forward(q, g, w, beta)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or el / n * (n + 1) > 3 * seconds:
+            break
+    return dict(value=round(w.size // 8 * len(ms) * n / el / 1e9, 4), unit="packed-W GB/s",
+                cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n} x (decode steps over {rows} of {W.shape[0]} output rows, +-1 weights "
+                       f"unpacked), M={ms}, {el:.1f} s")
 
 
 # ----------------------------------------------------------------------------- main
