@@ -13,8 +13,8 @@ the step.
 Inputs are seeded synthetic draws (workloads.py), resident in HBM before the
 timed region.  The packed weights rotate through at least 512 MB of copies so
 that consecutive steps cannot be served from the 256 MB Infinity Cache.
-Timed steps are replays of HIP graphs (one per weight copy), so host launch
-overhead does not pace the GPU.  Per-call kernel durations come from a second
+The K timed steps are one replay of a HIP graph holding all K of them, so
+host launch overhead does not pace the GPU.  Per-call kernel durations come from a second
 pass: for each call of the step, a HIP graph of that call alone, once per
 weight copy, replayed between two HIP events on the stream the kernels run on;
 the dominant forward call gives the roofline.
@@ -632,33 +632,40 @@ def main():
           f"{meta['weight_copies']} weight copies", file=sys.stderr, flush=True)
 
     ncopy = meta["weight_copies"]
-    graphs = None
-    if not args.eager:
-        graphs = []
-        s = torch.cuda.Stream(device=dev)
-        for c in range(ncopy):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                ops(c, RunAll())
-            graphs.append(g)
-        torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=dev)
 
-    def run(i):
-        if graphs is not None:
-            graphs[i % ncopy].replay()
+    def steps_graph(first, count):
+        """One HIP graph of `count` consecutive steps (step i uses weight copy
+        i mod ncopy): a single replay launches them all, so the host does not
+        pace the GPU between steps."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(first, first + count):
+                ops(i, RunAll())
+        return g
+
+    def run_steps(first, count):
+        if count <= 0:
+            return
+        if args.eager:
+            for i in range(first, first + count):
+                ops(i, RunAll())
         else:
-            ops(i, RunAll())
+            steps_graph(first, count).replay()
 
-    for i in range(args.warmup):
-        run(i)
+    run_steps(0, args.warmup)
+    timed = None if args.eager else steps_graph(args.warmup, args.steps)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(args.steps):
-        run(args.warmup + i)
+    if timed is not None:
+        timed.replay()
+    else:
+        run_steps(args.warmup, args.steps)
     e1.record()
     torch.cuda.synchronize()
+    del timed
     ms_step = e0.elapsed_time(e1) / args.steps
     print(f"# timed {args.steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
 
@@ -666,7 +673,7 @@ def main():
     # weight copy, replayed from one HIP graph (eager: from the host)
     kern = {}
     for name, per_step in rec.calls.items():
-        if graphs is None:
+        if args.eager:
             t = RunOne(torch, name)
             for i in range(args.steps):
                 ops(args.warmup + i, t)
@@ -732,7 +739,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": meta["workload"], "M": meta["M"], "K": meta["K"], "N": meta["N"],
                    "weight_copies": meta["weight_copies"],
-                   "timing": "eager" if args.eager else "hip_graph_per_step",
+                   "timing": "eager" if args.eager else "hip_graph_of_all_timed_steps",
                    "int8_eq_TOPS_per_step": round(meta["ops_per_step"] / (ms_step * 1e-3) / 1e12, 3),
                    "hbm_frac_per_step": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roof,
