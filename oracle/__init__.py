@@ -56,6 +56,8 @@ def _load() -> ctypes.CDLL:
             "oracle_binarize": [_c_p, _i64, _i64, _c_p],
             "oracle_pack1": [_c_p, _i64, _i64, _c_p],
             "oracle_unpack1": [_c_p, _i64, _i64, _c_p],
+            "oracle_quant_act_grouped": [_c_p, _c_p, ctypes.c_float, _i64, _i64, _i64, _c_p,
+                                         _c_p],
             "oracle_num_threads": [],
         }
         for name, args in sig.items():
@@ -69,6 +71,7 @@ def _load() -> ctypes.CDLL:
         lib.oracle_pack1.restype = ctypes.c_int64
         lib.oracle_unpack1.restype = None
         for name in ("oracle_bf16_to_f32", "oracle_quant_act", "oracle_rmsnorm_quant_act",
+                     "oracle_quant_act_grouped",
                      "oracle_rmsnorm_quant_act_literal", "oracle_unpack", "oracle_rescale",
                      "oracle_silu_mul"):
             getattr(lib, name).restype = None
@@ -108,6 +111,26 @@ def rmsnorm_quant_act(x: np.ndarray, gain: np.ndarray, eps: float) -> Tuple[np.n
     q = np.empty((M, K), dtype=np.int8)
     g = np.empty((M,), dtype=np.float32)
     _load().oracle_rmsnorm_quant_act(_p(x), _p(gain), float(np.float32(eps)), M, K, _p(q), _p(g))
+    return q, g
+
+
+def quant_act_grouped(x: np.ndarray, groups: int, gain: Optional[np.ndarray] = None,
+                      eps: float = 1e-6) -> Tuple[np.ndarray, np.ndarray]:
+    """Group quantisation (unite.ai article, Gruppenquantisierung): fp32 x
+    [M][K] -> (q int8 [G][M][K/G], gamma fp32 [G][M]), each run of K/G inputs
+    of each token with its own absmax scale; optional RMSNorm gain."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    G = int(groups)
+    if G < 1 or K % G:
+        raise ValueError("K must be a positive multiple of the group count")
+    q = np.empty((G, M, K // G), dtype=np.int8)
+    g = np.empty((G, M), dtype=np.float32)
+    gp = None
+    if gain is not None:
+        gain = _c(gain, np.float32)
+        gp = _p(gain)
+    _load().oracle_quant_act_grouped(_p(x), gp, float(np.float32(eps)), M, K, G, _p(q), _p(g))
     return q, g
 
 
@@ -208,6 +231,49 @@ def forward(q: np.ndarray, gamma: np.ndarray, w: np.ndarray, beta: float):
     """BitLinear on quantised activations -> (y fp32 [M][N], acc int32 [M][N])."""
     acc = accumulate(q, w)
     return rescale(acc, gamma, beta), acc
+
+
+def forward_grouped(q: np.ndarray, gamma: np.ndarray, w: np.ndarray, beta: np.ndarray):
+    """Grouped BitLinear (unite.ai article, Gruppenquantisierung, with
+    3. BitLinear-Betrieb per group): q int8 [G][M][K/G], gamma [G][M], ternary
+    w int8 [N][K] (group g = columns g*K/G .. (g+1)*K/G), beta [G] ->
+    (y fp32 [M][N], acc int32 [G][M][N]).  acc[g] is group g's exact product;
+    y = sum over g of acc[g] * beta[g] * gamma[g] / 128 in float64, rounded
+    once to fp32."""
+    q = _c(q, np.int8)
+    G, M, KG = q.shape
+    w = _c(w, np.int8)
+    N = w.shape[0]
+    if w.shape[1] != G * KG:
+        raise ValueError("K mismatch")
+    gamma = _c(gamma, np.float32).reshape(G, M)
+    beta = _c(beta, np.float32).reshape(G)
+    acc = np.empty((G, M, N), dtype=np.int32)
+    y64 = np.zeros((M, N), dtype=np.float64)
+    for g in range(G):
+        acc[g] = accumulate(q[g], w[:, g * KG:(g + 1) * KG])
+        y64 += acc[g].astype(np.float64) * float(beta[g]) * gamma[g].astype(np.float64)[:, None] / 128.0
+    return y64.astype(np.float32), acc
+
+
+def ternarize_grouped(W: np.ndarray, groups: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Absmean ternarisation per group of K/G input columns (datacamp article's
+    absmean rule applied per group, unite.ai article, Gruppenquantisierung):
+    fp32 W [N][K] -> (ternary int8 [N][K], beta float64 [G]); group g's beta
+    is the pairwise float64 mean |W| over the row-major entries of its
+    N x K/G block."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    G = int(groups)
+    if G < 1 or K % G:
+        raise ValueError("K must be a positive multiple of the group count")
+    KG = K // G
+    w = np.empty((N, K), dtype=np.int8)
+    betas = np.empty(G, dtype=np.float64)
+    for g in range(G):
+        wg, betas[g] = ternarize(np.ascontiguousarray(W[:, g * KG:(g + 1) * KG]))
+        w[:, g * KG:(g + 1) * KG] = wg
+    return w, betas
 
 
 def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:

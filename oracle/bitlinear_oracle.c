@@ -93,6 +93,38 @@ void oracle_rmsnorm_quant_act(const float* x, const float* g, float eps, int64_t
     free(u);
 }
 
+/* Group quantisation ([U] Gruppenquantisierung und -normalisierung: weights
+ * and activations are divided into G groups and the quantisation parameters
+ * are computed per group instead of for the whole matrix).  Groups split the
+ * K inputs into G equal runs; token m's run g gets its own absmax scale
+ * gamma[g][m] and codes q[g][m][0 .. K/G).  With a gain (RMSNorm), r is the
+ * token's whole-row factor and gamma[g][m] = fl32(r * max over the run of
+ * |u|), u = fl32(gain * x), as in the ungrouped variant.  Outputs are
+ * group-major: q [G][M][K/G], gamma [G][M]. */
+void oracle_quant_act_grouped(const float* x, const float* gain, float eps, int64_t M,
+                              int64_t K, int64_t G, int8_t* q, float* gamma) {
+    const int64_t KG = K / G;
+    float* u = (float*)malloc((size_t)(KG > 0 ? KG : 1) * sizeof(float));
+    for (int64_t m = 0; m < M; ++m) {
+        const float* xm = x + m * K;
+        double r = 1.0;
+        if (gain) {
+            double ss = 0.0;
+            for (int64_t k = 0; k < K; ++k) ss += (double)xm[k] * (double)xm[k];
+            r = 1.0 / sqrt((K > 0 ? ss / (double)K : 0.0) + (double)eps);
+        }
+        for (int64_t g = 0; g < G; ++g) {
+            for (int64_t k = 0; k < KG; ++k) {
+                const float xv = xm[g * KG + k];
+                u[k] = gain ? gain[g * KG + k] * xv : xv;
+            }
+            const float absmax = quant_row(u, KG, q + (g * M + m) * KG);
+            gamma[g * M + m] = gain ? (float)(r * (double)absmax) : absmax;
+        }
+    }
+    free(u);
+}
+
 /* The same two steps evaluated literally in float64: normalise, then quantise
  * the normalised vector.  Codes may differ from the fp32 contract only where
  * the scaled value sits within rounding distance of a half-integer. */

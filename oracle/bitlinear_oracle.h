@@ -40,6 +40,13 @@ void oracle_quant_act(const float* x, int64_t M, int64_t K, int8_t* q, float* ga
 void oracle_rmsnorm_quant_act(const float* x, const float* g, float eps, int64_t M,
                               int64_t K, int8_t* q, float* gamma);
 
+/* Group quantisation ([U] Gruppenquantisierung und -normalisierung): the K
+ * inputs split into G equal runs, each run of each token quantised with its
+ * own absmax scale.  gain NULL = no RMSNorm.  q int8 [G][M][K/G],
+ * gamma fp32 [G][M] (group-major).  K % G == 0. */
+void oracle_quant_act_grouped(const float* x, const float* gain, float eps, int64_t M,
+                              int64_t K, int64_t G, int8_t* q, float* gamma);
+
 /* Literal RMSNorm-then-quantise evaluated in float64 (informational). */
 void oracle_rmsnorm_quant_act_literal(const float* x, const float* g, float eps,
                                       int64_t M, int64_t K, int8_t* q, double* gamma);

@@ -502,3 +502,128 @@ def test_binary_weights_closed_form():
         for n in range(5):
             pos = q[m].astype(np.int64)[w[n] == 1].sum()
             assert acc[m, n] == 2 * pos - S[m]
+
+
+# ---------------------------------------------------------------- group quantisation
+
+def test_grouped_worked_example():
+    g = _golden("grouped_1x32.json")
+    x = np.array(g["x"], dtype=np.float32)
+    q, gamma = oracle.quant_act_grouped(x, g["G"])
+    np.testing.assert_array_equal(q, np.array(g["q"], dtype=np.int8))
+    np.testing.assert_array_equal(gamma, np.array(g["gamma"], dtype=np.float32))
+    y, acc = oracle.forward_grouped(q, gamma, np.array(g["w"], np.int8), np.array(g["beta"], np.float32))
+    np.testing.assert_array_equal(acc, np.array(g["acc"], dtype=np.int32))
+    np.testing.assert_array_equal(y, np.array(g["y"], dtype=np.float32))
+    # the stored y restated in exact rationals from the stored acc
+    for n in range(2):
+        exact = sum(Fraction(int(g["acc"][k][0][n])) * Fraction(g["beta"][k]) * Fraction(g["gamma"][k][0]) / 128
+                    for k in range(2))
+        assert exact == Fraction(g["y"][0][n])
+
+
+def test_grouped_one_group_is_the_ungrouped_layer():
+    rng = workloads.rng_for(920, 1)
+    x = rng.standard_normal((5, 96)).astype(np.float32)
+    w = workloads.ternary(rng, 7, 96, workloads.TERNARY_UNIFORM)
+    qg, gg = oracle.quant_act_grouped(x, 1)
+    q, gm = oracle.quant_act(x)
+    np.testing.assert_array_equal(qg[0], q)
+    np.testing.assert_array_equal(gg[0], gm)
+    gain = (rng.random(96) + 0.5).astype(np.float32)
+    qg, gg = oracle.quant_act_grouped(x, 1, gain, 1e-6)
+    q, gm = oracle.rmsnorm_quant_act(x, gain, 1e-6)
+    np.testing.assert_array_equal(qg[0], q)
+    np.testing.assert_array_equal(gg[0], gm)
+    yg, accg = oracle.forward_grouped(qg, gg, w, np.array([0.03], np.float32))
+    y, acc = oracle.forward(q, gm, w, 0.03)
+    np.testing.assert_array_equal(accg[0], acc)
+    np.testing.assert_array_equal(yg, y)
+
+
+def test_grouped_groups_are_independent():
+    # changing the inputs of group 1 leaves group 0's codes, scale and product alone
+    rng = workloads.rng_for(920, 2)
+    G, KG = 3, 32
+    x = rng.standard_normal((4, G * KG)).astype(np.float32)
+    w = workloads.ternary(rng, 6, G * KG, workloads.TERNARY_UNIFORM)
+    q, gamma = oracle.quant_act_grouped(x, G)
+    x2 = x.copy()
+    x2[:, KG:2 * KG] *= np.float32(-3.0)
+    x2[1, KG + 5] = np.float32(100.0)
+    q2, gamma2 = oracle.quant_act_grouped(x2, G)
+    for g in (0, 2):
+        np.testing.assert_array_equal(q2[g], q[g])
+        np.testing.assert_array_equal(gamma2[g], gamma[g])
+    w2 = w.copy()
+    w2[:, KG:2 * KG] = -w2[:, KG:2 * KG]
+    _, acc = oracle.forward_grouped(q, gamma, w, np.ones(G, np.float32))
+    _, acc2 = oracle.forward_grouped(q, gamma, w2, np.ones(G, np.float32))
+    np.testing.assert_array_equal(acc2[0], acc[0])
+    np.testing.assert_array_equal(acc2[2], acc[2])
+    np.testing.assert_array_equal(acc2[1], -acc[1])
+
+
+def test_grouped_scale_of_one_group():
+    # scaling group g's activations by 2^e scales its gamma by 2^e, keeps every
+    # code, and changes y by exactly (2^e - 1) times that group's term
+    rng = workloads.rng_for(920, 3)
+    G, KG = 4, 16
+    x = (rng.integers(-64, 65, (3, G * KG)) / 16.0).astype(np.float32)  # dyadic
+    w = workloads.ternary(rng, 5, G * KG, workloads.TERNARY_UNIFORM)
+    beta = np.array([0.5, 0.25, 0.125, 1.0], np.float32)
+    q, gamma = oracle.quant_act_grouped(x, G)
+    y, acc = oracle.forward_grouped(q, gamma, w, beta)
+    x2 = x.copy()
+    x2[:, 2 * KG:3 * KG] *= np.float32(4.0)
+    q2, gamma2 = oracle.quant_act_grouped(x2, G)
+    np.testing.assert_array_equal(q2, q)
+    np.testing.assert_array_equal(gamma2[2], gamma[2] * 4)
+    y2, acc2 = oracle.forward_grouped(q2, gamma2, w, beta)
+    np.testing.assert_array_equal(acc2, acc)
+    term = acc[2].astype(np.float64) * 0.125 * gamma[2].astype(np.float64)[:, None] / 128
+    np.testing.assert_array_equal(y2.astype(np.float64) - y.astype(np.float64), 3 * term)
+
+
+def test_grouped_with_a_shared_absmax_equals_the_ungrouped_product():
+    # every group of a token holds the token's absmax: the group codes are the
+    # ungrouped codes and the group products add up to the ungrouped product
+    rng = workloads.rng_for(920, 4)
+    G, KG = 4, 24
+    x = rng.uniform(-1, 1, (3, G * KG)).astype(np.float32)
+    for m in range(3):
+        for g in range(G):
+            x[m, g * KG + (m + g) % KG] = np.float32(2.0 if (m + g) % 2 else -2.0)
+    w = workloads.ternary(rng, 9, G * KG, workloads.TERNARY_UNIFORM)
+    q, gamma = oracle.quant_act_grouped(x, G)
+    q1, g1 = oracle.quant_act(x)
+    np.testing.assert_array_equal(np.concatenate(list(q), axis=1), q1)
+    assert (gamma == g1[None, :]).all()
+    _, acc = oracle.forward_grouped(q, gamma, w, np.ones(G, np.float32))
+    np.testing.assert_array_equal(acc.astype(np.int64).sum(axis=0), oracle.accumulate(q1, w))
+    # with RMSNorm the whole-row factor r is shared: each group's gamma is the
+    # ungrouped RMSNorm gamma
+    gain = np.ones(G * KG, np.float32)
+    qr, gr = oracle.quant_act_grouped(x, G, gain, 1e-6)
+    qr1, gr1 = oracle.rmsnorm_quant_act(x, gain, 1e-6)
+    np.testing.assert_array_equal(np.concatenate(list(qr), axis=1), qr1)
+    assert (gr == gr1[None, :]).all()
+
+
+def test_ternarize_grouped_recovers_scaled_ternary_blocks():
+    # W = a_g * T in group g: every code comes back and beta_g = a_g * nnz_g / (N K/G)
+    rng = workloads.rng_for(920, 5)
+    G, N, KG = 4, 32, 64
+    T = workloads.ternary(rng, N, G * KG, workloads.TERNARY_UNIFORM)
+    a = [0.5, 0.125, 2.0, 0.375]
+    W = np.concatenate([T[:, g * KG:(g + 1) * KG].astype(np.float32) * np.float32(a[g]) for g in range(G)],
+                       axis=1)
+    w, betas = oracle.ternarize_grouped(W, G)
+    np.testing.assert_array_equal(w, T)
+    for g in range(G):
+        nnz = int(np.count_nonzero(T[:, g * KG:(g + 1) * KG]))
+        assert Fraction(betas[g]) == Fraction(a[g]) * Fraction(nnz, N * KG)
+    w1, b1 = oracle.ternarize_grouped(W, 1)
+    w0, b0 = oracle.ternarize(W)
+    np.testing.assert_array_equal(w1, w0)
+    assert b1[0] == b0
