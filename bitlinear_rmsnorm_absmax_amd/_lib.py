@@ -37,6 +37,9 @@ _SIGNATURES = {
     "bitlinear_binarize": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "bitlinear_pack_weights1": [_vp, _i64, _i64, _vp, _vp, _vp],
     "bitlinear_forward1": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _vp],
+    "bitlinear_quant_act_grouped": [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _f32, _vp, _vp, _vp],
+    "bitlinear_forward_grouped": [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
+    "bitlinear_ternarize_grouped": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "bitlinear_last_error": [],
     "bitlinear_abi_version": [],
 }
@@ -233,6 +236,65 @@ def forward1(x_q: torch.Tensor, gamma: torch.Tensor, w_packed1: torch.Tensor, be
     _check(lib.bitlinear_forward1(x_q.data_ptr(), gamma.data_ptr(), M, K, w_packed1.data_ptr(), N,
                                   float(beta), y.data_ptr(), _ptr(acc), _stream(x_q)))
     return (y, acc) if want_acc else y
+
+
+def quant_act_grouped(x: torch.Tensor, groups: int, rms_gain: Optional[torch.Tensor] = None,
+                      rms_eps: float = 1e-6):
+    """Group quantisation of x [M][K] (fp32 or bf16): G runs of K/G inputs per
+    token, each with its own absmax scale.  Returns (x_q int8 [G][M][K/G],
+    gamma fp32 [G][M])."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    M, K = x.shape
+    G = int(groups)
+    if G < 1 or K % G:
+        raise ValueError(f"K={K} is not a multiple of G={G}")
+    if rms_gain is not None:
+        _dev(rms_gain, "rms_gain", (torch.float32,))
+    x_q = torch.empty((G, M, K // G), dtype=torch.int8, device=x.device)
+    gamma = torch.empty((G, M), dtype=torch.float32, device=x.device)
+    dt = BF16 if x.dtype == torch.bfloat16 else F32
+    _check(lib.bitlinear_quant_act_grouped(x.data_ptr(), dt, M, K, G, _ptr(rms_gain),
+                                           float(rms_eps), x_q.data_ptr(), gamma.data_ptr(),
+                                           _stream(x)))
+    return x_q, gamma
+
+
+def forward_grouped(x_q: torch.Tensor, gamma: torch.Tensor, w_packed: torch.Tensor,
+                    beta: torch.Tensor):
+    """Grouped BitLinear: x_q int8 [G][M][KG], gamma [G][M], w_packed
+    [G][N][KG/16], beta fp32 [G] on the device -> (y fp32 [M][N], acc int32
+    [G][M][N])."""
+    _dev(x_q, "x_q", (torch.int8,))
+    _dev(gamma, "gamma", (torch.float32,))
+    _dev(w_packed, "w_packed", (torch.int32, torch.uint32))
+    _dev(beta, "beta", (torch.float32,))
+    G, M, KG = x_q.shape
+    if w_packed.dim() != 3 or w_packed.shape[0] != G or w_packed.shape[2] * 16 != KG:
+        raise ValueError(f"w_packed shape {tuple(w_packed.shape)} does not match x_q {tuple(x_q.shape)}")
+    N = w_packed.shape[1]
+    y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
+    acc = torch.empty((G, M, N), dtype=torch.int32, device=x_q.device)
+    _check(lib.bitlinear_forward_grouped(x_q.data_ptr(), gamma.data_ptr(), M, G * KG, G,
+                                         w_packed.data_ptr(), N, beta.data_ptr(), y.data_ptr(),
+                                         acc.data_ptr(), _stream(x_q)))
+    return y, acc
+
+
+def ternarize_grouped(W_grouped: torch.Tensor, want_codes: bool = False):
+    """Absmean ternarisation per weight group of fp32 W_grouped [G][N][KG] ->
+    (packed int32 [G][N][KG/16], beta fp32 [G], beta64 float64 [G][, codes
+    int8 [G][N][KG]])."""
+    _dev(W_grouped, "W_grouped", (torch.float32,))
+    G, N, KG = W_grouped.shape
+    dev = W_grouped.device
+    packed = torch.empty((G, N, KG // 16), dtype=torch.int32, device=dev)
+    beta = torch.empty((G,), dtype=torch.float32, device=dev)
+    beta64 = torch.empty((G,), dtype=torch.float64, device=dev)
+    codes = torch.empty((G, N, KG), dtype=torch.int8, device=dev) if want_codes else None
+    _check(lib.bitlinear_ternarize_grouped(W_grouped.data_ptr(), N, G * KG, G, packed.data_ptr(),
+                                           _ptr(codes), beta.data_ptr(), beta64.data_ptr(),
+                                           _stream(W_grouped)))
+    return (packed, beta, beta64, codes) if want_codes else (packed, beta, beta64)
 
 
 def bitlinear(x: torch.Tensor, w_packed: torch.Tensor, beta: float,

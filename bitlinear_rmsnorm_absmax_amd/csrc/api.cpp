@@ -66,6 +66,34 @@ bitlinear_status_t need(const char* fn, const char* name, const void* p, bool re
     return BITLINEAR_OK;
 }
 
+// Kernel choice by M (or the forced path); y == nullptr stores only acc.
+hipError_t launch_forward_kernel(const int8_t* x_q, const float* gamma, int64_t M, int64_t K,
+                                 const uint32_t* w_packed, int64_t N, float beta, float* y,
+                                 int32_t* acc, int path, hipStream_t stream) {
+    if (path == BITLINEAR_PATH_AUTO)
+        path = (M <= 2) ? BITLINEAR_PATH_GEMV : (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
+    const int m = (int)M, n = (int)N, k = (int)K;
+    switch (path) {
+        case BITLINEAR_PATH_GEMV:
+            return bl::launch_gemv_valu(x_q, gamma, m, k, w_packed, n, beta, y, acc, stream);
+        case BITLINEAR_PATH_SKINNY:
+            return bl::launch_skinny_mfma(x_q, gamma, m, k, w_packed, n, beta, y, acc, stream);
+        default:
+            return bl::launch_gemm_mfma(x_q, gamma, m, k, w_packed, n, beta, y, acc, stream);
+    }
+}
+
+// Group count G: K split into G equal runs whose length is a multiple of `unit`.
+bitlinear_status_t check_groups(const char* fn, int64_t K, int64_t G, int64_t unit) {
+    if (G < 1 || G > BITLINEAR_MAX_K)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: G=%lld must be in [1, %d]", fn, (long long)G,
+                    BITLINEAR_MAX_K);
+    if (K % G != 0 || (K / G) % unit != 0)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld must be G=%lld runs of a multiple of %lld", fn,
+                    (long long)K, (long long)G, (long long)unit);
+    return BITLINEAR_OK;
+}
+
 bitlinear_status_t forward_impl(const char* fn, const int8_t* x_q, const float* gamma,
                                 int64_t M, int64_t K, const uint32_t* w_packed, int64_t N,
                                 float beta, float* y, int32_t* acc, int path,
@@ -90,22 +118,8 @@ bitlinear_status_t forward_impl(const char* fn, const int8_t* x_q, const float* 
     if (!any_out) return ok();
     if (K == 0) return from_hip(bl::launch_fill_zero(y, acc, M * N, stream), fn);
 
-    if (path == BITLINEAR_PATH_AUTO)
-        path = (M <= 2) ? BITLINEAR_PATH_GEMV : (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
-    const int m = (int)M, n = (int)N, k = (int)K;
-    hipError_t e;
-    switch (path) {
-        case BITLINEAR_PATH_GEMV:
-            e = bl::launch_gemv_valu(x_q, gamma, m, k, w_packed, n, beta, y, acc, stream);
-            break;
-        case BITLINEAR_PATH_SKINNY:
-            e = bl::launch_skinny_mfma(x_q, gamma, m, k, w_packed, n, beta, y, acc, stream);
-            break;
-        default:
-            e = bl::launch_gemm_mfma(x_q, gamma, m, k, w_packed, n, beta, y, acc, stream);
-            break;
-    }
-    return from_hip(e, fn);
+    return from_hip(launch_forward_kernel(x_q, gamma, M, K, w_packed, N, beta, y, acc, path, stream),
+                    fn);
 }
 
 }  // namespace
@@ -270,6 +284,92 @@ bitlinear_status_t bitlinear_forward1(const int8_t* x_q, const float* gamma, int
     return from_hip(bl::launch_forward1(x_q, gamma, (int)M, (int)K, w_packed1, (int)N, beta, y, acc,
                                         stream),
                     fn);
+}
+
+bitlinear_status_t bitlinear_quant_act_grouped(const void* x, bitlinear_dtype_t x_dtype, int64_t M,
+                                               int64_t K, int64_t G, const float* rms_gain,
+                                               float rms_eps, int8_t* x_q, float* gamma,
+                                               hipStream_t stream) {
+    const char* fn = "bitlinear_quant_act_grouped";
+    BL_TRY(check_rows(fn, "M", M, (1LL << 31) - 1));
+    BL_TRY(check_k(fn, "K", K));
+    BL_TRY(check_groups(fn, K, G, 16));
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16)
+        return fail(BITLINEAR_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)x_dtype);
+    if (rms_gain && !(std::isfinite(rms_eps) && rms_eps >= 0.0f))
+        return fail(BITLINEAR_ERR_VALUE, "%s: rms_eps must be finite and >= 0", fn);
+    const bool any = M > 0 && K > 0;
+    BL_TRY(need(fn, "x", x, any, 16));
+    BL_TRY(need(fn, "x_q", x_q, any, 16));
+    BL_TRY(need(fn, "gamma", gamma, M > 0, 4));
+    if (rms_gain && !aligned(rms_gain, 16))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: rms_gain is not 16-byte aligned", fn);
+    if (M == 0) return ok();
+    if (K == 0)  // every run is empty: gamma = 0
+        return from_hip(bl::launch_quant_act(x, 0, M * G, 0, nullptr, 0.f, x_q, gamma, stream), fn);
+    return from_hip(bl::launch_quant_act_grouped(x, x_dtype == BITLINEAR_BF16, M, K, G, rms_gain,
+                                                 rms_eps, x_q, gamma, stream),
+                    fn);
+}
+
+bitlinear_status_t bitlinear_forward_grouped(const int8_t* x_q, const float* gamma, int64_t M,
+                                             int64_t K, int64_t G, const uint32_t* w_packed,
+                                             int64_t N, const float* beta, float* y, int32_t* acc,
+                                             hipStream_t stream) {
+    const char* fn = "bitlinear_forward_grouped";
+    BL_TRY(check_rows(fn, "M", M, kMaxM));
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    BL_TRY(check_k(fn, "K", K));
+    BL_TRY(check_groups(fn, K, G, 64));
+    const bool any_out = M > 0 && N > 0;
+    const bool any_in = any_out && K > 0;
+    BL_TRY(need(fn, "x_q", x_q, any_in, 16));
+    BL_TRY(need(fn, "gamma", gamma, any_in, 4));
+    BL_TRY(need(fn, "w_packed", w_packed, any_in, 16));
+    BL_TRY(need(fn, "beta", beta, any_in, 4));
+    BL_TRY(need(fn, "y", y, any_out, 4));
+    BL_TRY(need(fn, "acc", acc, any_out, 4));
+    if (!any_out) return ok();
+    if (K == 0) {
+        hipError_t e = bl::launch_fill_zero(y, nullptr, M * N, stream);
+        if (e == hipSuccess) e = bl::launch_fill_zero(reinterpret_cast<float*>(acc), nullptr, G * M * N, stream);
+        return from_hip(e, fn);
+    }
+    const int64_t KG = K / G;
+    for (int64_t g = 0; g < G; ++g) {
+        const hipError_t e = launch_forward_kernel(x_q + g * M * KG, gamma + g * M, M, KG,
+                                                   w_packed + g * N * (KG / 16), N, 1.0f, nullptr,
+                                                   acc + g * M * N, BITLINEAR_PATH_AUTO, stream);
+        if (e != hipSuccess) return from_hip(e, fn);
+    }
+    return from_hip(bl::launch_group_sum(acc, gamma, beta, M, N, G, y, stream), fn);
+}
+
+bitlinear_status_t bitlinear_ternarize_grouped(const float* W_grouped, int64_t N, int64_t K,
+                                               int64_t G, uint32_t* w_packed, int8_t* w_ternary,
+                                               float* beta, double* beta64, hipStream_t stream) {
+    const char* fn = "bitlinear_ternarize_grouped";
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    BL_TRY(check_k(fn, "K", K));
+    BL_TRY(check_groups(fn, K, G, 64));
+    const bool any = N > 0 && K > 0;
+    if (any && N * (K / 16) > (1LL << 40))
+        return fail(BITLINEAR_ERR_SHAPE, "%s: N*K/16 exceeds 2^40", fn);
+    BL_TRY(need(fn, "W_grouped", W_grouped, any, 16));
+    BL_TRY(need(fn, "w_packed", w_packed, any, 16));
+    BL_TRY(need(fn, "beta", beta, true, 4));
+    BL_TRY(need(fn, "beta64", beta64, true, 8));
+    if (w_ternary && !aligned(w_ternary, 16))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: w_ternary is not 16-byte aligned", fn);
+    const int64_t KG = K / G;
+    for (int64_t g = 0; g < G; ++g) {
+        const hipError_t e = bl::launch_ternarize(
+            any ? W_grouped + g * N * KG : nullptr, any ? N : 0, any ? KG : 0,
+            any ? w_packed + g * N * (KG / 16) : nullptr,
+            (any && w_ternary) ? w_ternary + g * N * KG : nullptr, beta + g, beta64 + g, stream);
+        if (e != hipSuccess) return from_hip(e, fn);
+    }
+    return ok();
 }
 
 const char* bitlinear_last_error(void) { return g_err; }

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
                 if (row < M && col < N) {
                     const int a = (ONEBIT ? 2 * d : d) - Ssum[row];
                     const int64_t o = (int64_t)row * N + col;
-                    y[o] = (float)a * out_scale(beta, gamma[row]);
+                    if (y) y[o] = (float)a * out_scale(beta, gamma[row]);
                     if (acc_out) acc_out[o] = a;
                 }
             }

@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_valu_kernel(
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
             if (m < M) {
-                y[(int64_t)m * N + n] = yv[m];
+                if (y) y[(int64_t)m * N + n] = yv[m];
                 if (acc_out) acc_out[(int64_t)m * N + n] = av[m];
             }
         }

@@ -23,6 +23,7 @@ hipError_t launch_pack(const int8_t* w, int64_t N, int64_t K, uint32_t* packed, 
 hipError_t launch_fill_zero(float* y, int32_t* acc, int64_t count, hipStream_t s);
 
 // Path 1: VALU dot4 GEMV, M <= 8.
+// Forward launchers: y == nullptr stores only the accumulators (acc).
 hipError_t launch_gemv_valu(const int8_t* xq, const float* gamma, int M, int K,
                             const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                             hipStream_t s);
@@ -68,6 +69,13 @@ hipError_t launch_forward1(const int8_t* xq, const float* gamma, int M, int K, c
 // holds the partial sums in between, so K >= 32).
 hipError_t launch_ternarize(const float* W, int64_t N, int64_t K, uint32_t* packed, int8_t* codes,
                             float* beta32, double* beta64, hipStream_t s);
+// Group quantisation: q [G][M][K/G], gamma [G][M] (K/G % 16 == 0).
+hipError_t launch_quant_act_grouped(const void* x, int bf16, int64_t M, int64_t K, int64_t G,
+                                    const float* gain, float eps, int8_t* q, float* gamma,
+                                    hipStream_t s);
+// y = sum over g of fl32(acc[g]) * fl32(beta[g] * gamma[g][m]) / 128 (beta on the device).
+hipError_t launch_group_sum(const int32_t* acc, const float* gamma, const float* beta, int64_t M,
+                            int64_t N, int64_t G, float* y, hipStream_t s);
 hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
                            const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                            hipStream_t s);

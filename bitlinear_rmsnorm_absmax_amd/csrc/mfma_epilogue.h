@@ -8,6 +8,8 @@
 // come from block-local LDS arrays, so four consecutive rows are one 16-byte
 // LDS read.
 //
+// y == nullptr stores only the accumulators (acc_out).
+//
 // Tiles wholly inside the output take a path without per-element bounds
 // tests: one 32-bit row offset per row, column tiles addressed from
 // wave-uniform base pointers, so each store is one instruction on an SGPR
@@ -48,23 +50,25 @@ __device__ __forceinline__ void store_tiles(const v16i (&acc)[TM][TN], const int
     const bool inside = row_w + TM * 32 <= M && col_w + TN * 32 <= N &&
                         (int64_t)TM * 32 * N < (int64_t)1 << 31;
     if (inside) {
-        float* yw = y + (int64_t)row_w * N + col_w;
         int32_t* aw = acc_out ? acc_out + (int64_t)row_w * N + col_w : nullptr;
+        if (y) {
+            float* yw = y + (int64_t)row_w * N + col_w;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
+            for (int i = 0; i < TM; ++i) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int rb = 32 * i + 8 * g + 4 * h;  // wave-local row of v = 4g
-                const v4i s4 = *reinterpret_cast<const v4i*>(S + r0 + rb);
-                const v4f c4 = *reinterpret_cast<const v4f*>(sc + r0 + rb);
+                for (int g = 0; g < 4; ++g) {
+                    const int rb = 32 * i + 8 * g + 4 * h;  // wave-local row of v = 4g
+                    const v4i s4 = *reinterpret_cast<const v4i*>(S + r0 + rb);
+                    const v4f c4 = *reinterpret_cast<const v4f*>(sc + r0 + rb);
 #pragma unroll
-                for (int vv = 0; vv < 4; ++vv) {
-                    const uint32_t off = (uint32_t)(rb + vv) * (uint32_t)N + (uint32_t)l32;
+                    for (int vv = 0; vv < 4; ++vv) {
+                        const uint32_t off = (uint32_t)(rb + vv) * (uint32_t)N + (uint32_t)l32;
 #pragma unroll
-                    for (int t = 0; t < TN; ++t) {
-                        const int a = acc[i][t][4 * g + vv] - s4[vv];
-                        float* yt = yw + 32 * t;
-                        yt[off] = (float)a * c4[vv];
+                        for (int t = 0; t < TN; ++t) {
+                            const int a = acc[i][t][4 * g + vv] - s4[vv];
+                            float* yt = yw + 32 * t;
+                            yt[off] = (float)a * c4[vv];
+                        }
                     }
                 }
             }
@@ -104,7 +108,7 @@ __device__ __forceinline__ void store_tiles(const v16i (&acc)[TM][TN], const int
                 if (col >= N) continue;
                 const int a = acc[i][t][v] - sm;
                 const int64_t o = (int64_t)row * N + col;
-                y[o] = (float)a * s;
+                if (y) y[o] = (float)a * s;
                 if (acc_out) acc_out[o] = a;
             }
         }

@@ -184,6 +184,66 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
     }
 }
 
+// Group quantisation (unite.ai BitNet.cpp article, Gruppenquantisierung und
+// -normalisierung): row `row` split into G runs of K/G inputs, each run
+// quantised with its own absmax scale.  One workgroup per row; per group an
+// absmax pass and a quantisation pass over the run's 16-element chunks (the
+// second pass re-reads the run, L2-resident by then).  RMS: the whole row's
+// sum of squares first (same chunk order and reduction as quant_rows_kernel,
+// so r is the ungrouped r), gamma = fl32(r * max |u|) per run.  Outputs are
+// group-major: q + (g*M + row)*K/G, gamma_out[g*M + row].
+template <Src S, bool RMS>
+__global__ __launch_bounds__(kQuantThreads) void quant_groups_kernel(
+    RowSrc src, int K, int G, int M, const float* __restrict__ gain, float eps,
+    int8_t* __restrict__ q, float* __restrict__ gamma_out) {
+    const int64_t row = blockIdx.x;
+    const int KG = K / G, nch = KG / 16;
+    auto load_u = [&](int c, float v[16]) {  // chunk c of the row, gain applied
+        load_chunk<S>(src, row, K, c, v);
+        if constexpr (RMS) {
+            const float4* pg = reinterpret_cast<const float4*>(gain + (int64_t)c * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float4 g4 = pg[i];
+                v[4 * i + 0] *= g4.x; v[4 * i + 1] *= g4.y; v[4 * i + 2] *= g4.z; v[4 * i + 3] *= g4.w;
+            }
+        }
+    };
+    double r = 1.0;
+    if constexpr (RMS) {
+        float unused = 0.0f;
+        double ss = 0.0;
+        for (int c = threadIdx.x; c < K / 16; c += kQuantThreads) {
+            float v[16];
+            load_chunk<S>(src, row, K, c, v);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ss += (double)v[e] * (double)v[e];
+        }
+        block_reduce(unused, ss, true);
+        r = 1.0 / sqrt(ss / (double)K + (double)eps);
+        __syncthreads();  // the reduction scratch is reused below
+    }
+    for (int g = 0; g < G; ++g) {
+        float amax = 0.0f;
+        double unused = 0.0;
+        for (int c = threadIdx.x; c < nch; c += kQuantThreads) {
+            float v[16];
+            load_u(g * nch + c, v);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        }
+        block_reduce(amax, unused, false);
+        if (threadIdx.x == 0) gamma_out[(int64_t)g * M + row] = RMS ? (float)(r * (double)amax) : amax;
+        int8_t* qg = q + (int64_t)g * M * KG;
+        for (int c = threadIdx.x; c < nch; c += kQuantThreads) {
+            float v[16];
+            load_u(g * nch + c, v);
+            store_codes(qg, row, KG, c, v, amax);
+        }
+        __syncthreads();  // the reduction scratch is reused by the next group
+    }
+}
+
 // Rows with K == 0: gamma = 0 and nothing else to write.
 __global__ void zero_gamma_kernel(float* gamma, int64_t M) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -212,6 +272,27 @@ hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, const
             quant_rows_kernel<Src::F32, true, false><<<grid, block, 0, s>>>(src, k, gain, eps, nullptr, q, gamma);
         else
             quant_rows_kernel<Src::F32, false, false><<<grid, block, 0, s>>>(src, k, nullptr, 0.f, nullptr, q, gamma);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_grouped(const void* x, int bf16, int64_t M, int64_t K, int64_t G,
+                                    const float* gain, float eps, int8_t* q, float* gamma,
+                                    hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    RowSrc src{x, nullptr};
+    dim3 grid((unsigned)M), block(kQuantThreads);
+    const int k = (int)K, g = (int)G, m = (int)M;
+    if (bf16) {
+        if (gain)
+            quant_groups_kernel<Src::BF16, true><<<grid, block, 0, s>>>(src, k, g, m, gain, eps, q, gamma);
+        else
+            quant_groups_kernel<Src::BF16, false><<<grid, block, 0, s>>>(src, k, g, m, nullptr, 0.f, q, gamma);
+    } else {
+        if (gain)
+            quant_groups_kernel<Src::F32, true><<<grid, block, 0, s>>>(src, k, g, m, gain, eps, q, gamma);
+        else
+            quant_groups_kernel<Src::F32, false><<<grid, block, 0, s>>>(src, k, g, m, nullptr, 0.f, q, gamma);
     }
     return hipGetLastError();
 }

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(WAVES * kWave) void skinny_mfma_kernel(
             for (int w = 0; w < WAVES; ++w) a += red[w][p][v][lane];
             if (row < M && col < N) {
                 const int64_t o = (int64_t)row * N + col;
-                y[o] = (float)a * out_scale(beta, gamma[row]);
+                if (y) y[o] = (float)a * out_scale(beta, gamma[row]);
                 if (acc_out) acc_out[o] = a;
             }
         }

@@ -231,6 +231,60 @@ bitlinear_status_t bitlinear_forward1(const int8_t* x_q, const float* gamma, int
                                       const uint32_t* w_packed1, int64_t N, float beta, float* y,
                                       int32_t* acc, hipStream_t stream);
 
+/*
+ * Group quantisation (unite.ai article, section "Gruppenquantisierung und
+ * -normalisierung": weights and activations are divided into G groups and
+ * the quantisation parameters are estimated per group instead of for the
+ * whole matrix, so the groups need no communication).  Groups split the K
+ * inputs into G equal runs of KG = K/G: token m's run g has its own absmax
+ * scale gamma[g][m], weight group g (input columns g*KG .. (g+1)*KG) its own
+ * scale beta[g], each group is a BitLinear product of its own, and the layer
+ * output is the sum of the G group outputs.  All grouped operands are
+ * group-major, so group g of each is one contiguous block (the layout a
+ * per-group shard would hold).
+ */
+
+/* Activations of the grouped layer: the quantiser of bitlinear_quant_act per
+ * run.  x [M][K] fp32/bf16 as for bitlinear_quant_act; x_q out int8
+ * [G][M][KG] (16-byte aligned); gamma out fp32 [G][M].  With rms_gain the
+ * RMSNorm factor r is the token's whole-row factor and gamma[g][m] =
+ * fl32(r * max over the run of |gain * x|).  Requires G >= 1, K % G == 0,
+ * KG % 16 == 0.  K == 0 writes gamma = 0.  One launch. */
+bitlinear_status_t bitlinear_quant_act_grouped(const void* x, bitlinear_dtype_t x_dtype, int64_t M,
+                                               int64_t K, int64_t G, const float* rms_gain,
+                                               float rms_eps, int8_t* x_q, float* gamma,
+                                               hipStream_t stream);
+
+/* Grouped product:
+ *   acc[g][m][n] = sum over k < KG of w_g[n][k] * x_q[g][m][k]  (exact int32)
+ *   y[m][n]      = sum over g (in order g = 0 .. G-1, fp32) of
+ *                  fl32(acc[g][m][n]) * (fl32(beta[g] * gamma[g][m]) / 128)
+ * x_q [G][M][KG] int8 and gamma [G][M] from bitlinear_quant_act_grouped.
+ * w_packed uint32 [G][N][KG/16]: group g's ternary block packed as by
+ * bitlinear_pack_weights (packing a group-major int8 [G][N][KG] tensor as
+ * G*N rows of KG gives this layout).  beta: DEVICE fp32 [G] (finite; as
+ * written by bitlinear_ternarize_grouped).  y out fp32 [M][N].  acc out int32
+ * [G][M][N], REQUIRED: it holds the group products the final sum reads.
+ * Requires G >= 1, K % G == 0, KG % 64 == 0; other limits as for
+ * bitlinear_forward with K = KG.  Each group runs the kernel bitlinear_forward
+ * picks for (M, KG, N) in accumulator-only mode, then one launch adds the
+ * groups; G + 1 launches on `stream`, none allocates. */
+bitlinear_status_t bitlinear_forward_grouped(const int8_t* x_q, const float* gamma, int64_t M,
+                                             int64_t K, int64_t G, const uint32_t* w_packed,
+                                             int64_t N, const float* beta, float* y, int32_t* acc,
+                                             hipStream_t stream);
+
+/* Absmean ternarisation per weight group (the rule of bitlinear_ternarize
+ * applied to each group's N x KG block).  W_grouped: fp32 [G][N][KG], group g
+ * = input columns g*KG .. (g+1)*KG of the [N][K] weight matrix, contiguous.
+ * w_packed out uint32 [G][N][KG/16] (the layout bitlinear_forward_grouped
+ * takes); w_ternary optional out int8 [G][N][KG]; beta out fp32 [G]; beta64
+ * out double [G].  Requires G >= 1, K % G == 0, KG % 64 == 0.  3 or more
+ * launches per group on `stream`; none allocates. */
+bitlinear_status_t bitlinear_ternarize_grouped(const float* W_grouped, int64_t N, int64_t K,
+                                               int64_t G, uint32_t* w_packed, int8_t* w_ternary,
+                                               float* beta, double* beta64, hipStream_t stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 const char* bitlinear_last_error(void);
 

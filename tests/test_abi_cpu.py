@@ -20,6 +20,7 @@ def test_every_declared_symbol_is_exported():
         "bitlinear_quant_act", "bitlinear_pack_weights", "bitlinear_forward",
         "bitlinear_forward_path", "bitlinear_silu_mul_quant", "bitlinear_ternarize",
         "bitlinear_binarize", "bitlinear_pack_weights1", "bitlinear_forward1",
+        "bitlinear_quant_act_grouped", "bitlinear_forward_grouped", "bitlinear_ternarize_grouped",
         "bitlinear_last_error", "bitlinear_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -214,4 +215,68 @@ def _fwd1(xq=FAKE, g=FAKE, M=1, K=64, w=FAKE, N=1, beta=1.0, y=FAKE, acc=None):
 ])
 def test_forward1_rejects(kw, status, msg):
     assert _fwd1(**kw) == status
+    assert msg in bl.last_error()
+
+
+def _qg(x=FAKE, dt=0, M=2, K=128, G=2, gain=None, eps=1e-6, xq=FAKE, g=FAKE):
+    return bl.lib.bitlinear_quant_act_grouped(x, dt, M, K, G, gain, F(eps), xq, g, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(G=0), bl.ERR_SHAPE, "G=0"),
+    (dict(G=3), bl.ERR_SHAPE, "runs of a multiple of 16"),
+    (dict(K=96, G=4), bl.ERR_SHAPE, "runs of a multiple of 16"),
+    (dict(x=None), bl.ERR_NULL, "x is NULL"),
+    (dict(xq=None), bl.ERR_NULL, "x_q is NULL"),
+    (dict(g=None), bl.ERR_NULL, "gamma is NULL"),
+    (dict(dt=5), bl.ERR_DTYPE, "dtype"),
+    (dict(gain=FAKE, eps=-1.0), bl.ERR_VALUE, "rms_eps"),
+    (dict(gain=FAKE + 4), bl.ERR_ALIGN, "rms_gain"),
+])
+def test_quant_grouped_rejects(kw, status, msg):
+    assert _qg(**kw) == status
+    assert msg in bl.last_error()
+
+
+def _fg(xq=FAKE, g=FAKE, M=2, K=256, G=2, w=FAKE, N=3, beta=FAKE, y=FAKE, acc=FAKE):
+    return bl.lib.bitlinear_forward_grouped(xq, g, M, K, G, w, N, beta, y, acc, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(G=0), bl.ERR_SHAPE, "G=0"),
+    (dict(K=256, G=3), bl.ERR_SHAPE, "runs of a multiple of 64"),
+    (dict(K=128, G=4), bl.ERR_SHAPE, "runs of a multiple of 64"),
+    (dict(K=24), bl.ERR_SHAPE, "multiple of 16"),
+    (dict(acc=None), bl.ERR_NULL, "acc is NULL"),
+    (dict(beta=None), bl.ERR_NULL, "beta is NULL"),
+    (dict(y=None), bl.ERR_NULL, "y is NULL"),
+    (dict(w=FAKE + 8), bl.ERR_ALIGN, "w_packed is not 16-byte aligned"),
+    (dict(M=-1), bl.ERR_SHAPE, "M=-1"),
+])
+def test_forward_grouped_rejects(kw, status, msg):
+    assert _fg(**kw) == status
+    assert msg in bl.last_error()
+
+
+def test_grouped_empty_work_is_ok_without_pointers():
+    assert _fg(M=0, xq=None, g=None, w=None, beta=None, y=None, acc=None) == bl.OK
+    assert _fg(N=0, xq=None, g=None, w=None, beta=None, y=None, acc=None) == bl.OK
+    assert _qg(M=0, x=None, xq=None, g=None) == bl.OK
+
+
+def _tg(W=FAKE, N=4, K=256, G=2, wp=FAKE, codes=None, b=FAKE, b64=FAKE):
+    return bl.lib.bitlinear_ternarize_grouped(W, N, K, G, wp, codes, b, b64, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(G=0), bl.ERR_SHAPE, "G=0"),
+    (dict(K=192, G=2), bl.ERR_SHAPE, "runs of a multiple of 64"),
+    (dict(W=None), bl.ERR_NULL, "W_grouped is NULL"),
+    (dict(wp=None), bl.ERR_NULL, "w_packed is NULL"),
+    (dict(b=None), bl.ERR_NULL, "beta is NULL"),
+    (dict(b64=FAKE + 4), bl.ERR_ALIGN, "beta64"),
+    (dict(codes=FAKE + 8), bl.ERR_ALIGN, "w_ternary"),
+])
+def test_ternarize_grouped_rejects(kw, status, msg):
+    assert _tg(**kw) == status
     assert msg in bl.last_error()

@@ -530,3 +530,125 @@ def test_binarize_then_both_forward_paths(dev):
     np.testing.assert_array_equal(host(y1), host(y2))
     y_ref, acc_ref = oracle.forward(host(q), host(g), w_ref, np.float32(beta))
     np.testing.assert_array_equal(host(acc1), acc_ref)
+
+
+# ------------------------------------------------------------------ group quantisation
+
+def grouped_bound(acc_ref, beta, gamma_ref):
+    """|y - y_ref| bound of the grouped sum: each group term has two fp32
+    roundings, the G terms are added in fp32 (G - 1 roundings) and y_ref is
+    rounded once, so (G + 2) u times the sum of |terms| (u = 2^-24), with
+    one u of slack."""
+    G = acc_ref.shape[0]
+    terms = np.abs(acc_ref.astype(np.float64) * beta.astype(np.float64)[:, None, None]
+                   * gamma_ref.astype(np.float64)[:, :, None] / 128.0)
+    return (G + 3) * 2.0 ** -24 * terms.sum(axis=0)
+
+
+def group_major(a, G):
+    """[R][K] -> [G][R][K/G] (group g = columns g*K/G .. (g+1)*K/G)."""
+    R, K = a.shape
+    return np.ascontiguousarray(a.reshape(R, G, K // G).transpose(1, 0, 2))
+
+
+def pack_grouped(w, G, dev):
+    N, K = w.shape
+    packed, bad = bl.pack_weights(to_dev(group_major(w, G).reshape(G * N, K // G), dev))
+    assert int(host(bad)[0]) == 0
+    return packed.view(G, N, K // (16 * G))
+
+
+@pytest.mark.parametrize("M,K,G,src", [
+    (5, 1024, 4, "f32"), (3, 4096, 16, "f32"), (7, 2560, 5, "f32"), (1, 64, 4, "f32"),
+    (2, 512, 2, "bf16"), (4, 2560, 4, "rms"), (9, 4096, 8, "rms"), (300, 1024, 2, "f32")])
+def test_quant_grouped_parity(dev, M, K, G, src):
+    rng = workloads.rng_for(970, M, K, G)
+    x = (rng.standard_t(3, (M, K)) * 2.0).astype(np.float32)
+    x[:, 7] *= 50.0
+    if src == "bf16":
+        bits = workloads.f32_to_bf16_bits(x)
+        xd = to_dev(bits, dev, torch.bfloat16)
+        x_ref = oracle.bf16_to_f32(bits)
+    else:
+        xd = to_dev(x, dev)
+        x_ref = x
+    gain = (rng.random(K) + 0.5).astype(np.float32) if src == "rms" else None
+    q, g = bl.quant_act_grouped(xd, G, None if gain is None else to_dev(gain, dev), 1e-6)
+    q_ref, g_ref = oracle.quant_act_grouped(x_ref, G, gain, 1e-6)
+    np.testing.assert_array_equal(host(q), q_ref)
+    if gain is None:
+        np.testing.assert_array_equal(host(g), g_ref)
+    else:
+        assert_y_close(host(g), g_ref)
+
+
+@pytest.mark.parametrize("M,K,G,N", [
+    (1, 4096, 4, 1000), (4, 4096, 4, 700), (16, 4096, 4, 2000), (5, 2048, 2, 333),
+    (33, 1024, 4, 517), (100, 2560, 5, 300), (2, 512, 8, 129), (1, 256, 1, 64)])
+def test_forward_grouped_parity(dev, M, K, G, N):
+    rng = workloads.rng_for(971, M, K, G, N)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = workloads.ternary(rng, N, K, workloads.TERNARY_UNIFORM)
+    beta = rng.uniform(0.01, 0.05, G).astype(np.float32)
+    q_ref, g_ref = oracle.quant_act_grouped(x, G)
+    y_ref, acc_ref = oracle.forward_grouped(q_ref, g_ref, w, beta)
+    y, acc = bl.forward_grouped(to_dev(q_ref, dev), to_dev(g_ref, dev), pack_grouped(w, G, dev),
+                                to_dev(beta, dev))
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    err = np.abs(host(y).astype(np.float64) - y_ref.astype(np.float64))
+    assert (err <= grouped_bound(acc_ref, beta, g_ref)).all()
+
+
+def test_forward_grouped_one_group_is_forward(dev):
+    rng = workloads.rng_for(972, 1)
+    M, K, N = 6, 1024, 300
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = workloads.ternary(rng, N, K, workloads.TERNARY_HALF_ZERO)
+    q, g = bl.quant_act(to_dev(x, dev))
+    wp = gpu_pack(w, dev)
+    y1, acc1 = bl.forward(q, g, wp, 0.03, want_acc=True)
+    y, acc = bl.forward_grouped(q.view(1, M, K), g.view(1, M), wp.view(1, N, K // 16),
+                                torch.tensor([0.03], dtype=torch.float32, device=dev))
+    np.testing.assert_array_equal(host(acc)[0], host(acc1))
+    np.testing.assert_array_equal(host(y), host(y1))
+
+
+@pytest.mark.parametrize("N,K,G", [(300, 1024, 4), (64, 4096, 16), (1000, 2560, 5), (7, 128, 2)])
+def test_ternarize_grouped_parity(dev, N, K, G):
+    rng = workloads.rng_for(973, N, K, G)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    W[:, :K // G] *= 3.0  # groups with different scales
+    packed, beta, beta64, codes = bl.ternarize_grouped(to_dev(group_major(W, G), dev), want_codes=True)
+    w_ref, b_ref = oracle.ternarize_grouped(W, G)
+    np.testing.assert_array_equal(host(codes), group_major(w_ref, G))
+    np.testing.assert_array_equal(host(beta64), b_ref)
+    np.testing.assert_array_equal(host(beta), b_ref.astype(np.float32))
+    p_ref, bad = oracle.pack(group_major(w_ref, G).reshape(G * N, K // G))
+    assert bad == 0
+    np.testing.assert_array_equal(host(packed).view(np.uint32).reshape(G * N, -1), p_ref)
+
+
+def test_grouped_chain(dev):
+    # fp weights and activations -> grouped ternarisation and quantisation ->
+    # grouped product, all on the GPU, against the oracle chain
+    rng = workloads.rng_for(974, 1)
+    M, K, G, N = 9, 4096, 4, 1500
+    W = (rng.standard_normal((N, K)) * 0.03).astype(np.float32)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    packed, beta, _ = bl.ternarize_grouped(to_dev(group_major(W, G), dev))
+    q, g = bl.quant_act_grouped(to_dev(x, dev), G)
+    y, acc = bl.forward_grouped(q, g, packed, beta)
+    w_ref, b_ref = oracle.ternarize_grouped(W, G)
+    q_ref, g_ref = oracle.quant_act_grouped(x, G)
+    y_ref, acc_ref = oracle.forward_grouped(q_ref, g_ref, w_ref, b_ref.astype(np.float32))
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    err = np.abs(host(y).astype(np.float64) - y_ref.astype(np.float64))
+    assert (err <= grouped_bound(acc_ref, b_ref.astype(np.float32), g_ref)).all()
+
+
+def test_grouped_empty(dev):
+    q, g = bl.quant_act_grouped(torch.zeros((0, 256), device=dev), 4)
+    assert q.shape == (4, 0, 64)
+    q, g = bl.quant_act_grouped(torch.zeros((3, 256), device=dev), 4)
+    assert not host(q).any() and not host(g).any()
