@@ -57,11 +57,14 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
-    ap.add_argument("--op", choices=("layer", "ternarize", "binary"), default="layer",
+    ap.add_argument("--op", choices=("layer", "ternarize", "binary", "grouped"), default="layer",
                     help="layer: the BitLinear step (default); ternarize: absmean "
                          "ternarisation + packing of fp32 weights of the workload's shape; "
                          "binary: the step on 1-bit Sign(W - alpha) weights "
-                         "(bitlinear_quant_act + bitlinear_forward1 per token count)")
+                         "(bitlinear_quant_act + bitlinear_forward1 per token count); "
+                         "grouped: the step with --groups group scales along K "
+                         "(bitlinear_quant_act_grouped + bitlinear_forward_grouped)")
+    ap.add_argument("--groups", type=int, default=4, help="group count of --op grouped")
     ap.add_argument("--traffic-probe", metavar="JSON",
                     help="launch every call of one step once, then a plain copy kernel of "
                          f"{COPY_BYTES} bytes, write the launch order to JSON and exit "
@@ -593,6 +596,128 @@ def binary_cpu_baseline(args, W, beta, seconds):
                        f"unpacked), M={ms}, {el:.1f} s")
 
 
+# ----------------------------------------------------------------------------- grouped step
+
+def bench_grouped(args, torch, bl, dev):
+    """The decode step of the workload with group scales: the workload's ternary
+    weights split into G groups of K/G input columns (group-major, packed),
+    per-group betas U(0.01, 0.05); per token count bitlinear_quant_act_grouped
+    + bitlinear_forward_grouped; weights rotate through >= 512 MB of copies;
+    the timed steps are one graph replay."""
+    wl = workloads.WORKLOADS[args.workload]
+    N, K, G = wl.N, wl.K, args.groups
+    KG = K // G
+    w = workloads.workload_weights(args.workload)
+    wg = np.ascontiguousarray(w.reshape(N, G, KG).transpose(1, 0, 2)).reshape(G * N, KG)
+    packed, _ = bl.pack_weights(torch.from_numpy(wg).to(dev))
+    packed = packed.view(G, N, KG // 16)
+    beta = workloads.rng_for(args.workload, 32).uniform(0.01, 0.05, G).astype(np.float32)
+    beta_d = torch.from_numpy(beta).to(dev)
+    wbytes = N * K // 4
+    copies = [packed] + [packed.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / wbytes)) - 1)]
+    bufs = []
+    for M in [m for m in wl.ms if m <= 64]:
+        x = torch.from_numpy(workloads.workload_activations(args.workload, M)).to(dev)
+        bufs.append(dict(M=M, x=x, q=torch.empty((G, M, KG), dtype=torch.int8, device=dev),
+                         g=torch.empty((G, M), device=dev), y=torch.empty((M, N), device=dev),
+                         acc=torch.empty((G, M, N), dtype=torch.int32, device=dev)))
+    lib = bl.lib
+
+    def stream():
+        return torch.cuda.current_stream(dev).cuda_stream
+
+    def ops(step, only=None):
+        wp = copies[step % len(copies)].data_ptr()
+        for b in bufs:
+            M = b["M"]
+            if only in (None, f"quant_act_grouped_M{M}"):
+                assert lib.bitlinear_quant_act_grouped(b["x"].data_ptr(), bl.F32, M, K, G, None, 0.0,
+                                                       b["q"].data_ptr(), b["g"].data_ptr(), stream()) == 0
+            if only in (None, f"forward_grouped_M{M}"):
+                acc = None if lib.bitlinear_forward_grouped_one_launch(M, K, G, N) else b["acc"].data_ptr()
+                assert lib.bitlinear_forward_grouped(b["q"].data_ptr(), b["g"].data_ptr(), M, K, G, wp,
+                                                     N, beta_d.data_ptr(), b["y"].data_ptr(),
+                                                     acc, stream()) == 0
+
+    s = torch.cuda.Stream(device=dev)
+
+    def graph(first, count, only=None):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(first, first + count):
+                ops(i, only)
+        return g
+
+    def time_graph(g, per_replay):
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / per_replay
+
+    ops(0)
+    torch.cuda.synchronize()
+    graph(0, args.warmup).replay()
+    us_step = time_graph(graph(args.warmup, args.steps), args.steps)
+    per_call = {}
+    for b in bufs:
+        M = b["M"]
+        for name in (f"quant_act_grouped_M{M}", f"forward_grouped_M{M}"):
+            per_call[name] = dict(avg_us=round(time_graph(graph(0, len(copies), name), len(copies)), 3))
+        alg = wbytes + M * K + 4 * G * M + 4 * M * N
+        per_call[f"forward_grouped_M{M}"].update(alg_bytes=alg, packed_w_GBs=round(
+            wbytes / (per_call[f"forward_grouped_M{M}"]["avg_us"] * 1e-6) / 1e9, 1))
+    dom = max((k for k in per_call if k.startswith("forward")), key=lambda k: per_call[k]["avg_us"])
+    d = per_call[dom]
+    gbs = d["alg_bytes"] / (d["avg_us"] * 1e-6) / 1e9
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        xs = [workloads.workload_activations(args.workload, b["M"]) for b in bufs]
+        est = sum(b["M"] for b in bufs) * w.size * 1.5e-9
+        rows = N
+        if est / max(oracle.num_threads(), 1) > args.cpu_seconds:
+            rows = max(64, int(N * args.cpu_seconds * oracle.num_threads() / est / 3))
+        wr = np.ascontiguousarray(w[:rows])
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            for x in xs:
+                q, g = oracle.quant_act_grouped(x, G)
+                oracle.forward_grouped(q, g, wr, beta)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or el / n * (n + 1) > 3 * args.cpu_seconds:
+                break
+        cpu = dict(value=round(wr.size // 4 * len(xs) * n / el / 1e9, 4), unit="packed-W GB/s",
+                   cores=oracle.num_threads(), kind="oracle",
+                   sample=f"{n} x (decode steps over {rows} of {N} output rows, G={G}), "
+                          f"M={[b['M'] for b in bufs]}, {el:.1f} s")
+    line = {
+        "metric": f"BitLinear with {G} group scales along K: packed-W GB/s",
+        "value": round(wbytes * len(bufs) / (us_step * 1e-6) / 1e9, 2),
+        "unit": "packed-W GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_step * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"grouped{G}_{wl.name}", "M": [b["M"] for b in bufs], "K": K, "N": N,
+                   "G": G, "weight_copies": len(copies), "timing": "hip_graph_of_all_timed_steps"},
+        "roofline": dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, call=dom,
+                         kernel=("decode_lds_kernel (groups in the epilogue)"
+                                 if lib.bitlinear_forward_grouped_one_launch(int(dom.split("M")[-1]), K, G, N)
+                                 else f"{G} group products + group_sum_kernel"),
+                         avg_launch_us=d["avg_us"],
+                         alg_bytes_per_launch=d["alg_bytes"]),
+        "cpu_baseline": cpu,
+        "per_call": per_call,
+    }
+    print(json.dumps(line), flush=True)
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -618,6 +743,9 @@ def main():
         return
     if args.op == "binary":
         bench_binary(args, torch, bl, dev)
+        return
+    if args.op == "grouped":
+        bench_grouped(args, torch, bl, dev)
         return
     if args.traffic_probe:
         args.no_rotate = True

@@ -40,6 +40,7 @@ _SIGNATURES = {
     "bitlinear_quant_act_grouped": [_vp, ctypes.c_int, _i64, _i64, _i64, _vp, _f32, _vp, _vp, _vp],
     "bitlinear_forward_grouped": [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
     "bitlinear_ternarize_grouped": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
+    "bitlinear_forward_grouped_one_launch": [_i64, _i64, _i64, _i64],
     "bitlinear_last_error": [],
     "bitlinear_abi_version": [],
 }
@@ -260,10 +261,11 @@ def quant_act_grouped(x: torch.Tensor, groups: int, rms_gain: Optional[torch.Ten
 
 
 def forward_grouped(x_q: torch.Tensor, gamma: torch.Tensor, w_packed: torch.Tensor,
-                    beta: torch.Tensor):
+                    beta: torch.Tensor, want_acc: bool = True):
     """Grouped BitLinear: x_q int8 [G][M][KG], gamma [G][M], w_packed
     [G][N][KG/16], beta fp32 [G] on the device -> (y fp32 [M][N], acc int32
-    [G][M][N])."""
+    [G][M][N]), or y alone with ``want_acc=False`` (the accumulators are then
+    still allocated when the shape needs them as the group products' home)."""
     _dev(x_q, "x_q", (torch.int8,))
     _dev(gamma, "gamma", (torch.float32,))
     _dev(w_packed, "w_packed", (torch.int32, torch.uint32))
@@ -273,11 +275,13 @@ def forward_grouped(x_q: torch.Tensor, gamma: torch.Tensor, w_packed: torch.Tens
         raise ValueError(f"w_packed shape {tuple(w_packed.shape)} does not match x_q {tuple(x_q.shape)}")
     N = w_packed.shape[1]
     y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
-    acc = torch.empty((G, M, N), dtype=torch.int32, device=x_q.device)
+    acc = None
+    if want_acc or not lib.bitlinear_forward_grouped_one_launch(M, G * KG, G, N):
+        acc = torch.empty((G, M, N), dtype=torch.int32, device=x_q.device)
     _check(lib.bitlinear_forward_grouped(x_q.data_ptr(), gamma.data_ptr(), M, G * KG, G,
                                          w_packed.data_ptr(), N, beta.data_ptr(), y.data_ptr(),
-                                         acc.data_ptr(), _stream(x_q)))
-    return y, acc
+                                         _ptr(acc), _stream(x_q)))
+    return (y, acc) if want_acc else y
 
 
 def ternarize_grouped(W_grouped: torch.Tensor, want_codes: bool = False):

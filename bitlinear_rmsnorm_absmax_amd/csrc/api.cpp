@@ -328,13 +328,22 @@ bitlinear_status_t bitlinear_forward_grouped(const int8_t* x_q, const float* gam
     BL_TRY(need(fn, "w_packed", w_packed, any_in, 16));
     BL_TRY(need(fn, "beta", beta, any_in, 4));
     BL_TRY(need(fn, "y", y, any_out, 4));
-    BL_TRY(need(fn, "acc", acc, any_out, 4));
+    if (acc && !aligned(acc, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: acc is not 4-byte aligned", fn);
     if (!any_out) return ok();
     if (K == 0) {
         hipError_t e = bl::launch_fill_zero(y, nullptr, M * N, stream);
-        if (e == hipSuccess) e = bl::launch_fill_zero(reinterpret_cast<float*>(acc), nullptr, G * M * N, stream);
+        if (e == hipSuccess && acc)
+            e = bl::launch_fill_zero(reinterpret_cast<float*>(acc), nullptr, G * M * N, stream);
         return from_hip(e, fn);
     }
+    if (bl::decode_lds_grouped_supports((int)M, (int)K, (int)G, (int)N))  // one launch
+        return from_hip(bl::launch_decode_lds_grouped(x_q, gamma, (int)M, (int)K, (int)G, w_packed,
+                                                      (int)N, beta, y, acc, stream),
+                        fn);
+    if (!acc)
+        return fail(BITLINEAR_ERR_NULL,
+                    "%s: acc is NULL; it may be NULL only on the one-launch path (G in {2, 4, 8}, "
+                    "M <= 16, K/G %% 256 == 0)", fn);
     const int64_t KG = K / G;
     for (int64_t g = 0; g < G; ++g) {
         const hipError_t e = launch_forward_kernel(x_q + g * M * KG, gamma + g * M, M, KG,
@@ -343,6 +352,12 @@ bitlinear_status_t bitlinear_forward_grouped(const int8_t* x_q, const float* gam
         if (e != hipSuccess) return from_hip(e, fn);
     }
     return from_hip(bl::launch_group_sum(acc, gamma, beta, M, N, G, y, stream), fn);
+}
+
+int bitlinear_forward_grouped_one_launch(int64_t M, int64_t K, int64_t G, int64_t N) {
+    if (M < 1 || M > 16 || N < 1 || N > kMaxN || K < 256 || K > BITLINEAR_MAX_K || G < 2 || G > 8)
+        return 0;
+    return bl::decode_lds_grouped_supports((int)M, (int)K, (int)G, (int)N) ? 1 : 0;
 }
 
 bitlinear_status_t bitlinear_ternarize_grouped(const float* W_grouped, int64_t N, int64_t K,

@@ -67,18 +67,20 @@ __device__ __forceinline__ void fence_code() {
 // lane (j, g) loads words 8c + 2g, 8c + 2g + 1 of chunk c (the same 64 K
 // positions as the 2-bit words 16c + 4g .. +3), and MFMA s takes bits
 // 4(s%2) .. +3 of word s/2.
-template <int CT, int NTW, int B, bool ONEBIT>
+template <int CT, int NTW, int B, bool ONEBIT, int G>
 __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
     const uint32_t* wp, int N, float beta, float* __restrict__ y, int32_t* __restrict__ acc_out,
-    int a_bytes) {
+    int a_bytes, const float* __restrict__ beta_g) {
     constexpr int CG = CT / NTW;         // column groups of a workgroup
     constexpr int KS = kDecWaves / CG;   // K ranges per column group
+    static_assert(KS % G == 0, "every wave's K range lies inside one group");
     typedef typename std::conditional<ONEBIT, v2u, v4u>::type wvec;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* As = smem;                                       // activations, a_bytes
     int* red = reinterpret_cast<int*>(smem + a_bytes);     // [8 waves][NTW][4][64]
-    int* Ssum = red + kDecWaves * NTW * 4 * kWave;         // [16] activation sums
+    int* Ssum = red + kDecWaves * NTW * 4 * kWave;         // [G][16] activation sums
+    float* Ssc = reinterpret_cast<float*>(Ssum + 16 * G);  // [G][16] output scales
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -94,6 +96,11 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int c_begin = kp * cpw;
     const int c_end = min(c_begin + cpw, nchunks);
     const int last = max(min(c_end, nchunks) - 1, 0);
+    // groups (G > 1): group-major operands, KG = K / G inputs per group; the
+    // launcher makes every wave's chunk range lie inside one group, gw
+    const int KG = K / G, cpg = nchunks / G;
+    const int gw = G > 1 ? c_begin / cpg : 0;
+    const int WRWG = ONEBIT ? (KG >> 5) : (KG >> 4);  // weight words per row of a group
 
     v4i acc[NTW];
 #pragma unroll
@@ -103,7 +110,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const uint32_t* wrow[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
-        wrow[t] = wp + (int64_t)min(n_base + 16 * t + j, N - 1) * WRW + (ONEBIT ? 2 : 4) * g;
+        wrow[t] = wp + ((int64_t)gw * N + min(n_base + 16 * t + j, N - 1)) * WRWG + (ONEBIT ? 2 : 4) * g;
     // A-operand row of lane j; rows past M repeat row M-1 (never stored)
     const int arow = min(j, M - 1);
     const char* arow_p = As + arow * K;
@@ -115,7 +122,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 #pragma unroll
             for (int t = 0; t < NTW; ++t)
                 bw[i][t] = __builtin_nontemporal_load(reinterpret_cast<const wvec*>(
-                    wrow[t] + (ONEBIT ? 8 : 16) * min(cb + i, last)));
+                    wrow[t] + (ONEBIT ? 8 : 16) * (min(cb + i, last) - gw * cpg)));
     };
     auto mul_batch = [&](int cb, const wvec (&bw)[B][NTW]) {
 #pragma unroll
@@ -150,7 +157,9 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
         for (int q = wv; q < ninstr; q += kDecWaves) {
             const int pos = min(q * 64 + lane, pieces - 1);
             const int r = pos / WR, slot = pos - r * WR;
-            copy16_to_lds(xq + (int64_t)r * K + 16 * (slot ^ (r & 15)), As + 1024 * q);
+            const int k = 16 * (slot ^ (r & 15));  // input index of the piece
+            const int kg = k / KG;                 // its group
+            copy16_to_lds(xq + ((int64_t)kg * M + r) * KG + (k - kg * KG), As + 1024 * q);
         }
     }
     fence_code();
@@ -164,16 +173,26 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
         __builtin_amdgcn_s_waitcnt(vm_wait_imm(B * NTW));  // own copies (older) have landed
         __builtin_amdgcn_s_barrier();
         fence_code();
-        // row r = tid / 32, 32 threads per row, whole rows (the slot order
-        // inside a row does not change a sum)
-        const int r = tid >> 5, part = tid & 31;
+        // row r = tid / 32, 32 threads per row, per group (the slot order
+        // inside a row does not change a sum; group gg holds slots
+        // gg*KG/16 .. (gg+1)*KG/16 since KG is a multiple of 256)
+        // output scales fl32(beta_g * gamma[g][m]) / 128 of every (group, row)
+        if (tid < 16 * G) {
+            const int gi = tid >> 4, ri = tid & 15;
+            Ssc[tid] = ri < M ? out_scale(beta_g ? beta_g[gi] : beta, gamma[(int64_t)gi * M + ri]) : 0.0f;
+        }
+        // 32 / G lanes per (row, group): lane `sub` of group gg takes the
+        // group's pieces sub, sub + 32/G, ...
+        constexpr int L = 32 / G;
+        const int r = tid >> 5, gg = (tid & 31) / L, sub = tid & (L - 1);
+        const int pg = KG >> 4;  // pieces per group
         int sum = 0;
         if (r < M)
-            for (int q = part; q < WR; q += 32)
+            for (int q = gg * pg + sub; q < (gg + 1) * pg; q += L)
                 sum = byte_sum16(*reinterpret_cast<const v4i*>(As + r * K + 16 * q), sum);
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-        if (part == 0) Ssum[r] = sum;
+        for (int o = L / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+        if (sub == 0) Ssum[gg * 16 + r] = sum;
     };
     if (c_end - c_begin <= B) {
         // one batch
@@ -214,55 +233,90 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = 4 * g + v;
-                int d = 0;
-                for (int k2 = 0; k2 < KS; ++k2)
-                    d += red[(((k2 * CG + cg) * NTW + t) * 4 + v) * kWave + lane];
-                if (row < M && col < N) {
-                    const int a = (ONEBIT ? 2 * d : d) - Ssum[row];
-                    const int64_t o = (int64_t)row * N + col;
-                    if (y) y[o] = (float)a * out_scale(beta, gamma[row]);
-                    if (acc_out) acc_out[o] = a;
+                if (row >= M || col >= N) continue;
+                // group gi = K parts gi*KPG .. (gi+1)*KPG; y adds the group
+                // terms in group order (G == 1: the one term)
+                constexpr int KPG = KS / G;
+                float yv = 0.0f;
+#pragma unroll
+                for (int gi = 0; gi < G; ++gi) {
+                    int d = 0;
+#pragma unroll
+                    for (int k2 = gi * KPG; k2 < (gi + 1) * KPG; ++k2)
+                        d += red[(((k2 * CG + cg) * NTW + t) * 4 + v) * kWave + lane];
+                    const int a = (ONEBIT ? 2 * d : d) - Ssum[gi * 16 + row];
+                    const float term = (float)a * Ssc[gi * 16 + row];
+                    yv = gi == 0 ? term : yv + term;
+                    if (acc_out) acc_out[((int64_t)gi * M + row) * N + col] = a;
                 }
+                if (y) y[(int64_t)row * N + col] = yv;
             }
         }
     }
 }
 
 // LDS bytes: the activation block rounded up to whole 1 KB copies, the
-// reduction buffer and the 16 activation sums.
+// reduction buffer, and 16 activation sums and 16 output scales per group.
 int decode_a_bytes(int M, int K) { return ((M * K + 1023) / 1024) * 1024; }
-size_t decode_lds_bytes(int M, int K, int ntw) {
-    return (size_t)decode_a_bytes(M, K) + (size_t)kDecWaves * ntw * 4 * kWave * 4 + 16 * 4;
+size_t decode_lds_bytes(int M, int K, int ntw, int G = 1) {
+    return (size_t)decode_a_bytes(M, K) + (size_t)kDecWaves * ntw * 4 * kWave * 4 + 2 * 16 * 4 * (size_t)G;
 }
 
-template <int CT, int NTW, int B, bool ONEBIT>
+template <int CT, int NTW, int B, bool ONEBIT, int G>
 hipError_t launch_ctb(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
-                      float beta, float* y, int32_t* acc, hipStream_t s) {
+                      float beta, float* y, int32_t* acc, hipStream_t s, const float* beta_g) {
     static bool attr_set = false;  // per-kernel opt-in to more than 64 KB of dynamic LDS
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT>),
+            reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT, G>),
             hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int blocks = (N + 16 * CT - 1) / (16 * CT);
-    decode_lds_kernel<CT, NTW, B, ONEBIT><<<dim3(blocks), dim3(kDecWaves * kWave),
-                                            decode_lds_bytes(M, K, NTW), s>>>(
-        xq, gamma, M, K, wp, N, beta, y, acc, decode_a_bytes(M, K));
+    decode_lds_kernel<CT, NTW, B, ONEBIT, G><<<dim3(blocks), dim3(kDecWaves * kWave),
+                                               decode_lds_bytes(M, K, NTW, G), s>>>(
+        xq, gamma, M, K, wp, N, beta, y, acc, decode_a_bytes(M, K), beta_g);
     return hipGetLastError();
 }
 
 // Batch: a wave's whole K range in one batch when it has at most 4 chunks,
 // else a stream of 2-chunk batches (measured at K = 2560 .. 8192: larger
 // batches stall load issue, a 2-chunk stream is 15 % faster at K = 8192).
-template <int CT, int NTW, bool ONEBIT>
+template <int CT, int NTW, bool ONEBIT, int G = 1>
 hipError_t launch_ct(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
-                     float beta, float* y, int32_t* acc, hipStream_t s) {
+                     float beta, float* y, int32_t* acc, hipStream_t s,
+                     const float* beta_g = nullptr) {
     constexpr int KS = kDecWaves * NTW / CT;
     const int cpw = ((K >> 8) + KS - 1) / KS;
-    if (cpw <= 4) return launch_ctb<CT, NTW, 4, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    return launch_ctb<CT, NTW, 2, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (cpw <= 4) return launch_ctb<CT, NTW, 4, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    return launch_ctb<CT, NTW, 2, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+}
+
+// Grouped launch of one width: G as a template argument (2, 4 or 8, at most
+// the width's K parts).
+template <int CT, int NTW>
+hipError_t launch_ct_groups(const int8_t* xq, const float* gamma, int M, int K, int G,
+                            const uint32_t* wp, int N, const float* beta_g, float* y, int32_t* acc,
+                            hipStream_t s) {
+    constexpr int KS = kDecWaves * NTW / CT;
+    if (G == 2) return launch_ct<CT, NTW, false, 2>(xq, gamma, M, K, wp, N, 0.f, y, acc, s, beta_g);
+    if constexpr (KS >= 4)
+        if (G == 4) return launch_ct<CT, NTW, false, 4>(xq, gamma, M, K, wp, N, 0.f, y, acc, s, beta_g);
+    if constexpr (KS >= 8)
+        if (G == 8) return launch_ct<CT, NTW, false, 8>(xq, gamma, M, K, wp, N, 0.f, y, acc, s, beta_g);
+    return hipErrorInvalidValue;
+}
+
+// K parts of the widths below, widest first: <8,2> 2, <4,2> 4, <2,1> 4, <1,1> 8.
+// Grouped launches need KS % G == 0 and (K/256) % KS == 0 so that every wave's
+// K range lies inside one group.
+int grouped_width(int tiles, int G, int nchunks) {
+    const int ct[4] = {8, 4, 2, 1}, ks[4] = {2, 4, 4, 8}, min_tiles[4] = {8 * 160, 4 * 160, 2 * 160, 0};
+    int pick = -1;
+    for (int i = 3; i >= 0; --i)  // the widest fitting config that still leaves >= 160 workgroups
+        if (ks[i] % G == 0 && nchunks % ks[i] == 0 && (pick < 0 || tiles >= min_tiles[i])) pick = i;
+    return pick < 0 ? -1 : ct[pick];
 }
 
 template <bool ONEBIT>
@@ -283,6 +337,26 @@ hipError_t launch_widths(const int8_t* xq, const float* gamma, int M, int K, con
 bool decode_lds_supports(int M, int K, int N) {
     return M >= 1 && M <= 16 && K >= 256 && K % 256 == 0 && N > 0 &&
            decode_lds_bytes(M, K, 2) <= (size_t)kDecLdsMax;
+}
+
+bool decode_lds_grouped_supports(int M, int K, int G, int N) {
+    if ((G != 2 && G != 4 && G != 8) || M < 1 || M > 16 || N <= 0 || K % 256 != 0 || K % G != 0 || (K / G) % 256 != 0)
+        return false;
+    return grouped_width((N + 15) / 16, G, K >> 8) > 0 &&
+           decode_lds_bytes(M, K, 2, G) <= (size_t)kDecLdsMax;
+}
+
+hipError_t launch_decode_lds_grouped(const int8_t* xq, const float* gamma, int M, int K, int G,
+                                     const uint32_t* wp, int N, const float* beta_g, float* y,
+                                     int32_t* acc, hipStream_t s) {
+    if (G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
+    switch (grouped_width((N + 15) / 16, G, K >> 8)) {
+        case 8: return launch_ct_groups<8, 2>(xq, gamma, M, K, G, wp, N, beta_g, y, acc, s);
+        case 4: return launch_ct_groups<4, 2>(xq, gamma, M, K, G, wp, N, beta_g, y, acc, s);
+        case 2: return launch_ct_groups<2, 1>(xq, gamma, M, K, G, wp, N, beta_g, y, acc, s);
+        case 1: return launch_ct_groups<1, 1>(xq, gamma, M, K, G, wp, N, beta_g, y, acc, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,

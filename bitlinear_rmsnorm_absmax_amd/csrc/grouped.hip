@@ -25,18 +25,19 @@ __global__ __launch_bounds__(kGsThreads) void group_sum_kernel(const int32_t* __
     if (i >= MN) return;
     const int64_t m = i / N;
     float s[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) s[v] = 0.0f;
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < G; ++g) {  // the first term starts the sum
         const float sc = out_scale(beta[g], gamma[(int64_t)g * M + m]);
         const int32_t* a = acc + (int64_t)g * MN + i;
+        float t[V];
         if constexpr (V == 4) {
             const v4i a4 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(a));
-            s[0] += (float)a4.x * sc; s[1] += (float)a4.y * sc;
-            s[2] += (float)a4.z * sc; s[3] += (float)a4.w * sc;
+            t[0] = (float)a4.x * sc; t[1] = (float)a4.y * sc;
+            t[2] = (float)a4.z * sc; t[3] = (float)a4.w * sc;
         } else {
-            s[0] += (float)a[0] * sc;
+            t[0] = (float)a[0] * sc;
         }
+#pragma unroll
+        for (int v = 0; v < V; ++v) s[v] = g == 0 ? t[v] : s[v] + t[v];
     }
     if constexpr (V == 4)
         *reinterpret_cast<v4f*>(y + i) = v4f{s[0], s[1], s[2], s[3]};

@@ -40,6 +40,13 @@ hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
                              const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                              hipStream_t s);
 // Same kernel on 1-bit weights [N][K/32].
+// Grouped decode product in one launch (group-major x_q [G][M][K/G],
+// gamma [G][M], packed weights [G][N][K/G/16], beta [G] on the device; acc
+// [G][M][N] and y written), when decode_lds_grouped_supports() holds.
+bool decode_lds_grouped_supports(int M, int K, int G, int N);
+hipError_t launch_decode_lds_grouped(const int8_t* xq, const float* gamma, int M, int K, int G,
+                                     const uint32_t* wp, int N, const float* beta_g, float* y,
+                                     int32_t* acc, hipStream_t s);
 hipError_t launch_decode_lds1(const int8_t* xq, const float* gamma, int M, int K,
                               const uint32_t* wp1, int N, float beta, float* y, int32_t* acc,
                               hipStream_t s);

@@ -186,7 +186,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
 
 // Group quantisation (unite.ai BitNet.cpp article, Gruppenquantisierung und
 // -normalisierung): row `row` split into G runs of K/G inputs, each run
-// quantised with its own absmax scale.  One workgroup per row; per group an
+// quantised with its own absmax scale.  One workgroup per (row, run): an
 // absmax pass and a quantisation pass over the run's 16-element chunks (the
 // second pass re-reads the run, L2-resident by then).  RMS: the whole row's
 // sum of squares first (same chunk order and reduction as quant_rows_kernel,
@@ -197,6 +197,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_groups_kernel(
     RowSrc src, int K, int G, int M, const float* __restrict__ gain, float eps,
     int8_t* __restrict__ q, float* __restrict__ gamma_out) {
     const int64_t row = blockIdx.x;
+    const int g = blockIdx.y;
     const int KG = K / G, nch = KG / 16;
     auto load_u = [&](int c, float v[16]) {  // chunk c of the row, gain applied
         load_chunk<S>(src, row, K, c, v);
@@ -223,24 +224,21 @@ __global__ __launch_bounds__(kQuantThreads) void quant_groups_kernel(
         r = 1.0 / sqrt(ss / (double)K + (double)eps);
         __syncthreads();  // the reduction scratch is reused below
     }
-    for (int g = 0; g < G; ++g) {
-        float amax = 0.0f;
-        double unused = 0.0;
-        for (int c = threadIdx.x; c < nch; c += kQuantThreads) {
-            float v[16];
-            load_u(g * nch + c, v);
+    float amax = 0.0f;
+    double unused = 0.0;
+    for (int c = threadIdx.x; c < nch; c += kQuantThreads) {
+        float v[16];
+        load_u(g * nch + c, v);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
-        }
-        block_reduce(amax, unused, false);
-        if (threadIdx.x == 0) gamma_out[(int64_t)g * M + row] = RMS ? (float)(r * (double)amax) : amax;
-        int8_t* qg = q + (int64_t)g * M * KG;
-        for (int c = threadIdx.x; c < nch; c += kQuantThreads) {
-            float v[16];
-            load_u(g * nch + c, v);
-            store_codes(qg, row, KG, c, v, amax);
-        }
-        __syncthreads();  // the reduction scratch is reused by the next group
+        for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+    }
+    block_reduce(amax, unused, false);
+    if (threadIdx.x == 0) gamma_out[(int64_t)g * M + row] = RMS ? (float)(r * (double)amax) : amax;
+    int8_t* qg = q + (int64_t)g * M * KG;
+    for (int c = threadIdx.x; c < nch; c += kQuantThreads) {
+        float v[16];
+        load_u(g * nch + c, v);
+        store_codes(qg, row, KG, c, v, amax);
     }
 }
 
@@ -281,7 +279,7 @@ hipError_t launch_quant_act_grouped(const void* x, int bf16, int64_t M, int64_t 
                                     hipStream_t s) {
     if (M == 0) return hipSuccess;
     RowSrc src{x, nullptr};
-    dim3 grid((unsigned)M), block(kQuantThreads);
+    dim3 grid((unsigned)M, (unsigned)G), block(kQuantThreads);
     const int k = (int)K, g = (int)G, m = (int)M;
     if (bf16) {
         if (gain)

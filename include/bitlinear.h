@@ -264,15 +264,23 @@ bitlinear_status_t bitlinear_quant_act_grouped(const void* x, bitlinear_dtype_t 
  * bitlinear_pack_weights (packing a group-major int8 [G][N][KG] tensor as
  * G*N rows of KG gives this layout).  beta: DEVICE fp32 [G] (finite; as
  * written by bitlinear_ternarize_grouped).  y out fp32 [M][N].  acc out int32
- * [G][M][N], REQUIRED: it holds the group products the final sum reads.
+ * [G][M][N] (the group products).
  * Requires G >= 1, K % G == 0, KG % 64 == 0; other limits as for
- * bitlinear_forward with K = KG.  Each group runs the kernel bitlinear_forward
- * picks for (M, KG, N) in accumulator-only mode, then one launch adds the
- * groups; G + 1 launches on `stream`, none allocates. */
+ * bitlinear_forward with K = KG.
+ * Decode shapes (M <= 16, G in {2, 4, 8}, KG % 256 == 0, the activations
+ * fitting in LDS): one launch of the LDS decode kernel with the group terms
+ * added in its epilogue; acc may be NULL there.  Otherwise each group runs
+ * the kernel bitlinear_forward picks for (M, KG, N) in accumulator-only mode
+ * into acc, then one launch adds the groups (G + 1 launches); acc is then
+ * required (NULL returns BITLINEAR_ERR_NULL).  None allocates. */
 bitlinear_status_t bitlinear_forward_grouped(const int8_t* x_q, const float* gamma, int64_t M,
                                              int64_t K, int64_t G, const uint32_t* w_packed,
                                              int64_t N, const float* beta, float* y, int32_t* acc,
                                              hipStream_t stream);
+
+/* 1 if bitlinear_forward_grouped takes the one-launch path for this shape
+ * (acc may then be NULL), else 0.  Host-only, no HIP call. */
+int bitlinear_forward_grouped_one_launch(int64_t M, int64_t K, int64_t G, int64_t N);
 
 /* Absmean ternarisation per weight group (the rule of bitlinear_ternarize
  * applied to each group's N x KG block).  W_grouped: fp32 [G][N][KG], group g

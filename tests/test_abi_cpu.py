@@ -21,7 +21,7 @@ def test_every_declared_symbol_is_exported():
         "bitlinear_forward_path", "bitlinear_silu_mul_quant", "bitlinear_ternarize",
         "bitlinear_binarize", "bitlinear_pack_weights1", "bitlinear_forward1",
         "bitlinear_quant_act_grouped", "bitlinear_forward_grouped", "bitlinear_ternarize_grouped",
-        "bitlinear_last_error", "bitlinear_abi_version"}
+        "bitlinear_forward_grouped_one_launch", "bitlinear_last_error", "bitlinear_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -247,7 +247,8 @@ def _fg(xq=FAKE, g=FAKE, M=2, K=256, G=2, w=FAKE, N=3, beta=FAKE, y=FAKE, acc=FA
     (dict(K=256, G=3), bl.ERR_SHAPE, "runs of a multiple of 64"),
     (dict(K=128, G=4), bl.ERR_SHAPE, "runs of a multiple of 64"),
     (dict(K=24), bl.ERR_SHAPE, "multiple of 16"),
-    (dict(acc=None), bl.ERR_NULL, "acc is NULL"),
+    (dict(acc=None, M=33), bl.ERR_NULL, "acc is NULL"),
+    (dict(acc=FAKE + 2), bl.ERR_ALIGN, "acc is not 4-byte aligned"),
     (dict(beta=None), bl.ERR_NULL, "beta is NULL"),
     (dict(y=None), bl.ERR_NULL, "y is NULL"),
     (dict(w=FAKE + 8), bl.ERR_ALIGN, "w_packed is not 16-byte aligned"),
@@ -280,3 +281,13 @@ def _tg(W=FAKE, N=4, K=256, G=2, wp=FAKE, codes=None, b=FAKE, b64=FAKE):
 def test_ternarize_grouped_rejects(kw, status, msg):
     assert _tg(**kw) == status
     assert msg in bl.last_error()
+
+
+def test_grouped_one_launch_query():
+    q = bl.lib.bitlinear_forward_grouped_one_launch
+    assert q(16, 4096, 4, 11008) == 1
+    assert q(1, 2048, 2, 333) == 1
+    assert q(17, 4096, 4, 11008) == 0     # more tokens than the decode kernel takes
+    assert q(4, 512, 4, 1000) == 0        # runs of 128 inputs: not whole 256-chunks
+    assert q(4, 4096, 1, 1000) == 0       # one group is the ungrouped product
+    assert q(4, 3072, 3, 1000) == 0       # 3 groups: no K split divides into them

@@ -584,7 +584,8 @@ def test_quant_grouped_parity(dev, M, K, G, src):
 
 @pytest.mark.parametrize("M,K,G,N", [
     (1, 4096, 4, 1000), (4, 4096, 4, 700), (16, 4096, 4, 2000), (5, 2048, 2, 333),
-    (33, 1024, 4, 517), (100, 2560, 5, 300), (2, 512, 8, 129), (1, 256, 1, 64)])
+    (33, 1024, 4, 517), (100, 2560, 5, 300), (2, 512, 8, 129), (1, 256, 1, 64),
+    (8, 8192, 8, 600), (3, 4096, 2, 20480), (16, 2048, 8, 5000), (12, 4096, 4, 11008)])
 def test_forward_grouped_parity(dev, M, K, G, N):
     rng = workloads.rng_for(971, M, K, G, N)
     x = rng.standard_normal((M, K)).astype(np.float32)
@@ -652,3 +653,18 @@ def test_grouped_empty(dev):
     assert q.shape == (4, 0, 64)
     q, g = bl.quant_act_grouped(torch.zeros((3, 256), device=dev), 4)
     assert not host(q).any() and not host(g).any()
+
+
+def test_forward_grouped_without_acc(dev):
+    # the one-launch decode path takes acc = NULL and gives the same y
+    rng = workloads.rng_for(975, 1)
+    M, K, G, N = 16, 4096, 4, 3000
+    assert bl.lib.bitlinear_forward_grouped_one_launch(M, K, G, N) == 1
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = workloads.ternary(rng, N, K, workloads.TERNARY_HALF_ZERO)
+    beta = to_dev(rng.uniform(0.01, 0.05, G).astype(np.float32), dev)
+    q, g = bl.quant_act_grouped(to_dev(x, dev), G)
+    wp = pack_grouped(w, G, dev)
+    y1, _ = bl.forward_grouped(q, g, wp, beta)
+    y2 = bl.forward_grouped(q, g, wp, beta, want_acc=False)
+    np.testing.assert_array_equal(host(y2), host(y1))
