@@ -58,6 +58,8 @@ def _load() -> ctypes.CDLL:
             "oracle_unpack1": [_c_p, _i64, _i64, _c_p],
             "oracle_quant_act_grouped": [_c_p, _c_p, ctypes.c_float, _i64, _i64, _i64, _c_p,
                                          _c_p],
+            "oracle_pack3": [_c_p, _i64, _i64, _c_p],
+            "oracle_unpack3": [_c_p, _i64, _i64, _c_p],
             "oracle_num_threads": [],
         }
         for name, args in sig.items():
@@ -70,6 +72,8 @@ def _load() -> ctypes.CDLL:
         lib.oracle_binarize.restype = ctypes.c_double
         lib.oracle_pack1.restype = ctypes.c_int64
         lib.oracle_unpack1.restype = None
+        lib.oracle_pack3.restype = ctypes.c_int64
+        lib.oracle_unpack3.restype = None
         for name in ("oracle_bf16_to_f32", "oracle_quant_act", "oracle_rmsnorm_quant_act",
                      "oracle_quant_act_grouped",
                      "oracle_rmsnorm_quant_act_literal", "oracle_unpack", "oracle_rescale",
@@ -193,6 +197,26 @@ def unpack1(packed: np.ndarray, K: int) -> np.ndarray:
     N = packed.shape[0]
     w = np.empty((N, K), dtype=np.int8)
     _load().oracle_unpack1(_p(packed), N, K, _p(w))
+    return w
+
+
+def pack3(w: np.ndarray) -> Tuple[np.ndarray, int]:
+    """Ternary int8 [N][K] (K % 16 == 0) -> (base-3 bytes uint8
+    [N][ceil(K/80)*16], #entries outside {-1, 0, 1})."""
+    w = _c(w, np.int8)
+    N, K = w.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    out = np.empty((N, (K + 79) // 80 * 16), dtype=np.uint8)
+    bad = _load().oracle_pack3(_p(w), N, K, _p(out))
+    return out, int(bad)
+
+
+def unpack3(packed: np.ndarray, K: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    N = packed.shape[0]
+    w = np.empty((N, K), dtype=np.int8)
+    _load().oracle_unpack3(_p(packed), N, K, _p(w))
     return w
 
 

@@ -313,3 +313,57 @@ void oracle_unpack1(const uint32_t* packed, int64_t N, int64_t K, int8_t* w) {
             }
         }
 }
+
+/* Base-3 packing at 1.6 bits per weight ([U] Ternäres Gewichtssystem: three
+ * states need a little more than one bit, about 1.58; five ternary codes
+ * fit one byte since 3^5 = 243 <= 256).  Layout: a row is U = ceil(K/80)
+ * units of 16 bytes; byte b of 32-bit word w of unit u holds the five
+ * weights k = 80u + 20w + 4i + b (i = 0..4) as v = sum_i (w_k + 1) * 3^(4-i),
+ * stored as the byte ceil(256 v / 243); weights past K are 0.  The stored
+ * byte decodes as v = floor(243 b / 256) and then by base-3 digits. */
+static const int pow3[5] = {81, 27, 9, 3, 1};
+
+int64_t oracle_pack3(const int8_t* w, int64_t N, int64_t K, uint8_t* packed) {
+    const int64_t U = (K + 79) / 80;
+    int64_t bad = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t u = 0; u < U; ++u) {
+            for (int wd = 0; wd < 4; ++wd) {
+                for (int b = 0; b < 4; ++b) {
+                    int v = 0;
+                    for (int i = 0; i < 5; ++i) {
+                        const int64_t k = 80 * u + 20 * wd + 4 * i + b;
+                        int c = 1;
+                        if (k < K) {
+                            const int x = w[n * K + k];
+                            if (x < -1 || x > 1) ++bad;
+                            else c = x + 1;
+                        }
+                        v += c * pow3[i];
+                    }
+                    packed[(n * U + u) * 16 + 4 * wd + b] = (uint8_t)((256 * v + 242) / 243);
+                }
+            }
+        }
+    }
+    return bad;
+}
+
+void oracle_unpack3(const uint8_t* packed, int64_t N, int64_t K, int8_t* w) {
+    const int64_t U = (K + 79) / 80;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t u = 0; u < U; ++u) {
+            for (int wd = 0; wd < 4; ++wd) {
+                for (int b = 0; b < 4; ++b) {
+                    int v = (243 * (int)packed[(n * U + u) * 16 + 4 * wd + b]) / 256;
+                    for (int i = 0; i < 5; ++i) {
+                        const int c = v / pow3[i];
+                        v -= c * pow3[i];
+                        const int64_t k = 80 * u + 20 * wd + 4 * i + b;
+                        if (k < K) w[n * K + k] = (int8_t)(c - 1);
+                    }
+                }
+            }
+        }
+    }
+}

@@ -98,6 +98,17 @@ void oracle_unpack1(const uint32_t* packed, int64_t N, int64_t K, int8_t* w);
 /* Number of OpenMP threads the accumulate loop runs on. */
 int oracle_num_threads(void);
 
+/* Base-3 packing, 1.6 bits per weight ([U] Ternäres Gewichtssystem: about
+ * 1.58 bits carry three states; 3^5 = 243 fits a byte).  Ternary w int8
+ * [N][K] -> bytes [N][ceil(K/80)][16]: byte b of word w of unit u holds the
+ * weights k = 80u + 20w + 4i + b, i = 0..4, as v = sum (w_k + 1) 3^(4-i),
+ * stored as ceil(256 v / 243); weights past K are 0.  Returns the number of
+ * entries outside {-1, 0, 1} (packed as 0). */
+int64_t oracle_pack3(const int8_t* w, int64_t N, int64_t K, uint8_t* packed);
+
+/* Inverse of oracle_pack3: v = floor(243 b / 256), then base-3 digits. */
+void oracle_unpack3(const uint8_t* packed, int64_t N, int64_t K, int8_t* w);
+
 #ifdef __cplusplus
 }
 #endif

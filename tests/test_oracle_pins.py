@@ -627,3 +627,67 @@ def test_ternarize_grouped_recovers_scaled_ternary_blocks():
     w0, b0 = oracle.ternarize(W)
     np.testing.assert_array_equal(w1, w0)
     assert b1[0] == b0
+
+
+# ---------------------------------------------------------------- base-3 packing
+
+def test_pack3_worked_example():
+    g = _golden("pack3_1x96.json")
+    w = np.zeros((1, g["K"]), np.int8)
+    for k, v in g["nonzero"].items():
+        w[0, int(k)] = v
+    packed, bad = oracle.pack3(w)
+    assert bad == 0
+    np.testing.assert_array_equal(packed[0], np.array(g["packed"], np.uint8))
+    np.testing.assert_array_equal(oracle.unpack3(packed, g["K"]), w)
+
+
+def test_pack3_every_byte_value():
+    # all 243 five-trit combinations in byte 0 of word 0: the stored byte is
+    # ceil(256 v / 243) of the base-3 value (most significant digit first),
+    # computed here from the definition, and unpacks back
+    import itertools
+    rows = []
+    for digits in itertools.product((0, 1, 2), repeat=5):
+        w = np.zeros(80, np.int8)
+        for i, d in enumerate(digits):
+            w[4 * i] = d - 1
+        rows.append(w)
+    W = np.stack(rows)
+    packed, bad = oracle.pack3(W)
+    assert bad == 0
+    for r, digits in enumerate(itertools.product((0, 1, 2), repeat=5)):
+        v = sum(d * 3 ** (4 - i) for i, d in enumerate(digits))
+        assert int(packed[r, 0]) == -(-256 * v // 243)
+        assert (packed[r, 1:] == 128).all()
+    np.testing.assert_array_equal(oracle.unpack3(packed, 80), W)
+    assert len(set(packed[:, 0].tolist())) == 243
+
+
+def test_pack3_bytes_decode_by_multiplication():
+    # the stored byte b = ceil(256 v / 243) gives v's base-3 digits by the
+    # multiplication walk x <- 3x, digit = x // 256, x <- x mod 256 (five
+    # steps), for every v: the decode the vector-ALU kernels use
+    for v in range(243):
+        b = -(-256 * v // 243)
+        x, digits = b, []
+        for _ in range(5):
+            x *= 3
+            digits.append(x >> 8)
+            x &= 0xFF
+        assert sum(d * 3 ** (4 - i) for i, d in enumerate(digits)) == v, v
+
+
+def test_pack3_sizes_ranges_and_round_trip():
+    rng = workloads.rng_for(930, 1)
+    for K in (16, 80, 96, 4096, 2560, 6912):
+        w = workloads.ternary(rng, 5, K, workloads.TERNARY_UNIFORM)
+        packed, bad = oracle.pack3(w)
+        assert packed.shape == (5, 16 * ((K + 79) // 80)) and bad == 0
+        np.testing.assert_array_equal(oracle.unpack3(packed, K), w)
+    assert oracle.pack3(np.zeros((1, 80), np.int8))[0].tolist() == [[128] * 16]
+    assert oracle.pack3(np.ones((1, 80), np.int8))[0].tolist() == [[255] * 16]
+    assert oracle.pack3(-np.ones((1, 80), np.int8))[0].tolist() == [[0] * 16]
+    w = np.zeros((2, 32), np.int8)
+    w[1, 5] = 3
+    assert oracle.pack3(w)[1] == 1
