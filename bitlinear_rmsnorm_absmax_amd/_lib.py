@@ -41,6 +41,8 @@ _SIGNATURES = {
     "bitlinear_forward_grouped": [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
     "bitlinear_ternarize_grouped": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "bitlinear_forward_grouped_one_launch": [_i64, _i64, _i64, _i64],
+    "bitlinear_pack_weights3": [_vp, _i64, _i64, _vp, _vp, _vp],
+    "bitlinear_forward3": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _vp],
     "bitlinear_last_error": [],
     "bitlinear_abi_version": [],
 }
@@ -299,6 +301,40 @@ def ternarize_grouped(W_grouped: torch.Tensor, want_codes: bool = False):
                                            _ptr(codes), beta.data_ptr(), beta64.data_ptr(),
                                            _stream(W_grouped)))
     return (packed, beta, beta64, codes) if want_codes else (packed, beta, beta64)
+
+
+def pack_weights3(w: torch.Tensor, check: bool = True):
+    """Ternary int8 [N][K] -> base-3 packed bytes as int32 words [N][4*ceil(K/80)]
+    (1.6 bits per weight), and the bad-count int32 [1]."""
+    _dev(w, "w", (torch.int8,))
+    N, K = w.shape
+    packed3 = torch.empty((N, 4 * ((K + 79) // 80)), dtype=torch.int32, device=w.device)
+    bad = torch.zeros((1,), dtype=torch.int32, device=w.device)
+    _check(lib.bitlinear_pack_weights3(w.data_ptr(), N, K, packed3.data_ptr(), bad.data_ptr(),
+                                       _stream(w)))
+    if check:
+        n_bad = int(bad.item())
+        if n_bad:
+            raise ValueError(f"{n_bad} weight entries are not ternary")
+    return packed3, bad
+
+
+def forward3(x_q: torch.Tensor, gamma: torch.Tensor, w_packed3: torch.Tensor, beta: float,
+             want_acc: bool = False):
+    """BitLinear on base-3 weights -> y [M][N] (and acc with ``want_acc``)."""
+    _dev(x_q, "x_q", (torch.int8,))
+    _dev(gamma, "gamma", (torch.float32,))
+    _dev(w_packed3, "w_packed3", (torch.int32, torch.uint32))
+    M, K = x_q.shape
+    N = w_packed3.shape[0]
+    if w_packed3.shape[1] != 4 * ((K + 79) // 80):
+        raise ValueError(f"w_packed3 has {w_packed3.shape[1]} words per row, K={K} needs "
+                         f"{4 * ((K + 79) // 80)}")
+    y = torch.empty((M, N), dtype=torch.float32, device=x_q.device)
+    acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device) if want_acc else None
+    _check(lib.bitlinear_forward3(x_q.data_ptr(), gamma.data_ptr(), M, K, w_packed3.data_ptr(), N,
+                                  float(beta), y.data_ptr(), _ptr(acc), _stream(x_q)))
+    return (y, acc) if want_acc else y
 
 
 def bitlinear(x: torch.Tensor, w_packed: torch.Tensor, beta: float,

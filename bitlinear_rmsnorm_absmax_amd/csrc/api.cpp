@@ -387,6 +387,43 @@ bitlinear_status_t bitlinear_ternarize_grouped(const float* W_grouped, int64_t N
     return ok();
 }
 
+bitlinear_status_t bitlinear_pack_weights3(const int8_t* w, int64_t N, int64_t K,
+                                           uint32_t* w_packed3, int32_t* bad_count,
+                                           hipStream_t stream) {
+    const char* fn = "bitlinear_pack_weights3";
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    BL_TRY(check_k(fn, "K", K));
+    const bool any = N > 0 && K > 0;
+    BL_TRY(need(fn, "w", w, any, 16));
+    BL_TRY(need(fn, "w_packed3", w_packed3, any, 16));
+    if (bad_count && !aligned(bad_count, 4))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: bad_count is not 4-byte aligned", fn);
+    if (!any && !bad_count) return ok();
+    return from_hip(bl::launch_pack3(w, any ? N : 0, any ? K : 0, w_packed3, bad_count, stream), fn);
+}
+
+bitlinear_status_t bitlinear_forward3(const int8_t* x_q, const float* gamma, int64_t M, int64_t K,
+                                      const uint32_t* w_packed3, int64_t N, float beta, float* y,
+                                      int32_t* acc, hipStream_t stream) {
+    const char* fn = "bitlinear_forward3";
+    BL_TRY(check_rows(fn, "M", M, (1LL << 31) - 1));
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    BL_TRY(check_k(fn, "K", K));
+    if (!std::isfinite(beta)) return fail(BITLINEAR_ERR_VALUE, "%s: beta is not finite", fn);
+    const bool any_out = M > 0 && N > 0;
+    const bool any_in = any_out && K > 0;
+    BL_TRY(need(fn, "x_q", x_q, any_in, 16));
+    BL_TRY(need(fn, "gamma", gamma, any_in, 4));
+    BL_TRY(need(fn, "w_packed3", w_packed3, any_in, 16));
+    BL_TRY(need(fn, "y", y, any_out, 4));
+    if (acc && !aligned(acc, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: acc is not 4-byte aligned", fn);
+    if (!any_out) return ok();
+    if (K == 0) return from_hip(bl::launch_fill_zero(y, acc, M * N, stream), fn);
+    return from_hip(bl::launch_forward3(x_q, gamma, (int)M, (int)K, w_packed3, (int)N, beta, y, acc,
+                                        stream),
+                    fn);
+}
+
 const char* bitlinear_last_error(void) { return g_err; }
 
 int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }

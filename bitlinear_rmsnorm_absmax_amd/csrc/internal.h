@@ -83,6 +83,12 @@ hipError_t launch_quant_act_grouped(const void* x, int bf16, int64_t M, int64_t 
 // y = sum over g of fl32(acc[g]) * fl32(beta[g] * gamma[g][m]) / 128 (beta on the device).
 hipError_t launch_group_sum(const int32_t* acc, const float* gamma, const float* beta, int64_t M,
                             int64_t N, int64_t G, float* y, hipStream_t s);
+// Base-3 weights (1.6 bits): packing [N][ceil(K/80)][16 bytes] and the
+// decode product on the vector ALUs (passes of up to four tokens).
+hipError_t launch_pack3(const int8_t* w, int64_t N, int64_t K, uint32_t* packed3, int* bad_count,
+                        hipStream_t s);
+hipError_t launch_forward3(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
+                           int N, float beta, float* y, int32_t* acc, hipStream_t s);
 hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
                            const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                            hipStream_t s);

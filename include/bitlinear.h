@@ -293,6 +293,34 @@ bitlinear_status_t bitlinear_ternarize_grouped(const float* W_grouped, int64_t N
                                                int64_t G, uint32_t* w_packed, int8_t* w_ternary,
                                                float* beta, double* beta64, hipStream_t stream);
 
+/*
+ * Base-3 weights at 1.6 bits per weight (unite.ai article, section
+ * "Ternäres Gewichtssystem / Das Konzept": three states carry about 1.58
+ * bits; five ternary codes fit one byte since 3^5 = 243 <= 256), 20 % fewer
+ * weight bytes than the 2-bit layout.
+ *
+ * Layout: a row is U = ceil(K/80) units of 16 bytes, row n at byte 16*U*n.
+ * Byte b of little-endian 32-bit word w of unit u holds the weights
+ * k = 80u + 20w + 4i + b, i = 0..4, as v = sum (w_k + 1) * 3^(4-i), stored
+ * as the byte ceil(256 v / 243) (so v = floor(243 b / 256)); weights past K
+ * are 0.
+ */
+
+/* Ternary int8 [N][K] -> base-3 bytes [N][16*ceil(K/80)] (16-byte aligned).
+ * bad_count as for bitlinear_pack_weights (entries outside {-1,0,1} pack as
+ * 0).  K % 16 == 0.  One launch (two with bad_count). */
+bitlinear_status_t bitlinear_pack_weights3(const int8_t* w, int64_t N, int64_t K,
+                                           uint32_t* w_packed3, int32_t* bad_count,
+                                           hipStream_t stream);
+
+/* bitlinear_forward on base-3 weights: the same acc, y and argument rules,
+ * with w_packed3 the bitlinear_pack_weights3 layout (16-byte aligned).  A
+ * decode product on the vector ALUs: tokens go in passes of up to four, each
+ * a pass over the weights; for many tokens use the 2-bit layout. */
+bitlinear_status_t bitlinear_forward3(const int8_t* x_q, const float* gamma, int64_t M, int64_t K,
+                                      const uint32_t* w_packed3, int64_t N, float beta, float* y,
+                                      int32_t* acc, hipStream_t stream);
+
 /* Text of the last non-OK status on this thread ("" if none). */
 const char* bitlinear_last_error(void);
 

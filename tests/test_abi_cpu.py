@@ -21,7 +21,8 @@ def test_every_declared_symbol_is_exported():
         "bitlinear_forward_path", "bitlinear_silu_mul_quant", "bitlinear_ternarize",
         "bitlinear_binarize", "bitlinear_pack_weights1", "bitlinear_forward1",
         "bitlinear_quant_act_grouped", "bitlinear_forward_grouped", "bitlinear_ternarize_grouped",
-        "bitlinear_forward_grouped_one_launch", "bitlinear_last_error", "bitlinear_abi_version"}
+        "bitlinear_forward_grouped_one_launch", "bitlinear_pack_weights3", "bitlinear_forward3",
+        "bitlinear_last_error", "bitlinear_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -291,3 +292,33 @@ def test_grouped_one_launch_query():
     assert q(4, 512, 4, 1000) == 0        # runs of 128 inputs: not whole 256-chunks
     assert q(4, 4096, 1, 1000) == 0       # one group is the ungrouped product
     assert q(4, 3072, 3, 1000) == 0       # 3 groups: no K split divides into them
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((FAKE, 4, 24, FAKE, None), bl.ERR_SHAPE, "multiple of 16"),
+    ((None, 4, 32, FAKE, None), bl.ERR_NULL, "w is NULL"),
+    ((FAKE, 4, 32, None, None), bl.ERR_NULL, "w_packed3 is NULL"),
+    ((FAKE, 4, 32, FAKE + 4, None), bl.ERR_ALIGN, "w_packed3"),
+    ((FAKE, 4, 32, FAKE, FAKE + 2), bl.ERR_ALIGN, "bad_count"),
+    ((FAKE, -2, 32, FAKE, None), bl.ERR_SHAPE, "N=-2"),
+])
+def test_pack3_rejects(args, status, msg):
+    assert bl.lib.bitlinear_pack_weights3(*args, None) == status
+    assert msg in bl.last_error()
+
+
+def _f3(xq=FAKE, g=FAKE, M=1, K=160, w=FAKE, N=1, beta=1.0, y=FAKE, acc=None):
+    return bl.lib.bitlinear_forward3(xq, g, M, K, w, N, F(beta), y, acc, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(K=24), bl.ERR_SHAPE, "multiple of 16"),
+    (dict(w=FAKE + 8), bl.ERR_ALIGN, "w_packed3"),
+    (dict(xq=None), bl.ERR_NULL, "x_q is NULL"),
+    (dict(y=None), bl.ERR_NULL, "y is NULL"),
+    (dict(beta=float("nan")), bl.ERR_VALUE, "beta"),
+    (dict(acc=FAKE + 1), bl.ERR_ALIGN, "acc"),
+])
+def test_forward3_rejects(kw, status, msg):
+    assert _f3(**kw) == status
+    assert msg in bl.last_error()

@@ -668,3 +668,51 @@ def test_forward_grouped_without_acc(dev):
     y1, _ = bl.forward_grouped(q, g, wp, beta)
     y2 = bl.forward_grouped(q, g, wp, beta, want_acc=False)
     np.testing.assert_array_equal(host(y2), host(y1))
+
+
+# ------------------------------------------------------------------ base-3 weights
+
+@pytest.mark.parametrize("N,K", [(1, 16), (3, 96), (300, 4096), (64, 2560), (33, 6912), (7, 1040)])
+def test_pack3_parity(dev, N, K):
+    w = workloads.ternary(workloads.rng_for(980, N, K), N, K, workloads.TERNARY_UNIFORM)
+    packed3, bad = bl.pack_weights3(to_dev(w, dev))
+    p_ref, bad_ref = oracle.pack3(w)
+    assert bad_ref == 0
+    np.testing.assert_array_equal(host(packed3).view(np.uint8), p_ref)
+
+
+def test_pack3_counts_bad_entries(dev):
+    w = workloads.ternary(workloads.rng_for(980, 1), 5, 160, workloads.TERNARY_UNIFORM)
+    w[2, 17] = 2
+    w[4, 159] = -7
+    packed3, bad = bl.pack_weights3(to_dev(w, dev), check=False)
+    p_ref, bad_ref = oracle.pack3(w)
+    assert int(host(bad)[0]) == bad_ref == 2
+    np.testing.assert_array_equal(host(packed3).view(np.uint8), p_ref)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 1000), (4, 4096, 700), (16, 2560, 513), (3, 6912, 200),
+                                   (1, 16, 7), (5, 96, 33), (9, 1040, 100), (2, 8192, 300)])
+def test_forward3_parity(dev, M, K, N):
+    rng = workloads.rng_for(981, M, K, N)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, 3] *= 40.0
+    w = workloads.ternary(rng, N, K, workloads.TERNARY_HALF_ZERO)
+    q_ref, g_ref = oracle.quant_act(x)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, np.float32(0.021))
+    packed3, _ = bl.pack_weights3(to_dev(w, dev))
+    y, acc = bl.forward3(to_dev(q_ref, dev), to_dev(g_ref, dev), packed3, 0.021, want_acc=True)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    assert_y_close(host(y), y_ref)
+
+
+def test_forward3_matches_the_2bit_layout(dev):
+    rng = workloads.rng_for(982, 1)
+    M, K, N = 4, 4096, 2000
+    w = workloads.ternary(rng, N, K, workloads.TERNARY_UNIFORM)
+    q, g = bl.quant_act(to_dev(rng.standard_normal((M, K)).astype(np.float32), dev))
+    y2, acc2 = bl.forward(q, g, gpu_pack(w, dev), 0.03, want_acc=True)
+    packed3, _ = bl.pack_weights3(to_dev(w, dev))
+    y3, acc3 = bl.forward3(q, g, packed3, 0.03, want_acc=True)
+    np.testing.assert_array_equal(host(acc3), host(acc2))
+    np.testing.assert_array_equal(host(y3), host(y2))
