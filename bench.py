@@ -57,13 +57,16 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
-    ap.add_argument("--op", choices=("layer", "ternarize", "binary", "grouped"), default="layer",
+    ap.add_argument("--op", choices=("layer", "ternarize", "binary", "grouped", "base3"),
+                    default="layer",
                     help="layer: the BitLinear step (default); ternarize: absmean "
                          "ternarisation + packing of fp32 weights of the workload's shape; "
                          "binary: the step on 1-bit Sign(W - alpha) weights "
                          "(bitlinear_quant_act + bitlinear_forward1 per token count); "
                          "grouped: the step with --groups group scales along K "
-                         "(bitlinear_quant_act_grouped + bitlinear_forward_grouped)")
+                         "(bitlinear_quant_act_grouped + bitlinear_forward_grouped); "
+                         "base3: the step on 1.6-bit base-3 packed weights "
+                         "(bitlinear_quant_act + bitlinear_forward3)")
     ap.add_argument("--groups", type=int, default=4, help="group count of --op grouped")
     ap.add_argument("--traffic-probe", metavar="JSON",
                     help="launch every call of one step once, then a plain copy kernel of "
@@ -718,6 +721,119 @@ def bench_grouped(args, torch, bl, dev):
     print(json.dumps(line), flush=True)
 
 
+# ----------------------------------------------------------------------------- base-3 step
+
+def bench_base3(args, torch, bl, dev):
+    """The decode step of the workload on base-3 packed weights (1.6 bits per
+    weight): the workload's ternary weights packed by bitlinear_pack_weights3,
+    per token count bitlinear_quant_act + bitlinear_forward3; weights rotate
+    through >= 512 MB of copies; the timed steps are one graph replay."""
+    wl = workloads.WORKLOADS[args.workload]
+    N, K = wl.N, wl.K
+    beta = float(workloads.workload_beta(args.workload))
+    w = workloads.workload_weights(args.workload)
+    packed3, _ = bl.pack_weights3(torch.from_numpy(w).to(dev))
+    wbytes = packed3.numel() * 4
+    copies = [packed3] + [packed3.clone() for _ in range(max(1, math.ceil(ROTATE_BYTES / wbytes)) - 1)]
+    bufs = []
+    for M in [m for m in wl.ms if m <= 16]:
+        x = torch.from_numpy(workloads.workload_activations(args.workload, M)).to(dev)
+        bufs.append(dict(M=M, x=x, q=torch.empty((M, K), dtype=torch.int8, device=dev),
+                         g=torch.empty(M, device=dev), y=torch.empty((M, N), device=dev)))
+    lib = bl.lib
+
+    def stream():
+        return torch.cuda.current_stream(dev).cuda_stream
+
+    def ops(step, only=None):
+        wp = copies[step % len(copies)].data_ptr()
+        for b in bufs:
+            M = b["M"]
+            if only in (None, f"quant_act_M{M}"):
+                assert lib.bitlinear_quant_act(b["x"].data_ptr(), bl.F32, M, K, None, 0.0,
+                                               b["q"].data_ptr(), b["g"].data_ptr(), stream()) == 0
+            if only in (None, f"forward3_M{M}"):
+                assert lib.bitlinear_forward3(b["q"].data_ptr(), b["g"].data_ptr(), M, K, wp, N, beta,
+                                              b["y"].data_ptr(), None, stream()) == 0
+
+    s = torch.cuda.Stream(device=dev)
+
+    def graph(first, count, only=None):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(first, first + count):
+                ops(i, only)
+        return g
+
+    def time_graph(g, per_replay):
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / per_replay
+
+    ops(0)
+    torch.cuda.synchronize()
+    graph(0, args.warmup).replay()
+    us_step = time_graph(graph(args.warmup, args.steps), args.steps)
+    per_call = {}
+    for b in bufs:
+        M = b["M"]
+        for name in (f"quant_act_M{M}", f"forward3_M{M}"):
+            per_call[name] = dict(avg_us=round(time_graph(graph(0, len(copies), name), len(copies)), 3))
+        alg = wbytes + M * K + 4 * M + 4 * M * N
+        per_call[f"forward3_M{M}"].update(alg_bytes=alg, packed_w_GBs=round(
+            wbytes / (per_call[f"forward3_M{M}"]["avg_us"] * 1e-6) / 1e9, 1))
+    dom = max((k for k in per_call if k.startswith("forward")), key=lambda k: per_call[k]["avg_us"])
+    d = per_call[dom]
+    gbs = d["alg_bytes"] / (d["avg_us"] * 1e-6) / 1e9
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        xs = [workloads.workload_activations(args.workload, b["M"]) for b in bufs]
+        est = sum(b["M"] for b in bufs) * w.size * 1.5e-9
+        rows = N
+        if est / max(oracle.num_threads(), 1) > args.cpu_seconds:
+            rows = max(64, int(N * args.cpu_seconds * oracle.num_threads() / est / 3))
+        p3, _ = oracle.pack3(np.ascontiguousarray(w[:rows]))
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            wr = oracle.unpack3(p3, K)  # the oracle reads the packed bytes each step
+            for x in xs:
+                q, g = oracle.quant_act(x)
+                oracle.forward(q, g, wr, beta)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_seconds or el / n * (n + 1) > 3 * args.cpu_seconds:
+                break
+        cpu = dict(value=round(p3.size * len(xs) * n / el / 1e9, 4), unit="packed-W GB/s",
+                   cores=oracle.num_threads(), kind="oracle",
+                   sample=f"{n} x (unpack + decode steps over {rows} of {N} output rows), "
+                          f"M={[b['M'] for b in bufs]}, {el:.1f} s")
+    line = {
+        "metric": "BitLinear on 1.6-bit base-3 weights: packed-W GB/s",
+        "value": round(wbytes * len(bufs) / (us_step * 1e-6) / 1e9, 2),
+        "unit": "packed-W GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_step * 1e-3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"base3_{wl.name}", "M": [b["M"] for b in bufs], "K": K, "N": N,
+                   "weight_bytes": wbytes, "weight_copies": len(copies),
+                   "timing": "hip_graph_of_all_timed_steps"},
+        "roofline": dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                         frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, call=dom,
+                         kernel="gemv3_kernel", avg_launch_us=d["avg_us"],
+                         alg_bytes_per_launch=d["alg_bytes"]),
+        "cpu_baseline": cpu,
+        "per_call": per_call,
+    }
+    print(json.dumps(line), flush=True)
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -746,6 +862,9 @@ def main():
         return
     if args.op == "grouped":
         bench_grouped(args, torch, bl, dev)
+        return
+    if args.op == "base3":
+        bench_base3(args, torch, bl, dev)
         return
     if args.traffic_probe:
         args.no_rotate = True
