@@ -80,9 +80,10 @@ def parse():
 
 def forward_kernel(M: int, K: int) -> str:
     """Kernel that bitlinear_forward picks for M (the library's dispatch)."""
-    if M <= 2:
+    if M == 1:
         return "gemv_valu_kernel"
-    if 5 <= M <= 16 and K % 256 == 0 and ((M * K + 1023) // 1024) * 1024 + 16384 <= 160 * 1024:
+    lds_fits = K % 256 == 0 and ((M * K + 1023) // 1024) * 1024 + 16384 + 128 <= 160 * 1024
+    if (5 <= M <= 16 or (2 <= M <= 4 and K >= 6144)) and lds_fits:
         return "decode_lds_kernel"
     if M <= 32:
         return "skinny_mfma_kernel"

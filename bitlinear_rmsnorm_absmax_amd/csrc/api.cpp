@@ -71,7 +71,7 @@ hipError_t launch_forward_kernel(const int8_t* x_q, const float* gamma, int64_t 
                                  const uint32_t* w_packed, int64_t N, float beta, float* y,
                                  int32_t* acc, int path, hipStream_t stream) {
     if (path == BITLINEAR_PATH_AUTO)
-        path = (M <= 2) ? BITLINEAR_PATH_GEMV : (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
+        path = (M == 1) ? BITLINEAR_PATH_GEMV : (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
     const int m = (int)M, n = (int)N, k = (int)K;
     switch (path) {
         case BITLINEAR_PATH_GEMV:

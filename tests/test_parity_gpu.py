@@ -191,7 +191,8 @@ def test_forward_parity(dev, path, M, N, K):
 # >= 320, >= 640, >= 1280 tiles), ragged N, the largest K whose activation
 # block fits in LDS at 16 tokens (9216), and a zero token.
 DECODE_LDS_CASES = [(5, 1000, 256), (7, 5200, 512), (12, 10300, 1024), (16, 20500, 768),
-                    (16, 333, 9216), (9, 2570, 2560), (13, 40, 4096), (6, 17, 256)]
+                    (16, 333, 9216), (9, 2570, 2560), (13, 40, 4096), (6, 17, 256),
+                    (2, 3000, 8192), (3, 700, 6912), (4, 129, 6144)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_LDS_CASES)
