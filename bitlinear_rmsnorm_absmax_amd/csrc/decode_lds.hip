@@ -152,13 +152,20 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 
     // 1. activation copies of the whole workgroup, queued ahead of any weight load
     {
+        // row = pos / WR and group = k / KG by multiply-high with a reciprocal
+        // taken once: floor(x / d) = umulhi(x, floor((2^32 - 1) / d) + 1),
+        // exact for x * d < 2^32 (here pos * WR < 2^30 and (k/256) * (KG/256)
+        // < 2^18); the reciprocal of d = 1 does not fit 32 bits, so a group
+        // of 256 inputs takes k >> 8 directly
         const int pieces = M * WR;
         const int ninstr = (pieces + 63) >> 6;
+        const uint32_t wr_inv = 0xFFFFFFFFu / (uint32_t)WR + 1u;  // WR >= 16
+        const uint32_t kg_inv = (G > 1 && KG > 256) ? 0xFFFFFFFFu / (uint32_t)(KG >> 8) + 1u : 0u;
         for (int q = wv; q < ninstr; q += kDecWaves) {
             const int pos = min(q * 64 + lane, pieces - 1);
-            const int r = pos / WR, slot = pos - r * WR;
+            const int r = (int)__umulhi((uint32_t)pos, wr_inv), slot = pos - r * WR;
             const int k = 16 * (slot ^ (r & 15));  // input index of the piece
-            const int kg = k / KG;                 // its group
+            const int kg = G == 1 ? 0 : KG == 256 ? (k >> 8) : (int)__umulhi((uint32_t)(k >> 8), kg_inv);
             copy16_to_lds(xq + ((int64_t)kg * M + r) * KG + (k - kg * KG), As + 1024 * q);
         }
     }
