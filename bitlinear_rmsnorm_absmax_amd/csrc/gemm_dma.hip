@@ -32,6 +32,7 @@ namespace bl {
 namespace {
 
 constexpr int BK = 128;
+
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -70,19 +71,27 @@ struct DCfg {
     static_assert(kBBytes % (1024 * kWaves) == 0, "weight copies divide the waves");
 };
 
-template <int WM, int WN, int TM, int TN, int STAGES>
-__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// KSP > 1 splits K inside the workgroup: KSP groups of WM x WN waves, each
+// with its own LDS ring, run the same loop (so every wave meets the same
+// barriers) over their own K / KSP inputs; the groups' accumulators are added
+// through LDS before the epilogue.  For few tiles on a long K: the sequential
+// K steps of a tile drop by KSP and the compute unit holds KSP times the waves.
+template <int WM, int WN, int TM, int TN, int STAGES, int KSP>
+__global__ __launch_bounds__(KSP * WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M,
                      int K, const uint32_t* __restrict__ wp, int N, float beta,
                      float* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
                      int tiles_total) {
     using C = DCfg<WM, WN, TM, TN, STAGES>;
-    __shared__ __attribute__((aligned(16))) char lds[STAGES * C::kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds[KSP * STAGES * C::kStageBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wv_all = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int kgrp = wv_all / C::kWaves;   // K group
+    const int wv = wv_all % C::kWaves;     // wave within its group
     const int wm = wv / WN, wn = wv % WN;
+    char* ring = lds + kgrp * STAGES * C::kStageBytes;
     const int l32 = lane & 31, h = lane >> 5;
 
     int b = blockIdx.x;
@@ -91,13 +100,13 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     const int m0 = (b / tiles_n) * C::BM;
     const int n0 = (b % tiles_n) * C::BN;
     const int WR = K >> 4;
-    const int KT = K / BK;
+    const int KT = K / BK / KSP;  // K steps of each group (K % (BK * KSP) == 0)
 
     // per-lane source offsets of this wave's copies at step 0 (32-bit, from
     // the block's first row / column); rows and columns past the matrix are
     // clamped onto its last row / column (their products are never stored)
-    const int8_t* abase = xq + (int64_t)m0 * K;
-    const uint32_t* bbase = wp + (int64_t)n0 * WR;
+    const int8_t* abase = xq + (int64_t)m0 * K + (int64_t)kgrp * KT * BK;
+    const uint32_t* bbase = wp + (int64_t)n0 * WR + (int64_t)kgrp * KT * (BK / 16);
     uint32_t aoff[C::kAInstr];
 #pragma unroll
     for (int i = 0; i < C::kAInstr; ++i) {
@@ -116,7 +125,7 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     }
 
     auto issue = [&](int kt, int buf) {
-        char* stage = lds + buf * C::kStageBytes;
+        char* stage = ring + buf * C::kStageBytes;
         const int8_t* a_step = abase + (int64_t)kt * BK;
         const uint32_t* b_step = bbase + (int64_t)kt * (BK / 16);
 #pragma unroll
@@ -145,7 +154,7 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
         __builtin_amdgcn_s_barrier();
         issue(min(kt + STAGES - 1, KT - 1), (kt + STAGES - 1) % STAGES);
 
-        const char* stage = lds + (kt % STAGES) * C::kStageBytes;
+        const char* stage = ring + (kt % STAGES) * C::kStageBytes;
         const v4i* As = reinterpret_cast<const v4i*>(stage);
         const v4u* Bs = reinterpret_cast<const v4u*>(stage + C::kABytes);
         // all LDS operand reads of the step first, so their latency overlaps
@@ -183,30 +192,64 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __syncthreads();
 
-    int* Sp = reinterpret_cast<int*>(lds);  // [WN][BM] partial row sums
-    int* S = Sp + WN * C::BM;                // [BM]
+    // KSP > 1: the accumulators of groups 1.. go through LDS (lane-major, one
+    // int per lane and register) to group 0, whose waves own the epilogue
+    constexpr int kAccInts = C::kWaves * TM * TN * 16 * kWave;  // one group's accumulators
+    int* red = reinterpret_cast<int*>(lds);
+    int* Sp = reinterpret_cast<int*>(lds) + (KSP > 1 ? kAccInts : 0);  // [KSP*WN][BM] partial row sums
+    int* S = Sp + KSP * WN * C::BM;          // [BM]
     float* Ssc = reinterpret_cast<float*>(S + C::BM);
+    static_assert(KSP == 1 || (int64_t)(kAccInts + (KSP * WN + 2) * C::BM) * 4 <=
+                                  (int64_t)KSP * STAGES * C::kStageBytes,
+                  "the accumulator exchange fits the rings");
+    if constexpr (KSP > 1) {
+        for (int g = 1; g < KSP; ++g) {
+            if (kgrp == g) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            red[((wv * TM * TN + i * TN + t) * 16 + v) * kWave + lane] = acc[i][t][v];
+            }
+            __syncthreads();
+            if (kgrp == 0) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v)
+                            acc[i][t][v] += red[((wv * TM * TN + i * TN + t) * 16 + v) * kWave + lane];
+            }
+            __syncthreads();
+        }
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int sv = s_part[i] + __shfl_xor(s_part[i], 32, kWave);
-        if (h == 0) Sp[wn * C::BM + wm * TM * 32 + 32 * i + l32] = sv;
+        if (h == 0) Sp[(kgrp * WN + wn) * C::BM + wm * TM * 32 + 32 * i + l32] = sv;
     }
     __syncthreads();
-    epilogue_tables(Sp, WN, C::BM, m0, M, gamma, beta, S, Ssc, tid, C::kThreads);
+    epilogue_tables(Sp, KSP * WN, C::BM, m0, M, gamma, beta, S, Ssc, tid, KSP * C::kThreads);
     __syncthreads();
-    store_tiles<TM, TN>(acc, S, Ssc, wm * TM * 32, wn * TN * 32, m0, n0, M, N, y, acc_out, lane);
+    if (kgrp == 0)
+        store_tiles<TM, TN>(acc, S, Ssc, wm * TM * 32, wn * TN * 32, m0, n0, M, N, y, acc_out, lane);
 }
 
-template <int WM, int WN, int TM, int TN, int STAGES>
+template <int WM, int WN, int TM, int TN, int STAGES, int KSP = 1>
 hipError_t launch_dcfg(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
                        int N, float beta, float* y, int32_t* acc, hipStream_t s) {
     using C = DCfg<WM, WN, TM, TN, STAGES>;
+    if (K % (BK * KSP) != 0) return hipErrorInvalidValue;
     const int tm = (M + C::BM - 1) / C::BM;
     const int tn = (N + C::BN - 1) / C::BN;
     const int64_t total = (int64_t)tm * tn;
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-    gemm_dma_kernel<WM, WN, TM, TN, STAGES><<<dim3((unsigned)total), dim3(C::kThreads), 0, s>>>(
-        xq, gamma, M, K, wp, N, beta, y, acc, tn, (int)total);
+    gemm_dma_kernel<WM, WN, TM, TN, STAGES, KSP>
+        <<<dim3((unsigned)total), dim3(KSP * C::kThreads), 0, s>>>(xq, gamma, M, K, wp, N, beta, y,
+                                                                   acc, tn, (int)total);
     return hipGetLastError();
 }
 
@@ -225,6 +268,15 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
     const int64_t wide_tiles = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
     if (M >= 256 && wide_tiles >= 256)
         return launch_dcfg<2, 2, 2, 4, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    // fewer 128 x 128 tiles than CUs on a K of whole 256-steps: two K groups
+    // per workgroup (8 waves, 120 KB of LDS, one workgroup per CU).  Measured:
+    // M = 512, K = 6912, N = 2560 36 -> 33 us; M = 64, K = 8192, N = 28672
+    // 45 -> 43 us.  Per-wave timestamps show the K step then takes about twice
+    // as long: the compute unit's copy stream, not the step latency, bounds
+    // these shapes.
+    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles < 256 && K % (2 * BK) == 0)
+        return launch_dcfg<2, 2, 2, 2, 3, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     return launch_dcfg<2, 2, 2, 2, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
 
