@@ -717,3 +717,71 @@ def test_forward3_matches_the_2bit_layout(dev):
     y3, acc3 = bl.forward3(q, g, packed3, 0.03, want_acc=True)
     np.testing.assert_array_equal(host(acc3), host(acc2))
     np.testing.assert_array_equal(host(y3), host(y2))
+
+
+# ------------------------------------------------------------------ edge cases of the widened rows
+
+def test_grouped_rms_bf16_chain(dev):
+    # bf16 activations with RMSNorm through the grouped quantiser, then the
+    # grouped product (G-launch path: M = 33 > 16)
+    rng = workloads.rng_for(990, 1)
+    M, K, G, N = 33, 2048, 4, 700
+    bits = workloads.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    gain = (rng.random(K) + 0.5).astype(np.float32)
+    w = workloads.ternary(rng, N, K, workloads.TERNARY_UNIFORM)
+    beta = rng.uniform(0.01, 0.05, G).astype(np.float32)
+    q, g = bl.quant_act_grouped(to_dev(bits, dev, torch.bfloat16), G, to_dev(gain, dev), 1e-6)
+    q_ref, g_ref = oracle.quant_act_grouped(oracle.bf16_to_f32(bits), G, gain, 1e-6)
+    np.testing.assert_array_equal(host(q), q_ref)
+    assert_y_close(host(g), g_ref)
+    y, acc = bl.forward_grouped(q, g, pack_grouped(w, G, dev), to_dev(beta, dev))
+    # the product is checked against the oracle on the GPU's own gamma (its
+    # RMSNorm gamma may differ from the oracle's within the 1e-6 tolerance)
+    y_ref, acc_ref = oracle.forward_grouped(q_ref, host(g), w, beta)
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    err = np.abs(host(y).astype(np.float64) - y_ref.astype(np.float64))
+    assert (err <= grouped_bound(acc_ref, beta, host(g))).all()
+
+
+def test_grouped_longest_k_one_launch(dev):
+    rng = workloads.rng_for(990, 2)
+    M, K, G, N = 1, 131072, 8, 96
+    assert bl.lib.bitlinear_forward_grouped_one_launch(M, K, G, N) == 1
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    w = workloads.ternary(rng, N, K, workloads.TERNARY_HALF_ZERO)
+    beta = rng.uniform(0.01, 0.05, G).astype(np.float32)
+    q_ref, g_ref = oracle.quant_act_grouped(x, G)
+    y_ref, acc_ref = oracle.forward_grouped(q_ref, g_ref, w, beta)
+    y, acc = bl.forward_grouped(to_dev(q_ref, dev), to_dev(g_ref, dev), pack_grouped(w, G, dev),
+                                to_dev(beta, dev))
+    np.testing.assert_array_equal(host(acc), acc_ref)
+    err = np.abs(host(y).astype(np.float64) - y_ref.astype(np.float64))
+    assert (err <= grouped_bound(acc_ref, beta, g_ref)).all()
+
+
+def test_forward_grouped_empty(dev):
+    q = torch.zeros((4, 0, 64), dtype=torch.int8, device=dev)
+    g = torch.zeros((4, 0), dtype=torch.float32, device=dev)
+    wp = torch.zeros((4, 5, 4), dtype=torch.int32, device=dev)
+    y, acc = bl.forward_grouped(q, g, wp, torch.ones(4, device=dev))
+    assert y.shape == (0, 5) and acc.shape == (4, 0, 5)
+
+
+def test_base3_longest_k_and_single_row(dev):
+    rng = workloads.rng_for(990, 3)
+    for M, K, N in ((3, 131072, 5), (1, 4096, 1)):
+        x = rng.standard_normal((M, K)).astype(np.float32)
+        w = workloads.ternary(rng, N, K, workloads.TERNARY_UNIFORM)
+        q_ref, g_ref = oracle.quant_act(x)
+        y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, np.float32(0.02))
+        packed3, _ = bl.pack_weights3(to_dev(w, dev))
+        np.testing.assert_array_equal(host(packed3).view(np.uint8), oracle.pack3(w)[0])
+        y, acc = bl.forward3(to_dev(q_ref, dev), to_dev(g_ref, dev), packed3, 0.02, want_acc=True)
+        np.testing.assert_array_equal(host(acc), acc_ref)
+        assert_y_close(host(y), y_ref)
+
+
+def test_base3_empty(dev):
+    y = bl.forward3(torch.zeros((0, 160), dtype=torch.int8, device=dev),
+                    torch.zeros(0, device=dev), torch.zeros((3, 8), dtype=torch.int32, device=dev), 0.5)
+    assert y.shape == (0, 3)
