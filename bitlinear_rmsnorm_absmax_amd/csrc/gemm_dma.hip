@@ -238,6 +238,204 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
         store_tiles<TM, TN>(acc, S, Ssc, wm * TM * 32, wn * TN * 32, m0, n0, M, N, y, acc_out, lane);
 }
 
+
+// Biased byte sum of 16 int8 values: sum (q + 128) + acc.  v_sad_u8 against 0
+// adds the four unsigned bytes; flipping the sign bit first maps q to q + 128.
+// It runs on the vector ALU (v_dot4 would share the matrix pipe with the MFMAs).
+__device__ __forceinline__ unsigned biased_sum16(v4i a, unsigned acc) {
+    acc = __builtin_amdgcn_sad_u8((unsigned)a.x ^ 0x80808080u, 0u, acc);
+    acc = __builtin_amdgcn_sad_u8((unsigned)a.y ^ 0x80808080u, 0u, acc);
+    acc = __builtin_amdgcn_sad_u8((unsigned)a.z ^ 0x80808080u, 0u, acc);
+    acc = __builtin_amdgcn_sad_u8((unsigned)a.w ^ 0x80808080u, 0u, acc);
+    return acc;
+}
+
+// Software-pipelined variant of the ring loop above (same LDS layout, copies
+// and three-stage ring):
+//   - the A fragments of the next 32-wide K slice are read while the MFMAs of
+//     the current one run, and the packed weight words of the next K step are
+//     read right after the step's barrier, which sits between the two halves of
+//     the last slice's MFMAs, so the barrier and the first reads of a step
+//     overlap MFMA work;
+//   - wave wn takes the four K slices of a step in the order wn, wn + 1, ...
+//     (mod 4), so its share of the row sums (the slices kk with kk % WN == wn)
+//     falls on fixed unrolled positions and the loop has no branch on it; the
+//     weight words are then read one 32-bit word per slice;
+//   - the row sums use biased_sum16, the bias is removed once at the end.
+// Measured with a 1 x 4 wave layout (each wave 128 rows x 64 columns, so each
+// packed word is unpacked once per workgroup): M = 512, K = 8192, N = 28672
+// 125 -> 112 us; M = 2048, K = 4096, N = 11008 unchanged (about 103 us).
+template <int WM, int WN, int TM, int TN>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pipe_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M,
+                      int K, const uint32_t* __restrict__ wp, int N, float beta,
+                      float* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
+                      int tiles_total) {
+    constexpr int STAGES = 3;
+    using C = DCfg<WM, WN, TM, TN, STAGES>;
+    static_assert(4 % WN == 0, "the K slices of a step divide between the waves of a row");
+    __shared__ __attribute__((aligned(16))) char lds[STAGES * C::kStageBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wv / WN, wn = wv % WN;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    int b = blockIdx.x;
+    const int full = (tiles_total / kXcds) * kXcds;
+    if (b < full) b = (b % kXcds) * (full / kXcds) + b / kXcds;
+    const int m0 = (b / tiles_n) * C::BM;
+    const int n0 = (b % tiles_n) * C::BN;
+    const int WR = K >> 4;
+    const int KT = K / BK;
+
+    // per-lane source offsets as in gemm_dma_kernel (rows / columns past the
+    // matrix clamped onto its last row / column)
+    const int8_t* abase = xq + (int64_t)m0 * K;
+    const uint32_t* bbase = wp + (int64_t)n0 * WR;
+    uint32_t aoff[C::kAInstr];
+#pragma unroll
+    for (int i = 0; i < C::kAInstr; ++i) {
+        const int q = wv * C::kAInstr + i;
+        const int row = 8 * q + lane / 8;
+        const int lchunk = (lane % 8) ^ swz(row);
+        aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + 16u * lchunk;
+    }
+    uint32_t boff[C::kBInstr];
+#pragma unroll
+    for (int i = 0; i < C::kBInstr; ++i) {
+        const int q = wv * C::kBInstr + i;
+        const int col = 32 * q + lane / 2;
+        const int lhalf = (lane % 2) ^ ((col >> 3) & 1);
+        boff[i] = (uint32_t)(min(n0 + col, N - 1) - n0) * (uint32_t)WR + 4u * lhalf;
+    }
+    auto issue = [&](int kt, int buf) {
+        char* stage = lds + buf * C::kStageBytes;
+        const int8_t* a_step = abase + (int64_t)kt * BK;
+        const uint32_t* b_step = bbase + (int64_t)kt * (BK / 16);
+#pragma unroll
+        for (int i = 0; i < C::kAInstr; ++i)
+            copy16_to_lds(a_step + aoff[i], stage + 1024 * (wv * C::kAInstr + i));
+#pragma unroll
+        for (int i = 0; i < C::kBInstr; ++i)
+            copy16_to_lds(b_step + boff[i], stage + C::kABytes + 1024 * (wv * C::kBInstr + i));
+    };
+    // packed words of K slice (kk + wn) % 4 for this lane's columns
+    auto read_words = [&](int buf, uint32_t (&wq)[TN][4]) {
+        const uint32_t* Bs = reinterpret_cast<const uint32_t*>(lds + buf * C::kStageBytes + C::kABytes);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+            const int col = wn * TN * 32 + 32 * t + l32;
+            const uint32_t* p = Bs + (col * 2 + bswz(col, h)) * 4;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) wq[t][kk] = p[(kk + wn) & 3];
+        }
+    };
+    auto read_frags = [&](int buf, int kk, v4i (&af)[TM]) {
+        const v4i* As = reinterpret_cast<const v4i*>(lds + buf * C::kStageBytes);
+        const int ke = (kk + wn) & 3;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * TM * 32 + 32 * i + l32;
+            af[i] = As[r * 8 + ((4 * h + ke) ^ swz(r))];
+        }
+    };
+
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int t = 0; t < TN; ++t) acc[i][t] = v16i{};
+    unsigned s_biased[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) s_biased[i] = 0u;
+
+    // steps 0 and 1 in flight; step 0 landed everywhere; step 2 queued
+    issue(0, 0);
+    issue(min(1, KT - 1), 1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kPerStep, 0));
+    __builtin_amdgcn_s_barrier();
+    issue(min(2, KT - 1), 2);
+    uint32_t wq[TN][4], wqn[TN][4];
+    v4i a[2][TM];
+    read_words(0, wq);
+    read_frags(0, 0, a[0]);
+
+    int buf = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+        const bool more = kt + 1 < KT;  // uniform
+        const int nbuf = buf == STAGES - 1 ? 0 : buf + 1;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            if (kk < 3) read_frags(buf, kk + 1, a[(kk + 1) & 1]);
+            v4i bf[TN];
+#pragma unroll
+            for (int t = 0; t < TN; ++t) bf[t] = unpack_codes(wq[t][kk]);
+            if (kk % WN == 0) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i) s_biased[i] = biased_sum16(a[kk & 1][i], s_biased[i]);
+            }
+            if (kk < 3) {
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+                        acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[kk & 1][i], bf[t], acc[i][t], 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int i = 0; i < TM / 2; ++i)
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+                        acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1][i], bf[t], acc[i][t], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (more) {
+                    // this wave's copies of step kt+1 have landed and its reads
+                    // of this buffer are done; after the barrier every wave's
+                    // are, so step kt+1 can be read and this buffer refilled
+                    // (with step kt+3, or the last step again past the end)
+                    __builtin_amdgcn_s_waitcnt(waitcnt_imm(C::kPerStep, 0));
+                    __builtin_amdgcn_s_barrier();
+                    issue(min(kt + 3, KT - 1), buf);
+                    read_words(nbuf, wqn);
+                    read_frags(nbuf, 0, a[0]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = TM / 2; i < TM; ++i)
+#pragma unroll
+                    for (int t = 0; t < TN; ++t)
+                        acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1][i], bf[t], acc[i][t], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) wq[t][kk] = wqn[t][kk];
+        buf = nbuf;
+    }
+    // every copy (including the re-reads past the end) has landed before the
+    // LDS is reused below or released
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __syncthreads();
+
+    int* Sp = reinterpret_cast<int*>(lds);  // [WN][BM] partial row sums
+    int* S = Sp + WN * C::BM;               // [BM]
+    float* Ssc = reinterpret_cast<float*>(S + C::BM);
+    // each lane summed 16 bytes for 4 / WN slices of each of the KT steps
+    const unsigned bias = 2048u * (unsigned)KT * (unsigned)(4 / WN);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int sp = (int)(s_biased[i] - bias);
+        const int sv = sp + __shfl_xor(sp, 32, kWave);
+        if (h == 0) Sp[wn * C::BM + wm * TM * 32 + 32 * i + l32] = sv;
+    }
+    __syncthreads();
+    epilogue_tables(Sp, WN, C::BM, m0, M, gamma, beta, S, Ssc, tid, C::kThreads);
+    __syncthreads();
+    store_tiles<TM, TN>(acc, S, Ssc, wm * TM * 32, wn * TN * 32, m0, n0, M, N, y, acc_out, lane);
+}
+
 template <int WM, int WN, int TM, int TN, int STAGES, int KSP = 1>
 hipError_t launch_dcfg(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
                        int N, float beta, float* y, int32_t* acc, hipStream_t s) {
@@ -253,6 +451,21 @@ hipError_t launch_dcfg(const int8_t* xq, const float* gamma, int M, int K, const
     return hipGetLastError();
 }
 
+
+template <int WM, int WN, int TM, int TN>
+hipError_t launch_pipe(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
+                       int N, float beta, float* y, int32_t* acc, hipStream_t s) {
+    using C = DCfg<WM, WN, TM, TN, 3>;
+    if (K % BK != 0) return hipErrorInvalidValue;
+    const int tm = (M + C::BM - 1) / C::BM;
+    const int tn = (N + C::BN - 1) / C::BN;
+    const int64_t total = (int64_t)tm * tn;
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    gemm_pipe_kernel<WM, WN, TM, TN><<<dim3((unsigned)total), dim3(C::kThreads), 0, s>>>(
+        xq, gamma, M, K, wp, N, beta, y, acc, tn, (int)total);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemm_dma_supports(int M, int K, int N) { return K % BK == 0 && K > 0 && M > 0 && N > 0; }
@@ -261,13 +474,14 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
                            const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                            hipStream_t s) {
     // 128 x 256 tiles with a 3-stage ring (72 KB of LDS, two workgroups per
-    // CU) once there is at least one such tile per CU; else 128 x 128 tiles
-    // for more workgroups.  Measured on the M = 512 .. 2048 prefill shapes:
-    // the third stage gains 7-10 % over two, and at M = 512, N = 28672 the
-    // wide tiles win even with fewer tiles than workgroup slots.
+    // CU) once there is at least one such tile per CU, on the pipelined loop
+    // with four waves side by side; else 128 x 128 tiles for more workgroups.
+    // Measured on the M = 512 .. 2048 prefill shapes: the third stage gains
+    // 7-10 % over two, and at M = 512, N = 28672 the wide tiles win even with
+    // fewer tiles than workgroup slots.
     const int64_t wide_tiles = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
     if (M >= 256 && wide_tiles >= 256)
-        return launch_dcfg<2, 2, 2, 4, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return launch_pipe<1, 4, 4, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     // fewer 128 x 128 tiles than CUs on a K of whole 256-steps: two K groups
     // per workgroup (8 waves, 120 KB of LDS, one workgroup per CU).  Measured:
     // M = 512, K = 6912, N = 2560 36 -> 33 us; M = 64, K = 8192, N = 28672

@@ -186,6 +186,26 @@ def test_forward_parity(dev, path, M, N, K):
     assert_y_close(y, y_ref)
 
 
+# The GEMM takes 128 x 256 tiles on its pipelined ring loop once M >= 256 and
+# there are at least 256 such tiles: ragged M and N, and 1, 2, 3 and 5 K steps
+# of 128 (the prologue's re-reads past the end, and an odd ring rotation).
+WIDE_GEMM_CASES = [(257, 22053, 128), (256, 32769, 256), (300, 22016, 384), (384, 22016, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", WIDE_GEMM_CASES)
+def test_gemm_wide_tiles_parity(dev, M, N, K):
+    assert -(-M // 128) * -(-N // 256) >= 256
+    x, w, beta = workloads.random_case(900 + M + K, M, N, K, table=workloads.TERNARY_UNIFORM)
+    x = x.copy()
+    x[M - 2] = 0.0  # zero token in the last row tile
+    q, g, y, acc = run_forward(x, w, beta, dev, bl.PATH_GEMM)
+    q_ref, g_ref = oracle.quant_act(x)
+    np.testing.assert_array_equal(q, q_ref)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, beta)
+    np.testing.assert_array_equal(acc, acc_ref)
+    assert_y_close(y, y_ref)
+
+
 # The skinny path sends 5..16 tokens with K % 256 == 0 to the LDS-staged decode
 # kernel.  Cases cover its four workgroup widths (column tiles of 16: < 320,
 # >= 320, >= 640, >= 1280 tiles), ragged N, the largest K whose activation
