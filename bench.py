@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=2, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-rotate", action="store_true", help="one weight copy (warm cache)")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graphs")
+    ap.add_argument("--unfused", action="store_true",
+                    help="one-token steps as bitlinear_quant_act + bitlinear_forward instead of "
+                         "the fused bitlinear_quant_forward")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--op", choices=("layer", "ternarize", "binary", "grouped", "base3"),
@@ -99,13 +102,14 @@ class RunAll:
         self.calls = {}
         self.info = {}
 
-    def __call__(self, name, M=0, N=0, K=0, wbytes=0):
+    def __call__(self, name, M=0, N=0, K=0, wbytes=0, xbytes=0, kernel=None):
         self.calls[name] = self.calls.get(name, 0) + 1
         if wbytes:
             # algorithmic bytes of one forward launch: packed W + x_q + gamma + y
-            self.info[name] = dict(alg_bytes=wbytes + M * K + 4 * M + 4 * M * N,
+            # (+ the unquantised activations read by a fused call)
+            self.info[name] = dict(alg_bytes=wbytes + M * K + 4 * M + 4 * M * N + xbytes,
                                    ops=2 * M * N * K, wbytes=wbytes, M=M, N=N, K=K,
-                                   kernel=forward_kernel(M, K))
+                                   kernel=kernel or forward_kernel(M, K))
         return True
 
 
@@ -163,6 +167,11 @@ def build_plan(args, torch, bl, dev):
         if st != 0:
             raise RuntimeError(bl.last_error())
 
+    def fused(M, K, N):
+        # bitlinear_quant_forward runs as one kernel for one token, K % 64 == 0,
+        # K <= 16384, N <= 16384 (--unfused times the two calls instead)
+        return not args.unfused and M == 1 and K % 64 == 0 and K <= 16384 and N <= 16384
+
     meta = {"workload": wl.name, "K": wl.K, "N": wl.N, "M": list(wl.ms)}
     if wl.glu_f:
         wg, wu, wd = workloads.glu_weights(wid)
@@ -185,11 +194,23 @@ def build_plan(args, torch, bl, dev):
             c = step % ncopy
             for b in bufs:
                 M = b["M"]
-                if run(f"quant_act_rms_M{M}"):
+                projs = (("gate", layers[0], b["yg"]), ("up", layers[1], b["yu"]))
+                if fused(M, D, Fh):
+                    # RMSNorm + quantisation fused with the gate projection; the
+                    # up projection reuses its x_q and gamma
+                    L = layers[0]
+                    if run(f"quant_forward_rms_gate_M{M}", M, L.N, L.K, L.wbytes, 4 * M * D + 4 * D,
+                           "quant_gemv_kernel"):
+                        check(lib.bitlinear_quant_forward(
+                            b["x"].data_ptr(), bl.F32, M, D, gain.data_ptr(), wl.rms_eps,
+                            L.copies[c].data_ptr(), Fh, L.beta, b["q"].data_ptr(), b["g"].data_ptr(),
+                            b["yg"].data_ptr(), None, stream()))
+                    projs = projs[1:]
+                elif run(f"quant_act_rms_M{M}"):
                     check(lib.bitlinear_quant_act(b["x"].data_ptr(), bl.F32, M, D, gain.data_ptr(),
                                                   wl.rms_eps, b["q"].data_ptr(), b["g"].data_ptr(),
                                                   stream()))
-                for nm, L, out in (("gate", layers[0], b["yg"]), ("up", layers[1], b["yu"])):
+                for nm, L, out in projs:
                     if run(f"forward_{nm}_M{M}", M, L.N, L.K, L.wbytes):
                         check(lib.bitlinear_forward(b["q"].data_ptr(), b["g"].data_ptr(), M, D,
                                                     L.copies[c].data_ptr(), Fh, L.beta,
@@ -226,6 +247,14 @@ def build_plan(args, torch, bl, dev):
         wptr = L.copies[step % len(L.copies)].data_ptr()
         for b in bufs:
             M = b["M"]
+            if fused(M, K, N):
+                xb = M * K * (2 if b["dt"] == bl.BF16 else 4)
+                if run(f"quant_forward_M{M}", M, N, K, L.wbytes, xb, "quant_gemv_kernel"):
+                    check(lib.bitlinear_quant_forward(b["x"].data_ptr(), b["dt"], M, K, None, 0.0,
+                                                      wptr, N, L.beta, b["q"].data_ptr(),
+                                                      b["g"].data_ptr(), b["y"].data_ptr(), None,
+                                                      stream()))
+                continue
             if run(f"quant_act_M{M}"):
                 check(lib.bitlinear_quant_act(b["x"].data_ptr(), b["dt"], M, K, None, 0.0,
                                               b["q"].data_ptr(), b["g"].data_ptr(), stream()))
@@ -988,6 +1017,7 @@ def main():
         "config": {"workload": meta["workload"], "M": meta["M"], "K": meta["K"], "N": meta["N"],
                    "weight_copies": meta["weight_copies"],
                    "timing": "eager" if args.eager else "hip_graph_of_all_timed_steps",
+                   "one_token_calls": "two calls" if args.unfused else "fused quant_forward",
                    "int8_eq_TOPS_per_step": round(meta["ops_per_step"] / (ms_step * 1e-3) / 1e12, 3),
                    "hbm_frac_per_step": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roof,

@@ -32,6 +32,8 @@ _SIGNATURES = {
     "bitlinear_pack_weights": [_vp, _i64, _i64, _vp, _vp, _vp],
     "bitlinear_forward": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _vp],
     "bitlinear_forward_path": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, ctypes.c_int, _vp],
+    "bitlinear_quant_forward": [_vp, ctypes.c_int, _i64, _i64, _vp, _f32, _vp, _i64, _f32, _vp, _vp,
+                                _vp, _vp, _vp],
     "bitlinear_silu_mul_quant": [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp],
     "bitlinear_ternarize": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "bitlinear_binarize": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
@@ -163,6 +165,35 @@ def forward(x_q: torch.Tensor, gamma: torch.Tensor, w_packed: torch.Tensor, beta
                                       N, float(beta), y.data_ptr(), _ptr(acc), int(path),
                                       _stream(x_q)))
     return (y, acc) if want_acc else y
+
+
+def quant_forward(x: torch.Tensor, w_packed: torch.Tensor, beta: float,
+                  rms_gain: Optional[torch.Tensor] = None, rms_eps: float = 1e-6,
+                  want_acc: bool = False,
+                  out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """quant_act then forward in one call (one kernel for a single token):
+    returns (y, x_q, gamma), or (y, x_q, gamma, acc) with ``want_acc``.
+    ``out`` = (y, x_q, gamma) buffers to write."""
+    _dev(x, "x", (torch.float32, torch.bfloat16))
+    _dev(w_packed, "w_packed", (torch.int32, torch.uint32))
+    M, K = x.shape
+    N = w_packed.shape[0]
+    if w_packed.shape[1] * 16 != K:
+        raise ValueError(f"w_packed has {w_packed.shape[1]} words per row, K={K} needs {K // 16}")
+    if rms_gain is not None:
+        _dev(rms_gain, "rms_gain", (torch.float32,))
+    if out is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        x_q = torch.empty((M, K), dtype=torch.int8, device=x.device)
+        gamma = torch.empty((M,), dtype=torch.float32, device=x.device)
+    else:
+        y, x_q, gamma = out
+    acc = torch.empty((M, N), dtype=torch.int32, device=x.device) if want_acc else None
+    dt = BF16 if x.dtype == torch.bfloat16 else F32
+    _check(lib.bitlinear_quant_forward(x.data_ptr(), dt, M, K, _ptr(rms_gain), float(rms_eps),
+                                       w_packed.data_ptr(), N, float(beta), x_q.data_ptr(),
+                                       gamma.data_ptr(), y.data_ptr(), _ptr(acc), _stream(x)))
+    return (y, x_q, gamma, acc) if want_acc else (y, x_q, gamma)
 
 
 def silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, want_h: bool = False):

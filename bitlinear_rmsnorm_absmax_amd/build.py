@@ -13,7 +13,7 @@ LIB = os.path.join(HERE, "libbitlinear.so")
 
 SOURCES = ["api.cpp", "quant_act.hip", "pack.hip", "gemv_valu.hip", "skinny_mfma.hip",
            "decode_lds.hip", "gemm_mfma.hip", "gemm_dma.hip", "ternarize.hip", "binary.hip",
-           "grouped.hip", "base3.hip"]
+           "grouped.hip", "base3.hip", "quant_gemv.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

@@ -178,6 +178,45 @@ bitlinear_status_t bitlinear_forward_path(const int8_t* x_q, const float* gamma,
                         path, stream);
 }
 
+bitlinear_status_t bitlinear_quant_forward(const void* x, bitlinear_dtype_t x_dtype, int64_t M,
+                                           int64_t K, const float* rms_gain, float rms_eps,
+                                           const uint32_t* w_packed, int64_t N, float beta,
+                                           int8_t* x_q, float* gamma, float* y, int32_t* acc,
+                                           hipStream_t stream) {
+    const char* fn = "bitlinear_quant_forward";
+    BL_TRY(check_rows(fn, "M", M, kMaxM));
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    BL_TRY(check_k(fn, "K", K));
+    if (x_dtype != BITLINEAR_F32 && x_dtype != BITLINEAR_BF16)
+        return fail(BITLINEAR_ERR_DTYPE, "%s: unknown dtype %d", fn, (int)x_dtype);
+    if (rms_gain && !(std::isfinite(rms_eps) && rms_eps >= 0.0f))
+        return fail(BITLINEAR_ERR_VALUE, "%s: rms_eps must be finite and >= 0", fn);
+    if (!std::isfinite(beta)) return fail(BITLINEAR_ERR_VALUE, "%s: beta is not finite", fn);
+    const bool any_q = M > 0 && K > 0;
+    const bool any_out = M > 0 && N > 0;
+    BL_TRY(need(fn, "x", x, any_q, 16));
+    BL_TRY(need(fn, "x_q", x_q, any_q, 16));
+    BL_TRY(need(fn, "gamma", gamma, M > 0, 4));
+    if (rms_gain && !aligned(rms_gain, 16))
+        return fail(BITLINEAR_ERR_ALIGN, "%s: rms_gain is not 16-byte aligned", fn);
+    BL_TRY(need(fn, "w_packed", w_packed, any_out && K > 0, 16));
+    BL_TRY(need(fn, "y", y, any_out, 4));
+    if (acc && !aligned(acc, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: acc is not 4-byte aligned", fn);
+    if (M == 0) return ok();
+    if (bl::quant_gemv_supports((int)M, (int)K, (int)N))
+        return from_hip(bl::launch_quant_gemv(x, x_dtype == BITLINEAR_BF16, (int)K, rms_gain,
+                                              rms_eps, w_packed, (int)N, beta, y, acc, x_q, gamma,
+                                              stream),
+                        fn);
+    hipError_t e = bl::launch_quant_act(x, x_dtype == BITLINEAR_BF16, M, K, rms_gain, rms_eps, x_q,
+                                        gamma, stream);
+    if (e != hipSuccess || !any_out) return from_hip(e, fn);
+    if (K == 0) return from_hip(bl::launch_fill_zero(y, acc, M * N, stream), fn);
+    return from_hip(launch_forward_kernel(x_q, gamma, M, K, w_packed, N, beta, y, acc,
+                                          BITLINEAR_PATH_AUTO, stream),
+                    fn);
+}
+
 bitlinear_status_t bitlinear_silu_mul_quant(const float* gate, const float* up, int64_t M,
                                             int64_t F, float* h, int8_t* h_q, float* gamma_h,
                                             hipStream_t stream) {

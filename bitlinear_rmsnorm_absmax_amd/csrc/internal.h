@@ -13,6 +13,15 @@ namespace bl {
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, const float* gain,
                             float eps, int8_t* q, float* gamma, hipStream_t s);
 
+// Fused quantisation + one-token product (quant_gemv.hip): M == 1,
+// K % 64 == 0, K <= kFusedMaxK (the codes are staged in LDS), N <= kFusedMaxN.
+constexpr int kFusedMaxK = 16384;
+constexpr int kFusedMaxN = 16384;
+bool quant_gemv_supports(int M, int K, int N);
+hipError_t launch_quant_gemv(const void* x, bool bf16, int K, const float* gain, float eps,
+                             const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
+                             int8_t* q_out, float* gamma_out, hipStream_t s);
+
 hipError_t launch_silu_mul_quant(const float* gate, const float* up, int64_t M, int64_t F,
                                  float* h, int8_t* h_q, float* gamma, hipStream_t s);
 

@@ -14,84 +14,10 @@
 // (L2-resident by then).
 #include "device_common.h"
 #include "internal.h"
+#include "quant_rows.h"
 
 namespace bl {
 namespace {
-
-constexpr int kQuantThreads = 256;
-constexpr int kQuantCache = 2;
-
-enum class Src { F32, BF16, SILU_MUL };
-
-struct RowSrc {
-    const void* a;  // x (fp32 / bf16) or gate (fp32)
-    const float* b; // up (SILU_MUL only)
-};
-
-// Load chunk c (16 elements) of row `row` (length K) as fp32.
-template <Src S>
-__device__ __forceinline__ void load_chunk(const RowSrc& src, int64_t row, int K, int c,
-                                           float v[16]) {
-    const int64_t base = row * (int64_t)K + (int64_t)c * 16;
-    if constexpr (S == Src::F32) {
-        const v4f* p = reinterpret_cast<const v4f*>(static_cast<const float*>(src.a) + base);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v4f t = __builtin_nontemporal_load(p + i);
-            v[4 * i + 0] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-        }
-    } else if constexpr (S == Src::BF16) {
-        const v4u* p = reinterpret_cast<const v4u*>(static_cast<const uint16_t*>(src.a) + base);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            v4u t = __builtin_nontemporal_load(p + i);
-            uint32_t d[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[8 * i + 2 * j + 0] = __uint_as_float(d[j] << 16);          // exact widening
-                v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
-            }
-        }
-    } else {
-        const float4* pg = reinterpret_cast<const float4*>(static_cast<const float*>(src.a) + base);
-        const float4* pu = reinterpret_cast<const float4*>(src.b + base);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float4 g = pg[i];
-            float4 u = pu[i];
-            float gg[4] = {g.x, g.y, g.z, g.w};
-            float uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // silu(z) * up in float64, rounded once to fp32
-                double z = (double)gg[j];
-                double sl = z / (1.0 + exp(-z));
-                v[4 * i + j] = (float)(sl * (double)uu[j]);
-            }
-        }
-    }
-}
-
-// Block-wide reductions: max of a float and sum of a double.
-__device__ __forceinline__ void block_reduce(float& amax, double& ss, bool with_ss) {
-    __shared__ float s_max[kQuantThreads / kWave];
-    __shared__ double s_ss[kQuantThreads / kWave];
-    const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-    amax = wave_max(amax);
-    if (with_ss) ss = wave_sum_d(ss);
-    if (lane == 0) {
-        s_max[wv] = amax;
-        s_ss[wv] = ss;
-    }
-    __syncthreads();
-    amax = s_max[0];
-    ss = s_ss[0];
-#pragma unroll
-    for (int i = 1; i < kQuantThreads / kWave; ++i) {
-        amax = fmaxf(amax, s_max[i]);
-        ss += s_ss[i];
-    }
-}
 
 __device__ __forceinline__ void store_codes(int8_t* q, int64_t row, int K, int c,
                                             const float v[16], float gamma) {

@@ -123,6 +123,23 @@ bitlinear_status_t bitlinear_forward(const int8_t* x_q, const float* gamma, int6
                                      const uint32_t* w_packed, int64_t N, float beta, float* y,
                                      int32_t* acc, hipStream_t stream);
 
+/*
+ * The whole BitLinear forward from unquantised activations: bitlinear_quant_act
+ * followed by bitlinear_forward (datacamp article, Kerncomponenten: RMS norm,
+ * absmax quantisation, ternary product; unite.ai article, 2.
+ * Aktivierungsquantisierung and 3. BitLinear-Betrieb).  Arguments as in those
+ * two calls; x_q and gamma are outputs here and are written in every case.
+ * For one token with K % 64 == 0, K <= 16384 and N <= 16384 it runs as one
+ * kernel (each workgroup quantises the token into LDS and multiplies its
+ * weight rows); otherwise as the two calls in order on `stream`.  x_q, gamma, y and acc are
+ * bit-identical to those of the two calls.
+ */
+bitlinear_status_t bitlinear_quant_forward(const void* x, bitlinear_dtype_t x_dtype, int64_t M,
+                                           int64_t K, const float* rms_gain, float rms_eps,
+                                           const uint32_t* w_packed, int64_t N, float beta,
+                                           int8_t* x_q, float* gamma, float* y, int32_t* acc,
+                                           hipStream_t stream);
+
 /* bitlinear_forward with an explicit kernel (bitlinear_path_t).  A path that
  * cannot take this M (GEMV: M > 4, SKINNY: M > 64) returns BITLINEAR_ERR_VALUE. */
 bitlinear_status_t bitlinear_forward_path(const int8_t* x_q, const float* gamma, int64_t M,

@@ -18,7 +18,8 @@ def test_every_declared_symbol_is_exported():
     declared = bl.declared_symbols()
     assert set(declared) == {
         "bitlinear_quant_act", "bitlinear_pack_weights", "bitlinear_forward",
-        "bitlinear_forward_path", "bitlinear_silu_mul_quant", "bitlinear_ternarize",
+        "bitlinear_forward_path", "bitlinear_quant_forward", "bitlinear_silu_mul_quant",
+        "bitlinear_ternarize",
         "bitlinear_binarize", "bitlinear_pack_weights1", "bitlinear_forward1",
         "bitlinear_quant_act_grouped", "bitlinear_forward_grouped", "bitlinear_ternarize_grouped",
         "bitlinear_forward_grouped_one_launch", "bitlinear_pack_weights3", "bitlinear_forward3",
@@ -95,6 +96,42 @@ def test_quant_rejects(kw, status, msg):
 
 def test_quant_empty_is_ok():
     assert _quant(x=None, q=None, g=None, M=0) == bl.OK
+
+
+def _qfwd(x=FAKE, dt=0, M=1, K=64, gain=None, eps=1e-6, w=FAKE, N=1, beta=1.0, q=FAKE, g=FAKE,
+          y=FAKE, acc=None):
+    return bl.lib.bitlinear_quant_forward(x, dt, M, K, gain, F(eps), w, N, F(beta), q, g, y, acc,
+                                          None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(x=None), bl.ERR_NULL, "x is NULL"),
+    (dict(q=None), bl.ERR_NULL, "x_q is NULL"),
+    (dict(g=None), bl.ERR_NULL, "gamma is NULL"),
+    (dict(w=None), bl.ERR_NULL, "w_packed is NULL"),
+    (dict(y=None), bl.ERR_NULL, "y is NULL"),
+    (dict(dt=3), bl.ERR_DTYPE, "unknown dtype"),
+    (dict(K=40), bl.ERR_SHAPE, "multiple of 16"),
+    (dict(K=131072 + 16), bl.ERR_SHAPE, "K=131088"),
+    (dict(M=-1), bl.ERR_SHAPE, "M=-1"),
+    (dict(N=-3), bl.ERR_SHAPE, "N=-3"),
+    (dict(x=FAKE + 8), bl.ERR_ALIGN, "x is not 16-byte aligned"),
+    (dict(q=FAKE + 4), bl.ERR_ALIGN, "x_q is not 16-byte aligned"),
+    (dict(w=FAKE + 4), bl.ERR_ALIGN, "w_packed is not 16-byte aligned"),
+    (dict(y=FAKE + 2), bl.ERR_ALIGN, "y is not 4-byte aligned"),
+    (dict(acc=FAKE + 2), bl.ERR_ALIGN, "acc is not 4-byte aligned"),
+    (dict(gain=FAKE + 4), bl.ERR_ALIGN, "rms_gain is not 16-byte aligned"),
+    (dict(gain=FAKE, eps=float("inf")), bl.ERR_VALUE, "rms_eps"),
+    (dict(beta=float("nan")), bl.ERR_VALUE, "beta"),
+])
+def test_quant_forward_rejects(kw, status, msg):
+    assert _qfwd(**kw) == status
+    assert msg in bl.last_error()
+
+
+def test_quant_forward_empty_is_ok():
+    assert _qfwd(x=None, q=None, g=None, w=None, y=None, M=0) == bl.OK
+    assert bl.last_error() == ""
 
 
 @pytest.mark.parametrize("args,status,msg", [

@@ -805,3 +805,81 @@ def test_base3_empty(dev):
     y = bl.forward3(torch.zeros((0, 160), dtype=torch.int8, device=dev),
                     torch.zeros(0, device=dev), torch.zeros((3, 8), dtype=torch.int32, device=dev), 0.5)
     assert y.shape == (0, 3)
+
+
+# ------------------------------------------------------------------ fused quantise + forward
+
+# One token with K % 64 == 0, K <= 16384 and N <= 16384 runs as one kernel
+# (workgroups of 4, 8 or 16 waves by N: 4096, 8192 and 16384 rows are the
+# widest of each); the other cases (K not a multiple of 64, K past 16384, N
+# past 16384, several tokens) as the two calls.
+QFWD_CASES = [(1, 64, 1, "f32", None), (1, 2048, 1000, "bf16", "unit"),
+              (1, 4096, 11008, "f32", "rand"), (1, 8192, 17, "bf16", None),
+              (1, 16384, 300, "f32", "rand"), (1, 2560, 6912, "f32", "unit"),
+              (1, 1024, 4096, "f32", None), (1, 1024, 4097, "bf16", None),
+              (1, 512, 8193, "f32", "unit"), (1, 512, 16384, "f32", None),
+              (1, 256, 16385, "f32", None),
+              (1, 16448, 40, "f32", None), (1, 1040, 77, "bf16", "rand"),
+              (3, 4096, 500, "bf16", "rand"), (16, 2560, 700, "f32", None)]
+
+
+@pytest.mark.parametrize("M,K,N,dt,gain_kind", QFWD_CASES)
+def test_quant_forward_parity(dev, M, K, N, dt, gain_kind):
+    act = "normal_bf16" if dt == "bf16" else "normal_f32"
+    x, w, beta = workloads.random_case(1100 + K + N, M, N, K, act=act,
+                                       table=workloads.TERNARY_HALF_ZERO)
+    xf = oracle.bf16_to_f32(x) if dt == "bf16" else x
+    xd = to_dev(x, dev, torch.bfloat16) if dt == "bf16" else to_dev(x, dev)
+    rng = workloads.rng_for(1101, K)
+    gain = None if gain_kind is None else (np.ones(K, np.float32) if gain_kind == "unit" else
+                                           rng.uniform(0.5, 2.0, K).astype(np.float32))
+    gd = None if gain is None else to_dev(gain, dev)
+    wp = gpu_pack(w, dev)
+    y, q, g, acc = (host(t) for t in bl.quant_forward(xd, wp, beta, rms_gain=gd, rms_eps=1e-6,
+                                                     want_acc=True))
+    if gain is None:
+        q_ref, g_ref = oracle.quant_act(xf)
+        np.testing.assert_array_equal(g, g_ref)
+    else:
+        q_ref, g_ref = oracle.rmsnorm_quant_act(xf, gain, 1e-6)
+        assert_y_close(g, g_ref)
+    np.testing.assert_array_equal(q, q_ref)
+    y_ref, acc_ref = oracle.forward(q_ref, g, w, beta)
+    np.testing.assert_array_equal(acc, acc_ref)
+    assert_y_close(y, y_ref)
+    # bit-identical to bitlinear_quant_act followed by bitlinear_forward
+    q2, g2 = bl.quant_act(xd, gd, 1e-6)
+    y2, acc2 = bl.forward(q2, g2, wp, beta, want_acc=True)
+    np.testing.assert_array_equal(q, host(q2))
+    np.testing.assert_array_equal(g.view(np.uint32), host(g2).view(np.uint32))
+    np.testing.assert_array_equal(acc, host(acc2))
+    np.testing.assert_array_equal(y.view(np.uint32), host(y2).view(np.uint32))
+
+
+def test_quant_forward_zero_token_and_extremes(dev):
+    K, N = 4096, 333
+    w = workloads.ternary(workloads.rng_for(1102), N, K, workloads.TERNARY_UNIFORM)
+    w[0, :] = 1
+    w[1, :] = -1
+    wp = gpu_pack(w, dev)
+    y, q, g = bl.quant_forward(torch.zeros((1, K), device=dev), wp, 0.5)
+    assert not host(q).any() and host(g)[0] == 0.0 and not host(y).any()
+    # one large entry: gamma = |x_max|, its code 127, the rest 0 or small
+    x = np.zeros((1, K), np.float32)
+    x[0, 5] = -3.0e30
+    x[0, 9] = 1.0e29
+    y, q, g, acc = (host(t) for t in bl.quant_forward(to_dev(x, dev), wp, 0.5, want_acc=True))
+    q_ref, g_ref = oracle.quant_act(x)
+    np.testing.assert_array_equal(q, q_ref)
+    np.testing.assert_array_equal(g, g_ref)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, 0.5)
+    np.testing.assert_array_equal(acc, acc_ref)
+    assert_y_close(y, y_ref)
+
+
+def test_quant_forward_empty(dev):
+    wp = torch.zeros((5, 4), dtype=torch.int32, device=dev)
+    y, q, g = bl.quant_forward(torch.zeros((0, 64), device=dev), wp, 1.0)
+    assert y.shape == (0, 5) and q.shape == (0, 64)
+    y, q, g = bl.quant_forward(torch.ones((1, 64), device=dev), wp[:0], 1.0)
+    assert y.shape == (1, 0) and host(g)[0] == 1.0
