@@ -482,6 +482,16 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
     const int64_t wide_tiles = (int64_t)((M + 127) / 128) * ((N + 255) / 256);
     if (M >= 256 && wide_tiles >= 256)
         return launch_pipe<1, 4, 4, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    // at most one 64 x 128 tile per CU on a K of whole 256-steps: 64 x 128
+    // tiles, two K groups per workgroup (8 waves).  Small M wastes no padded
+    // rows and few-tile shapes spread over more CUs.  Measured against the
+    // 128 x 128 route below: M = 64, K = 8192, N = 28672 47 -> 31 us; M = 96,
+    // K = 4096, N = 11008 25 -> 17 us; M = 512, K = 6912, N = 2560 35 -> 24 us;
+    // M = 512, K = 2560, N = 2560 18 -> 13 us; with more than 256 such tiles it
+    // loses (M = 200, K = 4096, N = 11008 27 -> 31 us).
+    const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
+    if (tiles64 <= 256 && K % (2 * BK) == 0)
+        return launch_dcfg<2, 2, 1, 2, 3, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     // fewer 128 x 128 tiles than CUs on a K of whole 256-steps: two K groups
     // per workgroup (8 waves, 120 KB of LDS, one workgroup per CU).  Measured:
     // M = 512, K = 6912, N = 2560 36 -> 33 us; M = 64, K = 8192, N = 28672

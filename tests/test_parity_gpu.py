@@ -192,6 +192,26 @@ def test_forward_parity(dev, path, M, N, K):
 WIDE_GEMM_CASES = [(257, 22053, 128), (256, 32769, 256), (300, 22016, 384), (384, 22016, 640)]
 
 
+# At most 256 tiles of 64 x 128 and K % 256 == 0: 64-row tiles with two K
+# groups per workgroup (ragged M, a last row tile with one row, ragged N).
+SMALL_TILE_GEMM_CASES = [(64, 3000, 2560), (65, 1000, 768), (96, 2000, 1536), (300, 700, 1536),
+                         (512, 257, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL_TILE_GEMM_CASES)
+def test_gemm_small_tiles_parity(dev, M, N, K):
+    assert -(-M // 64) * -(-N // 128) <= 256 and K % 256 == 0
+    x, w, beta = workloads.random_case(950 + M + K, M, N, K, table=workloads.TERNARY_HALF_ZERO)
+    x = x.copy()
+    x[M - 1] = 0.0  # zero token in the last row tile
+    q, g, y, acc = run_forward(x, w, beta, dev, bl.PATH_GEMM)
+    q_ref, g_ref = oracle.quant_act(x)
+    np.testing.assert_array_equal(q, q_ref)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, beta)
+    np.testing.assert_array_equal(acc, acc_ref)
+    assert_y_close(y, y_ref)
+
+
 @pytest.mark.parametrize("M,N,K", WIDE_GEMM_CASES)
 def test_gemm_wide_tiles_parity(dev, M, N, K):
     assert -(-M // 128) * -(-N // 256) >= 256
