@@ -81,8 +81,8 @@ def parse():
     return ap.parse_args()
 
 
-def forward_kernel(M: int, K: int) -> str:
-    """Kernel that bitlinear_forward picks for M (the library's dispatch)."""
+def forward_kernel(M: int, K: int, N: int) -> str:
+    """Kernel that bitlinear_forward picks (the library's dispatch)."""
     if M == 1:
         return "gemv_valu_kernel"
     lds_fits = K % 256 == 0 and ((M * K + 1023) // 1024) * 1024 + 16384 + 128 <= 160 * 1024
@@ -90,7 +90,11 @@ def forward_kernel(M: int, K: int) -> str:
         return "decode_lds_kernel"
     if M <= 32:
         return "skinny_mfma_kernel"
-    return "gemm_dma_kernel" if K % 128 == 0 else "gemm_mfma_kernel"
+    if K % 128 != 0:
+        return "gemm_mfma_kernel"
+    if M >= 256 and -(-M // 128) * -(-N // 256) >= 256:
+        return "gemm_pipe_kernel"
+    return "gemm_dma_kernel"
 
 
 # ----------------------------------------------------------------------------- timers
@@ -109,7 +113,7 @@ class RunAll:
             # (+ the unquantised activations read by a fused call)
             self.info[name] = dict(alg_bytes=wbytes + M * K + 4 * M + 4 * M * N + xbytes,
                                    ops=2 * M * N * K, wbytes=wbytes, M=M, N=N, K=K,
-                                   kernel=kernel or forward_kernel(M, K))
+                                   kernel=kernel or forward_kernel(M, K, N))
         return True
 
 
@@ -344,7 +348,8 @@ def traffic_write(args):
             raise SystemExit(f"counter run holds {len(lib)} library dispatches, "
                              f"the probe made {len(calls)}")
         for call, (name, _) in zip(calls, lib):
-            want = "quant_rows" if call.startswith(("quant", "silu")) else "_kernel"
+            want = ("quant_gemv" if call.startswith("quant_forward") else
+                    "quant_rows" if call.startswith(("quant", "silu")) else "_kernel")
             if want not in name or (call.startswith("forward") and "quant_rows" in name):
                 raise SystemExit(f"dispatch {name} does not match call {call}")
         return lib, rows[copies[-1]]
