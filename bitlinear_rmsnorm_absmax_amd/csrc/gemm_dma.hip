@@ -263,8 +263,9 @@ __device__ __forceinline__ unsigned biased_sum16(v4i a, unsigned acc) {
 //     weight words are then read one 32-bit word per slice;
 //   - the row sums use biased_sum16, the bias is removed once at the end.
 // Measured with a 1 x 4 wave layout (each wave 128 rows x 64 columns, so each
-// packed word is unpacked once per workgroup): M = 512, K = 8192, N = 28672
-// 125 -> 112 us; M = 2048, K = 4096, N = 11008 unchanged (about 103 us).
+// packed word is unpacked once per workgroup), A/B in one session:
+// M = 512, K = 8192, N = 28672 125 -> 116 us; M = 2048, K = 4096, N = 11008
+// 101 -> 96 us.
 template <int WM, int WN, int TM, int TN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_pipe_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M,
@@ -492,16 +493,11 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
     const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
     if (tiles64 <= 256 && K % (2 * BK) == 0)
         return launch_dcfg<2, 2, 1, 2, 3, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    // fewer 128 x 128 tiles than CUs on a K of whole 256-steps: two K groups
-    // per workgroup (8 waves, 120 KB of LDS, one workgroup per CU).  Measured:
-    // M = 512, K = 6912, N = 2560 36 -> 33 us; M = 64, K = 8192, N = 28672
-    // 45 -> 43 us.  Per-wave timestamps show the K step then takes about twice
-    // as long: the compute unit's copy stream, not the step latency, bounds
-    // these shapes.
-    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles < 256 && K % (2 * BK) == 0)
-        return launch_dcfg<2, 2, 2, 2, 3, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    return launch_dcfg<2, 2, 2, 2, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    // else 128 x 128 tiles on the pipelined loop (2 x 2 waves of 64 x 64).
+    // Measured against the ring loop on the same tiles, with or without two K
+    // groups per workgroup: equal or up to 6 % faster (M = 512, K = 2560,
+    // N = 6912 20.9 -> 19.9 us; M = 1024, K = 4096, N = 11008 67.7 -> 64.8 us).
+    return launch_pipe<2, 2, 2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
 
 }  // namespace bl

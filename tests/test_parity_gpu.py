@@ -212,6 +212,24 @@ def test_gemm_small_tiles_parity(dev, M, N, K):
     assert_y_close(y, y_ref)
 
 
+# Neither of the above (K % 256 == 128, or more than 256 tiles of 64 x 128):
+# 128 x 128 tiles on the pipelined loop.
+MID_GEMM_CASES = [(100, 1000, 640), (200, 8300, 256), (129, 4200, 384), (255, 2100, 1152)]
+
+
+@pytest.mark.parametrize("M,N,K", MID_GEMM_CASES)
+def test_gemm_mid_tiles_parity(dev, M, N, K):
+    t64 = -(-M // 64) * -(-N // 128)
+    assert (t64 > 256 or K % 256 != 0) and not (M >= 256 and -(-M // 128) * -(-N // 256) >= 256)
+    x, w, beta = workloads.random_case(970 + M + K, M, N, K, table=workloads.TERNARY_UNIFORM)
+    q, g, y, acc = run_forward(x, w, beta, dev, bl.PATH_GEMM)
+    q_ref, g_ref = oracle.quant_act(x)
+    np.testing.assert_array_equal(q, q_ref)
+    y_ref, acc_ref = oracle.forward(q_ref, g_ref, w, beta)
+    np.testing.assert_array_equal(acc, acc_ref)
+    assert_y_close(y, y_ref)
+
+
 @pytest.mark.parametrize("M,N,K", WIDE_GEMM_CASES)
 def test_gemm_wide_tiles_parity(dev, M, N, K):
     assert -(-M // 128) * -(-N // 256) >= 256
