@@ -56,8 +56,10 @@ def parse():
     ap.add_argument("--no-rotate", action="store_true", help="one weight copy (warm cache)")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graphs")
     ap.add_argument("--unfused", action="store_true",
-                    help="one-token steps as bitlinear_quant_act + bitlinear_forward instead of "
-                         "the fused bitlinear_quant_forward")
+                    help="the separate calls: one-token steps as bitlinear_quant_act + "
+                         "bitlinear_forward instead of bitlinear_quant_forward, and the GLU's "
+                         "gate and up as two products + bitlinear_silu_mul_quant instead of "
+                         "one product on the stacked weights + bitlinear_silu_mul_quant_acc")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="time budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--op", choices=("layer", "ternarize", "binary", "grouped", "base3"),
@@ -93,8 +95,10 @@ def forward_kernel(M: int, K: int, N: int) -> str:
     if K % 128 != 0:
         return "gemm_mfma_kernel"
     if M >= 256 and -(-M // 128) * -(-N // 256) >= 256:
-        return "gemm_pipe_kernel"
-    return "gemm_dma_kernel"
+        return "gemm_pipe_kernel"   # 128 x 256 tiles
+    if -(-M // 64) * -(-N // 128) <= 256 and K % 256 == 0:
+        return "gemm_dma_kernel"    # 64 x 128 tiles, two K groups
+    return "gemm_pipe_kernel"       # 128 x 128 tiles
 
 
 # ----------------------------------------------------------------------------- timers
@@ -180,7 +184,16 @@ def build_plan(args, torch, bl, dev):
     if wl.glu_f:
         wg, wu, wd = workloads.glu_weights(wid)
         bg, bu, bd = workloads.glu_betas(wid)
-        layers = [Layer(torch, bl, dev, w, b, rotate) for w, b in ((wg, bg), (wu, bu), (wd, bd))]
+        # default: gate and up as one product on the stacked weights [W_gate; W_up]
+        # writing int32 accumulators, then bitlinear_silu_mul_quant_acc (one weight
+        # stream and one launch for both projections; every stage bit-identical to
+        # the separate calls); --unfused runs the separate calls
+        stacked = not args.unfused
+        if stacked:
+            layers = [Layer(torch, bl, dev, np.concatenate([wg, wu], axis=0), 1.0, rotate),
+                      Layer(torch, bl, dev, wd, bd, rotate)]
+        else:
+            layers = [Layer(torch, bl, dev, w, b, rotate) for w, b in ((wg, bg), (wu, bu), (wd, bd))]
         ncopy = min(len(L.copies) for L in layers)
         D, Fh = wl.K, wl.glu_f
         gain = torch.ones(D, dtype=torch.float32, device=dev)
@@ -191,6 +204,7 @@ def build_plan(args, torch, bl, dev):
                 M=M, x=x, q=torch.empty((M, D), dtype=torch.int8, device=dev),
                 g=torch.empty(M, device=dev), yg=torch.empty((M, Fh), device=dev),
                 yu=torch.empty((M, Fh), device=dev),
+                acc_gu=torch.empty((M, 2 * Fh), dtype=torch.int32, device=dev),
                 hq=torch.empty((M, Fh), dtype=torch.int8, device=dev),
                 gh=torch.empty(M, device=dev), y=torch.empty((M, D), device=dev)))
 
@@ -198,32 +212,44 @@ def build_plan(args, torch, bl, dev):
             c = step % ncopy
             for b in bufs:
                 M = b["M"]
-                projs = (("gate", layers[0], b["yg"]), ("up", layers[1], b["yu"]))
-                if fused(M, D, Fh):
-                    # RMSNorm + quantisation fused with the gate projection; the
-                    # up projection reuses its x_q and gamma
+                if stacked:
                     L = layers[0]
-                    if run(f"quant_forward_rms_gate_M{M}", M, L.N, L.K, L.wbytes, 4 * M * D + 4 * D,
-                           "quant_gemv_kernel"):
-                        check(lib.bitlinear_quant_forward(
-                            b["x"].data_ptr(), bl.F32, M, D, gain.data_ptr(), wl.rms_eps,
-                            L.copies[c].data_ptr(), Fh, L.beta, b["q"].data_ptr(), b["g"].data_ptr(),
-                            b["yg"].data_ptr(), None, stream()))
-                    projs = projs[1:]
-                elif run(f"quant_act_rms_M{M}"):
-                    check(lib.bitlinear_quant_act(b["x"].data_ptr(), bl.F32, M, D, gain.data_ptr(),
-                                                  wl.rms_eps, b["q"].data_ptr(), b["g"].data_ptr(),
-                                                  stream()))
-                for nm, L, out in projs:
-                    if run(f"forward_{nm}_M{M}", M, L.N, L.K, L.wbytes):
-                        check(lib.bitlinear_forward(b["q"].data_ptr(), b["g"].data_ptr(), M, D,
-                                                    L.copies[c].data_ptr(), Fh, L.beta,
-                                                    out.data_ptr(), None, stream()))
-                if run(f"silu_mul_quant_M{M}"):
-                    check(lib.bitlinear_silu_mul_quant(b["yg"].data_ptr(), b["yu"].data_ptr(), M, Fh,
-                                                       None, b["hq"].data_ptr(), b["gh"].data_ptr(),
-                                                       stream()))
-                L = layers[2]
+                    if fused(M, D, 2 * Fh):
+                        if run(f"quant_forward_rms_gateup_M{M}", M, L.N, L.K, L.wbytes,
+                               4 * M * D + 4 * D, "quant_gemv_kernel"):
+                            check(lib.bitlinear_quant_forward(
+                                b["x"].data_ptr(), bl.F32, M, D, gain.data_ptr(), wl.rms_eps,
+                                L.copies[c].data_ptr(), 2 * Fh, 1.0, b["q"].data_ptr(),
+                                b["g"].data_ptr(), None, b["acc_gu"].data_ptr(), stream()))
+                    else:
+                        if run(f"quant_act_rms_M{M}"):
+                            check(lib.bitlinear_quant_act(b["x"].data_ptr(), bl.F32, M, D,
+                                                          gain.data_ptr(), wl.rms_eps,
+                                                          b["q"].data_ptr(), b["g"].data_ptr(),
+                                                          stream()))
+                        if run(f"forward_gateup_M{M}", M, L.N, L.K, L.wbytes):
+                            check(lib.bitlinear_forward(b["q"].data_ptr(), b["g"].data_ptr(), M, D,
+                                                        L.copies[c].data_ptr(), 2 * Fh, 1.0, None,
+                                                        b["acc_gu"].data_ptr(), stream()))
+                    if run(f"silu_mul_quant_acc_M{M}"):
+                        check(lib.bitlinear_silu_mul_quant_acc(
+                            b["acc_gu"].data_ptr(), b["g"].data_ptr(), M, Fh, bg, bu, None,
+                            b["hq"].data_ptr(), b["gh"].data_ptr(), stream()))
+                else:
+                    if run(f"quant_act_rms_M{M}"):
+                        check(lib.bitlinear_quant_act(b["x"].data_ptr(), bl.F32, M, D,
+                                                      gain.data_ptr(), wl.rms_eps, b["q"].data_ptr(),
+                                                      b["g"].data_ptr(), stream()))
+                    for nm, L, out in (("gate", layers[0], b["yg"]), ("up", layers[1], b["yu"])):
+                        if run(f"forward_{nm}_M{M}", M, L.N, L.K, L.wbytes):
+                            check(lib.bitlinear_forward(b["q"].data_ptr(), b["g"].data_ptr(), M, D,
+                                                        L.copies[c].data_ptr(), Fh, L.beta,
+                                                        out.data_ptr(), None, stream()))
+                    if run(f"silu_mul_quant_M{M}"):
+                        check(lib.bitlinear_silu_mul_quant(b["yg"].data_ptr(), b["yu"].data_ptr(), M,
+                                                           Fh, None, b["hq"].data_ptr(),
+                                                           b["gh"].data_ptr(), stream()))
+                L = layers[-1]
                 if run(f"forward_down_M{M}", M, L.N, L.K, L.wbytes):
                     check(lib.bitlinear_forward(b["hq"].data_ptr(), b["gh"].data_ptr(), M, Fh,
                                                 L.copies[c].data_ptr(), D, L.beta, b["y"].data_ptr(),
@@ -1022,7 +1048,8 @@ def main():
         "config": {"workload": meta["workload"], "M": meta["M"], "K": meta["K"], "N": meta["N"],
                    "weight_copies": meta["weight_copies"],
                    "timing": "eager" if args.eager else "hip_graph_of_all_timed_steps",
-                   "one_token_calls": "two calls" if args.unfused else "fused quant_forward",
+                   "fusion": "separate calls" if args.unfused else
+                   "one-token quant_forward; GLU gate+up stacked",
                    "int8_eq_TOPS_per_step": round(meta["ops_per_step"] / (ms_step * 1e-3) / 1e12, 3),
                    "hbm_frac_per_step": round(value / HBM_PEAK_GBS, 4)},
         "roofline": roof,

@@ -35,6 +35,7 @@ _SIGNATURES = {
     "bitlinear_quant_forward": [_vp, ctypes.c_int, _i64, _i64, _vp, _f32, _vp, _i64, _f32, _vp, _vp,
                                 _vp, _vp, _vp],
     "bitlinear_silu_mul_quant": [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp],
+    "bitlinear_silu_mul_quant_acc": [_vp, _vp, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _vp],
     "bitlinear_ternarize": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "bitlinear_binarize": [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "bitlinear_pack_weights1": [_vp, _i64, _i64, _vp, _vp, _vp],
@@ -147,9 +148,11 @@ def pack_weights(w: torch.Tensor, check: bool = True):
 
 def forward(x_q: torch.Tensor, gamma: torch.Tensor, w_packed: torch.Tensor, beta: float,
             path: int = PATH_AUTO, want_acc: bool = False,
-            out: Optional[torch.Tensor] = None, acc_out: Optional[torch.Tensor] = None):
+            out: Optional[torch.Tensor] = None, acc_out: Optional[torch.Tensor] = None,
+            acc_only: bool = False):
     """y [M][N] = BitLinear(x_q, gamma; w_packed, beta).  Returns y, or
-    (y, acc) with ``want_acc``."""
+    (y, acc) with ``want_acc``; with ``acc_only`` only the int32 accumulators
+    are computed and returned."""
     _dev(x_q, "x_q", (torch.int8,))
     _dev(gamma, "gamma", (torch.float32,))
     _dev(w_packed, "w_packed", (torch.int32, torch.uint32))
@@ -157,23 +160,27 @@ def forward(x_q: torch.Tensor, gamma: torch.Tensor, w_packed: torch.Tensor, beta
     N = w_packed.shape[0]
     if w_packed.shape[1] * 16 != K:
         raise ValueError(f"w_packed has {w_packed.shape[1]} words per row, K={K} needs {K // 16}")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x_q.device)
+    y = None if acc_only else (out if out is not None else
+                               torch.empty((M, N), dtype=torch.float32, device=x_q.device))
     acc = acc_out
-    if want_acc and acc is None:
+    if (want_acc or acc_only) and acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=x_q.device)
     _check(lib.bitlinear_forward_path(x_q.data_ptr(), gamma.data_ptr(), M, K, w_packed.data_ptr(),
-                                      N, float(beta), y.data_ptr(), _ptr(acc), int(path),
+                                      N, float(beta), _ptr(y), _ptr(acc), int(path),
                                       _stream(x_q)))
+    if acc_only:
+        return acc
     return (y, acc) if want_acc else y
 
 
 def quant_forward(x: torch.Tensor, w_packed: torch.Tensor, beta: float,
                   rms_gain: Optional[torch.Tensor] = None, rms_eps: float = 1e-6,
                   want_acc: bool = False,
-                  out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+                  out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                  acc_only: bool = False):
     """quant_act then forward in one call (one kernel for a single token):
-    returns (y, x_q, gamma), or (y, x_q, gamma, acc) with ``want_acc``.
-    ``out`` = (y, x_q, gamma) buffers to write."""
+    returns (y, x_q, gamma), or (y, x_q, gamma, acc) with ``want_acc``, or
+    (acc, x_q, gamma) with ``acc_only``.  ``out`` = (y, x_q, gamma) buffers."""
     _dev(x, "x", (torch.float32, torch.bfloat16))
     _dev(w_packed, "w_packed", (torch.int32, torch.uint32))
     M, K = x.shape
@@ -188,12 +195,35 @@ def quant_forward(x: torch.Tensor, w_packed: torch.Tensor, beta: float,
         gamma = torch.empty((M,), dtype=torch.float32, device=x.device)
     else:
         y, x_q, gamma = out
-    acc = torch.empty((M, N), dtype=torch.int32, device=x.device) if want_acc else None
+    if acc_only:
+        y = None
+    acc = torch.empty((M, N), dtype=torch.int32, device=x.device) if want_acc or acc_only else None
     dt = BF16 if x.dtype == torch.bfloat16 else F32
     _check(lib.bitlinear_quant_forward(x.data_ptr(), dt, M, K, _ptr(rms_gain), float(rms_eps),
                                        w_packed.data_ptr(), N, float(beta), x_q.data_ptr(),
-                                       gamma.data_ptr(), y.data_ptr(), _ptr(acc), _stream(x)))
+                                       gamma.data_ptr(), _ptr(y), _ptr(acc), _stream(x)))
+    if acc_only:
+        return acc, x_q, gamma
     return (y, x_q, gamma, acc) if want_acc else (y, x_q, gamma)
+
+
+def silu_mul_quant_acc(acc_gu: torch.Tensor, gamma: torch.Tensor, beta_gate: float,
+                       beta_up: float, want_h: bool = False):
+    """GLU glue from the int32 accumulators [M][2F] of the stacked gate + up
+    product -> (h_q, gamma_h[, h])."""
+    _dev(acc_gu, "acc_gu", (torch.int32,))
+    _dev(gamma, "gamma", (torch.float32,))
+    M, F2 = acc_gu.shape
+    if F2 % 2:
+        raise ValueError(f"acc_gu has {F2} columns, expected 2F")
+    F = F2 // 2
+    h_q = torch.empty((M, F), dtype=torch.int8, device=acc_gu.device)
+    g = torch.empty((M,), dtype=torch.float32, device=acc_gu.device)
+    h = torch.empty((M, F), dtype=torch.float32, device=acc_gu.device) if want_h else None
+    _check(lib.bitlinear_silu_mul_quant_acc(acc_gu.data_ptr(), gamma.data_ptr(), M, F,
+                                            float(beta_gate), float(beta_up), _ptr(h),
+                                            h_q.data_ptr(), g.data_ptr(), _stream(acc_gu)))
+    return (h_q, g, h) if want_h else (h_q, g)
 
 
 def silu_mul_quant(gate: torch.Tensor, up: torch.Tensor, want_h: bool = False):

@@ -109,7 +109,8 @@ bitlinear_status_t forward_impl(const char* fn, const int8_t* x_q, const float* 
     BL_TRY(need(fn, "x_q", x_q, any_in, 16));
     BL_TRY(need(fn, "gamma", gamma, any_in, 4));
     BL_TRY(need(fn, "w_packed", w_packed, any_in, 16));
-    BL_TRY(need(fn, "y", y, any_out, 4));
+    BL_TRY(need(fn, "y", y, any_out && !acc, 4));
+    if (y && !aligned(y, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: y is not 4-byte aligned", fn);
     if (acc && !aligned(acc, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: acc is not 4-byte aligned", fn);
     if (path == BITLINEAR_PATH_GEMV && M > 4)
         return fail(BITLINEAR_ERR_VALUE, "%s: the GEMV path takes M <= 4 (M=%lld)", fn, (long long)M);
@@ -200,7 +201,8 @@ bitlinear_status_t bitlinear_quant_forward(const void* x, bitlinear_dtype_t x_dt
     if (rms_gain && !aligned(rms_gain, 16))
         return fail(BITLINEAR_ERR_ALIGN, "%s: rms_gain is not 16-byte aligned", fn);
     BL_TRY(need(fn, "w_packed", w_packed, any_out && K > 0, 16));
-    BL_TRY(need(fn, "y", y, any_out, 4));
+    BL_TRY(need(fn, "y", y, any_out && !acc, 4));
+    if (y && !aligned(y, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: y is not 4-byte aligned", fn);
     if (acc && !aligned(acc, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: acc is not 4-byte aligned", fn);
     if (M == 0) return ok();
     if (bl::quant_gemv_supports((int)M, (int)K, (int)N))
@@ -231,6 +233,27 @@ bitlinear_status_t bitlinear_silu_mul_quant(const float* gate, const float* up, 
     if (h && !aligned(h, 16)) return fail(BITLINEAR_ERR_ALIGN, "%s: h is not 16-byte aligned", fn);
     if (M == 0) return ok();
     return from_hip(bl::launch_silu_mul_quant(gate, up, M, F, h, h_q, gamma_h, stream), fn);
+}
+
+bitlinear_status_t bitlinear_silu_mul_quant_acc(const int32_t* acc_gu, const float* gamma,
+                                                int64_t M, int64_t F, float beta_gate,
+                                                float beta_up, float* h, int8_t* h_q,
+                                                float* gamma_h, hipStream_t stream) {
+    const char* fn = "bitlinear_silu_mul_quant_acc";
+    BL_TRY(check_rows(fn, "M", M, (1LL << 31) - 1));
+    BL_TRY(check_k(fn, "F", F));
+    if (!std::isfinite(beta_gate) || !std::isfinite(beta_up))
+        return fail(BITLINEAR_ERR_VALUE, "%s: beta_gate and beta_up must be finite", fn);
+    const bool any = M > 0 && F > 0;
+    BL_TRY(need(fn, "acc_gu", acc_gu, any, 16));
+    BL_TRY(need(fn, "gamma", gamma, any, 4));
+    BL_TRY(need(fn, "h_q", h_q, any, 16));
+    BL_TRY(need(fn, "gamma_h", gamma_h, M > 0, 4));
+    if (h && !aligned(h, 16)) return fail(BITLINEAR_ERR_ALIGN, "%s: h is not 16-byte aligned", fn);
+    if (M == 0) return ok();
+    return from_hip(bl::launch_silu_mul_quant_acc(acc_gu, gamma, M, F, beta_gate, beta_up, h, h_q,
+                                                  gamma_h, stream),
+                    fn);
 }
 
 bitlinear_status_t bitlinear_ternarize(const float* W, int64_t N, int64_t K, uint32_t* w_packed,

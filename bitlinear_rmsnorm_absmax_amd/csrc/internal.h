@@ -24,6 +24,11 @@ hipError_t launch_quant_gemv(const void* x, bool bf16, int K, const float* gain,
 
 hipError_t launch_silu_mul_quant(const float* gate, const float* up, int64_t M, int64_t F,
                                  float* h, int8_t* h_q, float* gamma, hipStream_t s);
+// The same from the int32 accumulators [M][2F] of one product with stacked
+// gate and up weights (gate half, then up half of each row).
+hipError_t launch_silu_mul_quant_acc(const int32_t* acc_gu, const float* gamma_in, int64_t M,
+                                     int64_t F, float beta_gate, float beta_up, float* h,
+                                     int8_t* h_q, float* gamma, hipStream_t s);
 
 hipError_t launch_pack(const int8_t* w, int64_t N, int64_t K, uint32_t* packed, int32_t* bad,
                        hipStream_t s);

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ y,
                                                         int32_t* __restrict__ acc, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * 256) {
-        y[i] = 0.0f;
+        if (y) y[i] = 0.0f;
         if (acc) acc[i] = 0;
     }
 }

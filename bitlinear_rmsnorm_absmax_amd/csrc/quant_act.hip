@@ -237,4 +237,21 @@ hipError_t launch_silu_mul_quant(const float* gate, const float* up, int64_t M, 
     return hipGetLastError();
 }
 
+hipError_t launch_silu_mul_quant_acc(const int32_t* acc_gu, const float* gamma_in, int64_t M,
+                                     int64_t F, float beta_gate, float beta_up, float* h,
+                                     int8_t* h_q, float* gamma, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    if (F == 0) {
+        zero_gamma_kernel<<<dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s>>>(gamma, M);
+        return hipGetLastError();
+    }
+    RowSrc src{acc_gu, nullptr, gamma_in, beta_gate, beta_up};
+    dim3 grid((unsigned)M), block(kQuantThreads);
+    if (h)
+        quant_rows_kernel<Src::SILU_ACC, false, true><<<grid, block, 0, s>>>(src, (int)F, nullptr, 0.f, h, h_q, gamma);
+    else
+        quant_rows_kernel<Src::SILU_ACC, false, false><<<grid, block, 0, s>>>(src, (int)F, nullptr, 0.f, nullptr, h_q, gamma);
+    return hipGetLastError();
+}
+
 }  // namespace bl

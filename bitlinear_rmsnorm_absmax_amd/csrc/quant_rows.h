@@ -12,11 +12,18 @@ namespace bl {
 constexpr int kQuantThreads = 256;
 constexpr int kQuantCache = 2;
 
-enum class Src { F32, BF16, SILU_MUL };
+// F32 / BF16: activations x.  SILU_MUL: h = SiLU(gate) * up from fp32 gate
+// and up.  SILU_ACC: the same h from the int32 accumulators of one product
+// with stacked gate and up weights, each half rescaled as the product would
+// rescale it, fl32(acc) * fl32(beta * gamma_m) / 128.
+enum class Src { F32, BF16, SILU_MUL, SILU_ACC };
 
 struct RowSrc {
-    const void* a;  // x (fp32 / bf16) or gate (fp32)
+    const void* a;  // x (fp32 / bf16), gate (fp32) or the [M][2F] accumulators (int32)
     const float* b; // up (SILU_MUL only)
+    const float* gamma = nullptr;  // SILU_ACC: per-row scale of the product's input
+    float beta_a = 0.f;            // SILU_ACC: beta of the gate half
+    float beta_b = 0.f;            // SILU_ACC: beta of the up half
 };
 
 // Load chunk c (16 elements) of row `row` (length K) as fp32.
@@ -41,6 +48,27 @@ __device__ __forceinline__ void load_chunk(const RowSrc& src, int64_t row, int K
             for (int j = 0; j < 4; ++j) {
                 v[8 * i + 2 * j + 0] = __uint_as_float(d[j] << 16);          // exact widening
                 v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+            }
+        }
+    } else if constexpr (S == Src::SILU_ACC) {
+        // row stride 2K: the gate half, then the up half of the stacked product
+        const int64_t abase = row * 2 * (int64_t)K + (int64_t)c * 16;
+        const int32_t* pa = static_cast<const int32_t*>(src.a);
+        const float g = src.gamma[row];
+        const float sg = out_scale(src.beta_a, g), su = out_scale(src.beta_b, g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const v4i ag = *reinterpret_cast<const v4i*>(pa + abase + 4 * i);
+            const v4i au = *reinterpret_cast<const v4i*>(pa + abase + K + 4 * i);
+            const int gi[4] = {ag.x, ag.y, ag.z, ag.w};
+            const int ui[4] = {au.x, au.y, au.z, au.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float gate = (float)gi[j] * sg;
+                const float up = (float)ui[j] * su;
+                const double z = (double)gate;
+                const double sl = z / (1.0 + exp(-z));
+                v[4 * i + j] = (float)(sl * (double)up);
             }
         }
     } else {

@@ -115,7 +115,8 @@ bitlinear_status_t bitlinear_pack_weights(const int8_t* w, int64_t N, int64_t K,
  *   x_q, gamma  outputs of bitlinear_quant_act ([M][K] int8, [M] fp32).
  *   w_packed    [N][K/16] from bitlinear_pack_weights (16-byte aligned).
  *   beta        per-tensor fp32 weight scale (finite).
- *   y           out [M][N] fp32.
+ *   y           out [M][N] fp32; may be NULL when acc is given (then only the
+ *               accumulators are written, e.g. for bitlinear_silu_mul_quant_acc).
  *   acc         optional out [M][N] int32 accumulators; NULL to skip.
  * The result does not depend on which kernel runs (bit-identical acc and y).
  */
@@ -132,7 +133,7 @@ bitlinear_status_t bitlinear_forward(const int8_t* x_q, const float* gamma, int6
  * For one token with K % 64 == 0, K <= 16384 and N <= 16384 it runs as one
  * kernel (each workgroup quantises the token into LDS and multiplies its
  * weight rows); otherwise as the two calls in order on `stream`.  x_q, gamma, y and acc are
- * bit-identical to those of the two calls.
+ * bit-identical to those of the two calls; y may be NULL when acc is given.
  */
 bitlinear_status_t bitlinear_quant_forward(const void* x, bitlinear_dtype_t x_dtype, int64_t M,
                                            int64_t K, const float* rms_gain, float rms_eps,
@@ -163,6 +164,26 @@ bitlinear_status_t bitlinear_forward_path(const int8_t* x_q, const float* gamma,
 bitlinear_status_t bitlinear_silu_mul_quant(const float* gate, const float* up, int64_t M,
                                             int64_t F, float* h, int8_t* h_q, float* gamma_h,
                                             hipStream_t stream);
+
+/*
+ * The same GLU glue when the gate and up projections are one product with the
+ * two weight matrices stacked along N ([W_gate; W_up], 2F rows, one packed
+ * buffer) and that product wrote only its accumulators (bitlinear_forward with
+ * y = NULL): one launch and one weight stream for both projections.
+ *
+ *   acc_gu     [M][2F] int32: row m holds the F gate accumulators, then the F
+ *              up accumulators.
+ *   gamma      [M] fp32 scale of the product's input (from bitlinear_quant_act).
+ *   beta_gate, beta_up  per-tensor scales of the two weight matrices (finite).
+ * gate and up are rescaled exactly as bitlinear_forward rescales,
+ * fl32(acc) * fl32(beta * gamma_m) / 128, then h, h_q and gamma_h follow
+ * bitlinear_silu_mul_quant: the outputs are bit-identical to running the two
+ * projections separately and bitlinear_silu_mul_quant on their outputs.
+ */
+bitlinear_status_t bitlinear_silu_mul_quant_acc(const int32_t* acc_gu, const float* gamma,
+                                                int64_t M, int64_t F, float beta_gate,
+                                                float beta_up, float* h, int8_t* h_q,
+                                                float* gamma_h, hipStream_t stream);
 
 /*
  * bitlinear_ternarize -- absmean ternarisation of full-precision weights,

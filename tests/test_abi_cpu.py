@@ -19,6 +19,7 @@ def test_every_declared_symbol_is_exported():
     assert set(declared) == {
         "bitlinear_quant_act", "bitlinear_pack_weights", "bitlinear_forward",
         "bitlinear_forward_path", "bitlinear_quant_forward", "bitlinear_silu_mul_quant",
+        "bitlinear_silu_mul_quant_acc",
         "bitlinear_ternarize",
         "bitlinear_binarize", "bitlinear_pack_weights1", "bitlinear_forward1",
         "bitlinear_quant_act_grouped", "bitlinear_forward_grouped", "bitlinear_ternarize_grouped",
@@ -127,6 +128,36 @@ def _qfwd(x=FAKE, dt=0, M=1, K=64, gain=None, eps=1e-6, w=FAKE, N=1, beta=1.0, q
 def test_quant_forward_rejects(kw, status, msg):
     assert _qfwd(**kw) == status
     assert msg in bl.last_error()
+
+
+def _sacc(acc=FAKE, g=FAKE, M=1, F=16, bg=1.0, bu=1.0, h=None, q=FAKE, gh=FAKE):
+    return bl.lib.bitlinear_silu_mul_quant_acc(acc, g, M, F, ctypes.c_float(bg), ctypes.c_float(bu),
+                                               h, q, gh, None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(acc=None), bl.ERR_NULL, "acc_gu is NULL"),
+    (dict(g=None), bl.ERR_NULL, "gamma is NULL"),
+    (dict(q=None), bl.ERR_NULL, "h_q is NULL"),
+    (dict(gh=None), bl.ERR_NULL, "gamma_h is NULL"),
+    (dict(F=40), bl.ERR_SHAPE, "multiple of 16"),
+    (dict(M=-1), bl.ERR_SHAPE, "M=-1"),
+    (dict(bg=float("nan")), bl.ERR_VALUE, "beta_gate and beta_up"),
+    (dict(bu=float("inf")), bl.ERR_VALUE, "beta_gate and beta_up"),
+    (dict(acc=FAKE + 4), bl.ERR_ALIGN, "acc_gu is not 16-byte aligned"),
+    (dict(h=FAKE + 4), bl.ERR_ALIGN, "h is not 16-byte aligned"),
+])
+def test_silu_mul_quant_acc_rejects(kw, status, msg):
+    assert _sacc(**kw) == status
+    assert msg in bl.last_error()
+
+
+def test_forward_y_optional_only_with_acc():
+    # y may be NULL when acc is given; both NULL is an error
+    assert _fwd(y=None, acc=None) == bl.ERR_NULL
+    assert "y is NULL" in bl.last_error()
+    assert _fwd(y=FAKE + 2, acc=FAKE) == bl.ERR_ALIGN
+    assert "y is not 4-byte aligned" in bl.last_error()
 
 
 def test_quant_forward_empty_is_ok():

@@ -428,6 +428,56 @@ def test_glu_stagewise(dev, M):
           f"h_q codes differ at {int((diff != 0).sum())}")
 
 
+@pytest.mark.parametrize("M", [1, 33, 512])
+def test_glu_stacked_matches_stagewise(dev, M):
+    """Gate and up as one product on the stacked weights [W_gate; W_up] that
+    writes only accumulators (M = 1: fused with the RMSNorm quantisation), then
+    bitlinear_silu_mul_quant_acc: every stage bit-identical to the stage-wise
+    chain, which test_glu_stagewise pins to the oracle."""
+    wl = workloads.WORKLOADS[4]
+    x = workloads.workload_activations(4, M)
+    wg, wu, wd = workloads.glu_weights()
+    betas = workloads.glu_betas()
+    F = wg.shape[0]
+    gain = to_dev(np.ones(wl.K, np.float32), dev)
+    pg, pu, pd = (gpu_pack(w, dev) for w in (wg, wu, wd))
+    xd = to_dev(x, dev)
+    st = {k: host(v) for k, v in bl.glu(xd, pg, pu, pd, betas, gain, wl.rms_eps,
+                                         stages=True).items()}
+    gu = torch.cat([pg, pu], dim=0).contiguous()
+    if M == 1:
+        acc_gu, q, g = bl.quant_forward(xd, gu, 1.0, rms_gain=gain, rms_eps=wl.rms_eps,
+                                        acc_only=True)
+    else:
+        q, g = bl.quant_act(xd, gain, wl.rms_eps)
+        acc_gu = bl.forward(q, g, gu, 1.0, acc_only=True)
+    h_q, g_h, h = bl.silu_mul_quant_acc(acc_gu, g, betas[0], betas[1], want_h=True)
+    y = bl.forward(h_q, g_h, pd, betas[2])
+    acc_gu = host(acc_gu)
+    np.testing.assert_array_equal(host(q), st["q"])
+    np.testing.assert_array_equal(host(g).view(np.uint32), st["gamma"].view(np.uint32))
+    np.testing.assert_array_equal(acc_gu[:, :F], st["acc_gate"])
+    np.testing.assert_array_equal(acc_gu[:, F:], st["acc_up"])
+    np.testing.assert_array_equal(host(h).view(np.uint32), st["h"].view(np.uint32))
+    np.testing.assert_array_equal(host(h_q), st["h_q"])
+    np.testing.assert_array_equal(host(g_h).view(np.uint32), st["gamma_h"].view(np.uint32))
+    np.testing.assert_array_equal(host(y).view(np.uint32), st["y"].view(np.uint32))
+
+
+def test_forward_accumulators_only(dev):
+    x, w, beta = workloads.random_case(1200, 40, 300, 512)
+    q, g = bl.quant_act(to_dev(x, dev))
+    wp = gpu_pack(w, dev)
+    for path in (bl.PATH_SKINNY, bl.PATH_GEMM, bl.PATH_AUTO):
+        acc = bl.forward(q, g, wp, beta, path=path, acc_only=True)
+        y2, acc2 = bl.forward(q, g, wp, beta, path=path, want_acc=True)
+        np.testing.assert_array_equal(host(acc), host(acc2))
+    acc_k0 = bl.forward(torch.zeros((3, 0), dtype=torch.int8, device=dev),
+                        torch.zeros(3, device=dev), torch.zeros((5, 0), dtype=torch.int32, device=dev),
+                        1.0, acc_only=True)
+    assert acc_k0.shape == (3, 5) and not host(acc_k0).any()
+
+
 def test_glu_down_projection_on_oracle_codes(dev):
     """The down projection (K = 6912) on the oracle's own requantised h."""
     wl = workloads.WORKLOADS[4]
