@@ -5,6 +5,7 @@ accumulators; fp32 outputs within 1e-6 relative (y_ref = 0 forces y = 0).
 Every input comes from workloads.py; every expected value from oracle/.
 """
 
+import ctypes
 import json
 import os
 
@@ -971,3 +972,61 @@ def test_quant_forward_empty(dev):
     assert y.shape == (0, 5) and q.shape == (0, 64)
     y, q, g = bl.quant_forward(torch.ones((1, 64), device=dev), wp[:0], 1.0)
     assert y.shape == (1, 0) and host(g)[0] == 1.0
+
+
+# ------------------------------------------------------------------ HIP graph replay
+
+def test_graph_replays_match_eager(dev):
+    """The calls of a decode step, a GEMM-sized call and the stacked GLU glue
+    captured in one HIP graph: each of three replays (with eager work and
+    synchronisation in between) reproduces the eager outputs bit for bit."""
+    K, N, F = 4096, 3000, 1024
+    rng = workloads.rng_for(1300)
+    w = workloads.ternary(rng, N, K, workloads.TERNARY_UNIFORM)
+    wp = gpu_pack(w, dev)
+    wgu = gpu_pack(workloads.ternary(rng, 2 * F, K, workloads.TERNARY_HALF_ZERO), dev)
+    beta = 0.03
+    xs = [to_dev(rng.standard_normal((M, K)).astype(np.float32), dev) for M in (1, 4, 16, 300)]
+
+    def run(bufs):
+        for x, b in zip(xs, bufs):
+            bl.quant_forward(x, wp, beta, out=(b["y"], b["q"], b["g"]))
+        b = bufs[-1]
+        bl.forward(b["q"], b["g"], wgu, 1.0, acc_only=True, acc_out=b["acc_gu"])
+        h_q, g_h = b["hq"], b["gh"]
+        st = bl.lib.bitlinear_silu_mul_quant_acc(b["acc_gu"].data_ptr(), b["g"].data_ptr(), 300, F,
+                                                 ctypes.c_float(0.02), ctypes.c_float(0.04), None,
+                                                 h_q.data_ptr(), g_h.data_ptr(),
+                                                 torch.cuda.current_stream().cuda_stream)
+        assert st == 0, bl.last_error()
+
+    def bufs_for():
+        out = []
+        for x in xs:
+            M = x.shape[0]
+            out.append(dict(y=torch.empty((M, N), device=dev), q=torch.empty((M, K), dtype=torch.int8, device=dev),
+                            g=torch.empty(M, device=dev)))
+        out[-1].update(acc_gu=torch.empty((300, 2 * F), dtype=torch.int32, device=dev),
+                       hq=torch.empty((300, F), dtype=torch.int8, device=dev),
+                       gh=torch.empty(300, device=dev))
+        return out
+
+    ref = bufs_for()
+    run(ref)
+    torch.cuda.synchronize()
+    ref = [{k: host(v) for k, v in b.items()} for b in ref]
+    got = bufs_for()
+    s = torch.cuda.Stream(device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run(got)
+    for _ in range(3):
+        for b in got:
+            for v in b.values():
+                v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for b, r in zip(got, ref):
+            for k, v in b.items():
+                np.testing.assert_array_equal(host(v).view(np.uint8), r[k].view(np.uint8), err_msg=k)
