@@ -88,7 +88,6 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int cg = wv % CG, kp = wv / CG;
     const int j = lane & 15, g = lane >> 4;
     const int WR = K >> 4;          // 16-byte pieces per activation row (= 2-bit words per row)
-    const int WRW = ONEBIT ? (K >> 5) : WR;  // weight words per row
     const int nchunks = K >> 8;
     const int n_base = blockIdx.x * (16 * CT) + cg * 16 * NTW;
 
