@@ -70,8 +70,16 @@ bitlinear_status_t need(const char* fn, const char* name, const void* p, bool re
 hipError_t launch_forward_kernel(const int8_t* x_q, const float* gamma, int64_t M, int64_t K,
                                  const uint32_t* w_packed, int64_t N, float beta, float* y,
                                  int32_t* acc, int path, hipStream_t stream) {
-    if (path == BITLINEAR_PATH_AUTO)
-        path = (M == 1) ? BITLINEAR_PATH_GEMV : (M <= 32) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMM;
+    if (path == BITLINEAR_PATH_AUTO) {
+        // 17..32 tokens over at least 128 column tiles of 128 (N >= 16257) run
+        // the GEMM's 64-row tiles: K = 8192, N = 28672 at 17..32 tokens 28-30 us
+        // against 49-75 us on the skinny kernel; with fewer column tiles the
+        // skinny kernel keeps more CUs busy (K = 6912, N = 2560: 10-12 vs 21 us)
+        const bool wide_n = (N + 127) / 128 >= 128 && K % 256 == 0;
+        path = (M == 1) ? BITLINEAR_PATH_GEMV
+             : (M <= 16 || (M <= 32 && !wide_n)) ? BITLINEAR_PATH_SKINNY
+                                                  : BITLINEAR_PATH_GEMM;
+    }
     const int m = (int)M, n = (int)N, k = (int)K;
     switch (path) {
         case BITLINEAR_PATH_GEMV:

@@ -169,6 +169,8 @@ for _M in (1, 64, 100, 257):
         FWD_CASES.append(("gemm", _M, _N, _K))
 for _M in (1, 8, 31, 40, 96):
     FWD_CASES.append(("auto", _M, 777, 2112))
+# 17..32 tokens over >= 128 column tiles of 128 take the GEMM's 64-row tiles
+FWD_CASES += [("auto", 17, 16385, 256), ("auto", 32, 16400, 512), ("auto", 24, 16256, 768)]
 
 
 @pytest.mark.parametrize("path,M,N,K", FWD_CASES)
