@@ -122,6 +122,47 @@ def test_rmsnorm_quant(dev, M, K, gain_kind):
     assert_y_close(host(g), g_ref)
 
 
+def _near_half_integer_rows(K):
+    """Rows whose entries sit within 1e-7..2.5e-4 of a code boundary
+    (x / gamma * 128 near k + 0.5), the absmax first; and rows with a tiny
+    gamma, one of them subnormal."""
+    rng = workloads.rng_for(1400, K)
+    eps_set = np.array([0.0, 1e-7, -1e-7, 1e-6, -1e-6, 1e-5, -1e-5, 2.5e-5, -2.5e-5,
+                        1e-4, -1e-4, 2.4e-4, -2.4e-4])
+    rows = []
+    for g0 in (1.0, 3.0, 0.7071067, 123.456, 2.5e-3):
+        k = rng.integers(-128, 128, K - 1)
+        e = rng.choice(eps_set, K - 1)
+        x = np.clip((np.float64(np.float32(g0)) * (k + 0.5 + e) / 128.0).astype(np.float32),
+                    -np.float32(g0), np.float32(g0))
+        rows.append(np.concatenate([[np.float32(g0)], x]))
+    for g0 in (1e-35, 3e-39):
+        x = (np.float32(g0) * rng.uniform(-1, 1, K)).astype(np.float32)
+        x[0] = np.float32(g0)
+        rows.append(x)
+    return np.array(rows, np.float32)
+
+
+def test_quant_codes_near_half_integers(dev):
+    """Codes decided by the correctly rounded division at its hardest inputs,
+    in the row quantiser, the grouped quantiser and the fused one-token kernel."""
+    K = 4096
+    x = _near_half_integer_rows(K)
+    q_ref, g_ref = oracle.quant_act(x)
+    q, g = bl.quant_act(to_dev(x, dev))
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(host(g), g_ref)
+    qg_ref, gg_ref = oracle.quant_act_grouped(x, 4)
+    qg, gg = bl.quant_act_grouped(to_dev(x, dev), 4)
+    np.testing.assert_array_equal(host(qg), qg_ref)
+    np.testing.assert_array_equal(host(gg), gg_ref)
+    wp = gpu_pack(workloads.ternary(workloads.rng_for(1401), 300, K, workloads.TERNARY_UNIFORM), dev)
+    for r in range(x.shape[0]):
+        _, q1, g1 = bl.quant_forward(to_dev(x[r:r + 1], dev), wp, 0.25)
+        np.testing.assert_array_equal(host(q1)[0], q_ref[r])
+        assert host(g1)[0] == g_ref[r]
+
+
 def test_quant_empty_shapes(dev):
     q, g = bl.quant_act(torch.zeros((0, 64), device=dev))
     assert q.shape == (0, 64)
