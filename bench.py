@@ -88,7 +88,7 @@ def forward_kernel(M: int, K: int, N: int) -> str:
     if M == 1:
         return "gemv_valu_kernel"
     lds_fits = K % 256 == 0 and ((M * K + 1023) // 1024) * 1024 + 16384 + 128 <= 160 * 1024
-    if (5 <= M <= 16 or (2 <= M <= 4 and K >= 6144)) and lds_fits:
+    if (5 <= M <= 16 or (2 <= M <= 4 and K >= 4096)) and lds_fits:
         return "decode_lds_kernel"
     if M <= 16 or (M <= 32 and not (-(-N // 128) >= 128 and K % 256 == 0)):
         return "skinny_mfma_kernel"

@@ -328,13 +328,16 @@ int grouped_width(int tiles, int G, int nchunks) {
 template <bool ONEBIT>
 hipError_t launch_widths(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
                          int N, float beta, float* y, int32_t* acc, hipStream_t s) {
-    // widest workgroup that still leaves >= 160 workgroups (measured on
-    // N = 2560 .. 28672, K = 2560 .. 8192): fewer, wider groups copy the
-    // activation block fewer times, too few leave CUs idle
+    // widest workgroup that still leaves >= 200 workgroups: fewer, wider
+    // groups copy the activation block fewer times, too few leave CUs idle.
+    // Measured on N = 2560 .. 28672, K = 2560 .. 8192, 2 to 16 tokens: at
+    // K = 4096, N = 11008 (688 tiles) 344 workgroups of 2 tiles beat 172 of 4
+    // up to 8 tokens (M = 4: 6.5 vs 7.2 us; M = 8: 6.7 vs 7.2 us) and tie at
+    // 16; at K = 8192, N = 28672 224 groups of 8 tiles beat 448 of 4.
     const int tiles = (N + 15) / 16;
-    if (tiles >= 8 * 160) return launch_ct<8, 2, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    if (tiles >= 4 * 160) return launch_ct<4, 2, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    if (tiles >= 2 * 160) return launch_ct<2, 1, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (tiles >= 8 * 200) return launch_ct<8, 2, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (tiles >= 4 * 200) return launch_ct<4, 2, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (tiles >= 2 * 200) return launch_ct<2, 1, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     return launch_ct<1, 1, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
 

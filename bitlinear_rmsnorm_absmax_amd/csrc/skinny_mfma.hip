@@ -170,11 +170,12 @@ hipError_t launch_mt(const int8_t* xq, const float* gamma, int M, int K, const u
 hipError_t launch_skinny_mfma(const int8_t* xq, const float* gamma, int M, int K,
                               const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                               hipStream_t s) {
-    // 5..16 tokens, and 2..4 tokens at K >= 6144: the LDS-staged kernel
+    // 5..16 tokens, and 2..4 tokens at K >= 4096: the LDS-staged kernel
     // (measured on N x K = 11008 x 4096, 28672 x 8192, 6912 x 2560 and
-    // 2560 x 6912: at K = 8192 it takes 16 us for 2..4 tokens against 18..23 us
-    // here; at K <= 4096 this kernel is as fast or faster below 5 tokens)
-    if ((M >= 5 || (M >= 2 && K >= 6144)) && decode_lds_supports(M, K, N))
+    // 2560 x 2560: at K = 8192 it takes 16 us for 2..4 tokens against 18..23 us
+    // here, at K = 4096, N = 11008 6.1-6.6 us against 6.5-7.3 us; at K = 2560
+    // this kernel is as fast or faster below 5 tokens)
+    if ((M >= 5 || (M >= 2 && K >= 4096)) && decode_lds_supports(M, K, N))
         return launch_decode_lds(xq, gamma, M, K, wp, N, beta, y, acc, s);
     switch ((M + 15) / 16) {
         case 1: return launch_mt<1>(xq, gamma, M, K, wp, N, beta, y, acc, s);

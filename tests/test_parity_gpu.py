@@ -288,13 +288,16 @@ def test_gemm_wide_tiles_parity(dev, M, N, K):
     assert_y_close(y, y_ref)
 
 
-# The skinny path sends 5..16 tokens with K % 256 == 0 to the LDS-staged decode
-# kernel.  Cases cover its four workgroup widths (column tiles of 16: < 320,
-# >= 320, >= 640, >= 1280 tiles), ragged N, the largest K whose activation
-# block fits in LDS at 16 tokens (9216), and a zero token.
+# The skinny path sends 5..16 tokens (2..4 at K >= 4096) with K % 256 == 0 to
+# the LDS-staged decode kernel.  Cases cover its four workgroup widths (column
+# tiles of 16: < 400, >= 400, >= 800, >= 1600 tiles, and the old boundaries
+# 320, 640, 1280), ragged N, the largest K whose activation block fits in LDS
+# at 16 tokens (9216), and a zero token.
 DECODE_LDS_CASES = [(5, 1000, 256), (7, 5200, 512), (12, 10300, 1024), (16, 20500, 768),
                     (16, 333, 9216), (9, 2570, 2560), (13, 40, 4096), (6, 17, 256),
-                    (2, 3000, 8192), (3, 700, 6912), (4, 129, 6144)]
+                    (2, 3000, 8192), (3, 700, 6912), (4, 129, 6144),
+                    (8, 6401, 512), (11, 12800, 256), (9, 25700, 512), (4, 11008, 4096),
+                    (2, 6500, 4096), (3, 40, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_LDS_CASES)
