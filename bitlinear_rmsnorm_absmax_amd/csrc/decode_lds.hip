@@ -318,9 +318,9 @@ hipError_t launch_ct_groups(const int8_t* xq, const float* gamma, int M, int K, 
 // Grouped launches need KS % G == 0 and (K/256) % KS == 0 so that every wave's
 // K range lies inside one group.
 int grouped_width(int tiles, int G, int nchunks) {
-    const int ct[4] = {8, 4, 2, 1}, ks[4] = {2, 4, 4, 8}, min_tiles[4] = {8 * 160, 4 * 160, 2 * 160, 0};
+    const int ct[4] = {8, 4, 2, 1}, ks[4] = {2, 4, 4, 8}, min_tiles[4] = {8 * 200, 4 * 200, 2 * 200, 0};
     int pick = -1;
-    for (int i = 3; i >= 0; --i)  // the widest fitting config that still leaves >= 160 workgroups
+    for (int i = 3; i >= 0; --i)  // the widest fitting config that still leaves >= 200 workgroups
         if (ks[i] % G == 0 && nchunks % ks[i] == 0 && (pick < 0 || tiles >= min_tiles[i])) pick = i;
     return pick < 0 ? -1 : ct[pick];
 }
