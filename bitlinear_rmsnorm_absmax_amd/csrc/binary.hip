@@ -220,8 +220,9 @@ hipError_t launch_pack1(const int8_t* w, int64_t N, int64_t K, uint32_t* packed1
 
 hipError_t launch_forward1(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
                            int N, float beta, float* y, int32_t* acc, hipStream_t s) {
-    // 5..16 tokens: the LDS-staged MFMA decode kernel in its 1-bit form
-    if (M >= 5 && decode_lds_supports(M, K, N))
+    // 5..16 tokens, and 2..4 tokens at K >= 4096 (as for 2-bit weights): the
+    // LDS-staged MFMA decode kernel in its 1-bit form
+    if ((M >= 5 || (M >= 2 && K >= 4096)) && decode_lds_supports(M, K, N))
         return launch_decode_lds1(xq, gamma, M, K, wp, N, beta, y, acc, s);
     // else groups of up to four tokens on the vector ALUs, each a pass over the weights
     for (int m0 = 0; m0 < M; m0 += 4) {

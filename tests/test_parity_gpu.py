@@ -648,13 +648,15 @@ def test_pack_weights1_parity(dev):
     assert int(host(bad)[0]) == 2
 
 
-# 1..4 tokens and K % 256 != 0: vector-ALU kernel; 5..16 tokens with K % 256 == 0:
-# the LDS-staged MFMA kernel in its 1-bit form (all four workgroup widths);
-# 17 and 20 tokens: several vector-ALU passes
+# 1 token, 2..4 tokens below K = 4096, and K % 256 != 0: vector-ALU kernel;
+# 5..16 tokens (2..4 from K = 4096) with K % 256 == 0: the LDS-staged MFMA kernel
+# in its 1-bit form (all four workgroup widths); 17 and 20 tokens: several
+# vector-ALU passes
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (2, 17, 192), (3, 1000, 4096), (4, 333, 2560),
                                    (5, 640, 1024), (9, 100, 64), (1, 11008, 4096),
                                    (7, 5200, 512), (12, 10300, 1024), (16, 20500, 768),
-                                   (16, 333, 8192), (17, 200, 512), (20, 96, 320)])
+                                   (16, 333, 8192), (17, 200, 512), (20, 96, 320),
+                                   (4, 11008, 4096), (2, 6500, 8192), (3, 40, 4096)])
 def test_forward1_parity(dev, M, N, K):
     rng = workloads.rng_for(962, M, N, K)
     w = np.where(rng.random((N, K)) < 0.5, 1, -1).astype(np.int8)
