@@ -850,7 +850,17 @@ def test_pack3_counts_bad_entries(dev):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 1000), (4, 4096, 700), (16, 2560, 513), (3, 6912, 200),
-                                   (1, 16, 7), (5, 96, 33), (9, 1040, 100), (2, 8192, 300)])
+                                   (1, 16, 7), (5, 96, 33), (9, 1040, 100), (2, 8192, 300),
+                                   # one pass on MFMA with the activations staged in LDS:
+                                   # ragged K (not a multiple of 80 or 320) and N, a K of one
+                                   # 16-byte group, every tile width (N = 25600, 13000, 6912,
+                                   # 1000 pick 8, 4, 2, 1 tiles of 16 columns a workgroup), the
+                                   # largest staged block at 16 tokens (K = 8960) and the
+                                   # first K past it (back to the passes)
+                                   (6, 4096, 1000), (7, 16, 5), (8, 11008, 257), (11, 6912, 95),
+                                   (13, 2048, 31), (15, 4000, 64), (16, 8960, 70), (16, 8976, 70),
+                                   (3, 2048, 25600), (16, 4096, 13000), (4, 4096, 6912), (4, 4096, 11008),
+                                   (1, 2560, 6912), (2, 336, 17)])
 def test_forward3_parity(dev, M, K, N):
     rng = workloads.rng_for(981, M, K, N)
     x = rng.standard_normal((M, K)).astype(np.float32)
