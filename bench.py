@@ -83,6 +83,19 @@ def parse():
     return ap.parse_args()
 
 
+def forward1_kernel(M: int, K: int) -> str:
+    """The kernel bitlinear_forward1 runs for M tokens (its dispatch, for the
+    bench shapes: K % 256 == 0 and the activation block fits LDS)."""
+    return "decode_lds_kernel" if M >= 5 or (M >= 2 and K >= 4096) else "gemv1_kernel"
+
+
+def forward3_kernel(M: int, K: int) -> str:
+    """The kernel bitlinear_forward3 runs for M tokens (its dispatch)."""
+    steps = (-(-K // 80) + 3) // 4
+    fits = M * (20 * steps + 1) * 16 <= 144 * 1024
+    return "gemv3_mfma_kernel" if 2 <= M <= 16 and fits else "gemv3_kernel"
+
+
 def forward_kernel(M: int, K: int, N: int) -> str:
     """Kernel that bitlinear_forward picks (the library's dispatch)."""
     if M == 1:
@@ -623,7 +636,7 @@ def bench_binary(args, torch, bl, dev):
                    "weight_copies": len(copies), "timing": "hip_graph_per_step"},
         "roofline": dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, call=dom,
-                         kernel="decode_lds_kernel" if int(dom.split("M")[-1]) >= 5 else "gemv1_kernel",
+                         kernel=forward1_kernel(int(dom.split("M")[-1]), K),
                          avg_launch_us=d["avg_us"],
                          alg_bytes_per_launch=d["alg_bytes"]),
         "cpu_baseline": cpu,
@@ -887,7 +900,7 @@ def bench_base3(args, torch, bl, dev):
                    "timing": "hip_graph_of_all_timed_steps"},
         "roofline": dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, call=dom,
-                         kernel="gemv3_kernel", avg_launch_us=d["avg_us"],
+                         kernel=forward3_kernel(int(dom.split("M")[-1]), K), avg_launch_us=d["avg_us"],
                          alg_bytes_per_launch=d["alg_bytes"]),
         "cpu_baseline": cpu,
         "per_call": per_call,

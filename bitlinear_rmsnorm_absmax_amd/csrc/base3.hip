@@ -365,9 +365,10 @@ hipError_t launch_b3(const int8_t* xq, const float* gamma, int M, int K, const u
     return hipGetLastError();
 }
 
-// The widest CT that still leaves >= 160 workgroups (or CT = 1: measured at
-// K = 4096 N = 11008, 172 workgroups of 4 tiles beat 344 of 2 by 20 % and 86
-// of 8 by 30 %); a wave's
+// The widest CT <= 4 that still leaves >= 160 workgroups (or CT = 1):
+// measured at K = 4096 N = 11008, 172 workgroups of 4 tiles beat 344 of 2 by
+// 20 % and 86 of 8 by 30 %; at K = 8192 N = 28672, 448 of 4 beat 224 of 8 by
+// 6 % (two waves a tile split its steps).  A wave's
 // steps in one batch when it has at most 4, else a stream of 2-step batches.
 template <int CT>
 hipError_t launch_b3_ct(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
@@ -381,7 +382,6 @@ hipError_t launch_b3_ct(const int8_t* xq, const float* gamma, int M, int K, cons
 hipError_t launch_gemv3_mfma(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
                              int N, float beta, float* y, int32_t* acc, hipStream_t s) {
     const int64_t tiles = (N + 15) / 16;
-    if ((tiles + 7) / 8 >= 160) return launch_b3_ct<8>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     if ((tiles + 3) / 4 >= 160) return launch_b3_ct<4>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     if ((tiles + 1) / 2 >= 160) return launch_b3_ct<2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     return launch_b3_ct<1>(xq, gamma, M, K, wp, N, beta, y, acc, s);

@@ -853,8 +853,8 @@ def test_pack3_counts_bad_entries(dev):
                                    (1, 16, 7), (5, 96, 33), (9, 1040, 100), (2, 8192, 300),
                                    # one pass on MFMA with the activations staged in LDS:
                                    # ragged K (not a multiple of 80 or 320) and N, a K of one
-                                   # 16-byte group, every tile width (N = 25600, 13000, 6912,
-                                   # 1000 pick 8, 4, 2, 1 tiles of 16 columns a workgroup), the
+                                   # 16-byte group, every tile width (N = 13000, 6912, 1000
+                                   # pick 4, 2, 1 tiles of 16 columns a workgroup), the
                                    # largest staged block at 16 tokens (K = 8960) and the
                                    # first K past it (back to the passes)
                                    (6, 4096, 1000), (7, 16, 5), (8, 11008, 257), (11, 6912, 95),
