@@ -5,7 +5,8 @@
 // h = SiLU(gate) * up followed by the same quantisation (datacamp article,
 // MatMul-vrije GLU).
 //
-// One workgroup of 256 threads per token row.  A row is split into 16-element
+// One workgroup of 256 threads per token row (512 for the SiLU rows longer
+// than 4096 elements).  A row is split into 16-element
 // chunks (K % 16 == 0) dealt round-robin to the threads, so each load and
 // each 16-byte code store is contiguous across the wave.  The first
 // kQuantCache chunks of every thread stay in registers between the absmax
@@ -36,8 +37,11 @@ __device__ __forceinline__ void store_codes(int8_t* q, int64_t row, int K, int c
 
 // RMS: gain applied before the absmax (u = g * x), sum of x^2 in float64.
 // H_OUT: also write the fp32 values being quantised (the SiLU*up product).
-template <Src S, bool RMS, bool H_OUT>
-__global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
+// THREADS: kQuantThreads, or wider for rows without RMSNorm (their only
+// reduction is a max, exact in any order, so gamma and the codes do not
+// depend on how the chunks are dealt).
+template <Src S, bool RMS, bool H_OUT, int THREADS = kQuantThreads>
+__global__ __launch_bounds__(THREADS) void quant_rows_kernel(
     RowSrc src, int K, const float* __restrict__ gain, float eps, float* __restrict__ h_out,
     int8_t* __restrict__ q, float* __restrict__ gamma_out) {
     const int64_t row = blockIdx.x;
@@ -74,14 +78,14 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
 
 #pragma unroll
     for (int i = 0; i < kQuantCache; ++i) {
-        int c = threadIdx.x + i * kQuantThreads;
+        int c = threadIdx.x + i * THREADS;
         if (c < nchunk) prepare(c, cache[i]);
     }
-    for (int c = threadIdx.x + kQuantCache * kQuantThreads; c < nchunk; c += kQuantThreads) {
+    for (int c = threadIdx.x + kQuantCache * THREADS; c < nchunk; c += THREADS) {
         float v[16];
         prepare(c, v);
     }
-    block_reduce(amax, ss, RMS);
+    block_reduce<THREADS / kWave>(amax, ss, RMS);
 
     float gamma = amax;
     if constexpr (RMS) {
@@ -92,10 +96,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
 
 #pragma unroll
     for (int i = 0; i < kQuantCache; ++i) {
-        int c = threadIdx.x + i * kQuantThreads;
+        int c = threadIdx.x + i * THREADS;
         if (c < nchunk) store_codes(q, row, K, c, cache[i], amax);
     }
-    for (int c = threadIdx.x + kQuantCache * kQuantThreads; c < nchunk; c += kQuantThreads) {
+    for (int c = threadIdx.x + kQuantCache * THREADS; c < nchunk; c += THREADS) {
         float v[16];
         load_chunk<S>(src, row, K, c, v);
         if constexpr (RMS) {
@@ -230,6 +234,17 @@ hipError_t launch_silu_mul_quant(const float* gate, const float* up, int64_t M, 
     }
     RowSrc src{gate, up};
     dim3 grid((unsigned)M), block(kQuantThreads);
+    if (F / 16 > kQuantThreads) {
+        // wider rows: one 16-element chunk per thread up to 8192 elements (the
+        // float64 SiLU is the bulk of the work; more waves hide its latency)
+        if (h)
+            quant_rows_kernel<Src::SILU_MUL, false, true, 2 * kQuantThreads>
+                <<<grid, dim3(2 * kQuantThreads), 0, s>>>(src, (int)F, nullptr, 0.f, h, h_q, gamma);
+        else
+            quant_rows_kernel<Src::SILU_MUL, false, false, 2 * kQuantThreads>
+                <<<grid, dim3(2 * kQuantThreads), 0, s>>>(src, (int)F, nullptr, 0.f, nullptr, h_q, gamma);
+        return hipGetLastError();
+    }
     if (h)
         quant_rows_kernel<Src::SILU_MUL, false, true><<<grid, block, 0, s>>>(src, (int)F, nullptr, 0.f, h, h_q, gamma);
     else
@@ -247,6 +262,17 @@ hipError_t launch_silu_mul_quant_acc(const int32_t* acc_gu, const float* gamma_i
     }
     RowSrc src{acc_gu, nullptr, gamma_in, beta_gate, beta_up};
     dim3 grid((unsigned)M), block(kQuantThreads);
+    if (F / 16 > kQuantThreads) {
+        // wider rows: one 16-element chunk per thread up to 8192 elements (the
+        // float64 SiLU is the bulk of the work; more waves hide its latency)
+        if (h)
+            quant_rows_kernel<Src::SILU_ACC, false, true, 2 * kQuantThreads>
+                <<<grid, dim3(2 * kQuantThreads), 0, s>>>(src, (int)F, nullptr, 0.f, h, h_q, gamma);
+        else
+            quant_rows_kernel<Src::SILU_ACC, false, false, 2 * kQuantThreads>
+                <<<grid, dim3(2 * kQuantThreads), 0, s>>>(src, (int)F, nullptr, 0.f, nullptr, h_q, gamma);
+        return hipGetLastError();
+    }
     if (h)
         quant_rows_kernel<Src::SILU_ACC, false, true><<<grid, block, 0, s>>>(src, (int)F, nullptr, 0.f, h, h_q, gamma);
     else

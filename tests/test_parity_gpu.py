@@ -475,6 +475,29 @@ def test_glu_stagewise(dev, M):
           f"h_q codes differ at {int((diff != 0).sum())}")
 
 
+@pytest.mark.parametrize("F", [16, 4096, 4112, 6912, 16384, 20000])
+def test_silu_quant_row_widths(dev, F):
+    """SiLU(gate) * up and its quantisation across the row widths of the
+    quantiser: 256 threads up to 4096 elements, 512 beyond (one chunk per
+    thread up to 8192, values kept in registers up to 16384, re-read past
+    that).  h agrees with the oracle's float64 product rounded to fp32 within
+    one ulp (the device and host exp may differ in the last bit); the codes
+    and gamma are exact on the device's own h."""
+    rng = workloads.rng_for(1990, F)
+    M = 3
+    gate = (3.0 * rng.standard_normal((M, F))).astype(np.float32)
+    up = rng.standard_normal((M, F)).astype(np.float32)
+    gate[1, F // 2] = 40.0  # a large product sets gamma of row 1
+    h_q, g, h = bl.silu_mul_quant(to_dev(gate, dev), to_dev(up, dev), want_h=True)
+    h = host(h)
+    h_ref = oracle.silu_mul(gate, up).astype(np.float32)
+    ulp = np.spacing(np.abs(h_ref)).astype(np.float64)
+    assert (np.abs(h.astype(np.float64) - h_ref.astype(np.float64)) <= ulp).all()
+    q_ref, g_ref = oracle.quant_act(h)
+    np.testing.assert_array_equal(host(h_q), q_ref)
+    np.testing.assert_array_equal(host(g).view(np.uint32), g_ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("M", [1, 33, 512])
 def test_glu_stacked_matches_stagewise(dev, M):
     """Gate and up as one product on the stacked weights [W_gate; W_up] that
