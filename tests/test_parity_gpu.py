@@ -202,6 +202,11 @@ FWD_CASES = []
 for _M in (1, 2, 3, 4):
     for _N, _K in ((1, 16), (17, 48), (1000, 1040), (2048, 2048), (300, 4096)):
         FWD_CASES.append(("gemv", _M, _N, _K))
+# few rows over long K: the vector GEMV splits each row group's units over 2
+# or 4 waves (ragged and unaligned rows, a last slice with a single unit)
+for _M in (1, 3):
+    for _N, _K in ((300, 4112), (2560, 6912), (100, 16400), (5, 12288), (7, 12352)):
+        FWD_CASES.append(("gemv", _M, _N, _K))
 for _M in (1, 5, 16, 17, 33, 64):
     for _N, _K in ((1, 16), (17, 48), (1000, 1040), (2048, 2048), (300, 4160)):
         FWD_CASES.append(("skinny", _M, _N, _K))
