@@ -312,10 +312,17 @@ def build_plan(args, torch, bl, dev):
 
 # ----------------------------------------------------------------------------- traffic
 
+# The sources of the calls whose traffic is recorded (the decode step: the
+# quantiser, the fused one-token call, the skinny dispatch and the LDS decode
+# kernel) with the shared headers and the ABI's dispatch.
+TRAFFIC_SOURCES = ("api.cpp", "device_common.h", "internal.h", "quant_rows.h", "quant_act.hip",
+                   "quant_gemv.hip", "skinny_mfma.hip", "decode_lds.hip", "gemv_valu.hip")
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bitlinear_rmsnorm_absmax_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in TRAFFIC_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
