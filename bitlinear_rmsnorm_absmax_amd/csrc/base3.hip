@@ -352,13 +352,10 @@ __global__ __launch_bounds__(kB3Waves * kWave) void gemv3_mfma_kernel(
 template <int CT, int BATCH>
 hipError_t launch_b3(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
                      float beta, float* y, int32_t* acc, hipStream_t s) {
-    static bool attr_set = false;  // per-kernel opt-in to more than 64 KB of dynamic LDS
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv3_mfma_kernel<CT, BATCH>),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kB3ActMax);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static DynLdsOptIn opt_in;
+    const hipError_t e =
+        opt_in.ensure(reinterpret_cast<const void*>(&gemv3_mfma_kernel<CT, BATCH>), kB3ActMax);
+    if (e != hipSuccess) return e;
     const int blocks = (N + 16 * CT - 1) / (16 * CT);
     gemv3_mfma_kernel<CT, BATCH><<<dim3(blocks), dim3(kB3Waves * kWave), b3_act_bytes(M, K), s>>>(
         xq, gamma, M, K, reinterpret_cast<const v4u*>(wp), N, beta, y, acc);

@@ -271,14 +271,10 @@ size_t decode_lds_bytes(int M, int K, int ntw, int G = 1) {
 template <int CT, int NTW, int B, bool ONEBIT, int G>
 hipError_t launch_ctb(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
                       float beta, float* y, int32_t* acc, hipStream_t s, const float* beta_g) {
-    static bool attr_set = false;  // per-kernel opt-in to more than 64 KB of dynamic LDS
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT, G>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, kDecLdsMax);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static DynLdsOptIn opt_in;
+    const hipError_t e = opt_in.ensure(
+        reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT, G>), kDecLdsMax);
+    if (e != hipSuccess) return e;
     const int blocks = (N + 16 * CT - 1) / (16 * CT);
     decode_lds_kernel<CT, NTW, B, ONEBIT, G><<<dim3(blocks), dim3(kDecWaves * kWave),
                                                decode_lds_bytes(M, K, NTW, G), s>>>(

@@ -5,7 +5,31 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace bl {
+
+// Opt-in of one kernel to more than 64 KB of dynamic LDS, made once per
+// device (the attribute belongs to the calling thread's current device, the
+// device of the launch's stream in the usual setup).  One object per kernel
+// (a function-local static of its launcher); concurrent first calls may both
+// set the attribute, which is idempotent.
+class DynLdsOptIn {
+  public:
+    hipError_t ensure(const void* kernel, int bytes) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < kMaxDevices && done_[dev].load(std::memory_order_acquire)) return hipSuccess;
+        e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done_[dev].store(true, std::memory_order_release);
+        return e;
+    }
+
+  private:
+    static constexpr int kMaxDevices = 64;
+    std::atomic<bool> done_[kMaxDevices] = {};
+};
 
 // Every launcher validates nothing (api.cpp does) and returns the launch
 // status (hipGetLastError after the launch).
