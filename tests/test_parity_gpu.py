@@ -995,7 +995,14 @@ QFWD_CASES = [(1, 64, 1, "f32", None), (1, 2048, 1000, "bf16", "unit"),
               (1, 512, 8193, "f32", "unit"), (1, 512, 16384, "f32", None),
               (1, 256, 16385, "f32", None),
               (1, 16448, 40, "f32", None), (1, 1040, 77, "bf16", "rand"),
-              (3, 4096, 500, "bf16", "rand"), (16, 2560, 700, "f32", None)]
+              (3, 4096, 500, "bf16", "rand"), (16, 2560, 700, "f32", None),
+              # 2..4 tokens on the LDS decode route (K >= 4096) at every tile
+              # width (N = 1000, 11008, 13000, 25600 pick 1, 2, 4, 8 tiles of
+              # 16 columns), one output column, and K = 3840 (skinny kernel)
+              (2, 4096, 1000, "f32", None), (4, 4096, 11008, "f32", None),
+              (3, 4096, 13000, "bf16", None), (2, 8192, 25600, "bf16", None),
+              (4, 4096, 1, "f32", None), (3, 5120, 77, "f32", None),
+              (3, 5632, 300, "f32", None), (4, 3840, 500, "f32", None)]
 
 
 @pytest.mark.parametrize("M,K,N,dt,gain_kind", QFWD_CASES)
@@ -1003,6 +1010,9 @@ def test_quant_forward_parity(dev, M, K, N, dt, gain_kind):
     act = "normal_bf16" if dt == "bf16" else "normal_f32"
     x, w, beta = workloads.random_case(1100 + K + N, M, N, K, act=act,
                                        table=workloads.TERNARY_HALF_ZERO)
+    if M >= 3:
+        x = x.copy()
+        x[1] = 0  # a zero token: gamma = 0, codes 0
     xf = oracle.bf16_to_f32(x) if dt == "bf16" else x
     xd = to_dev(x, dev, torch.bfloat16) if dt == "bf16" else to_dev(x, dev)
     rng = workloads.rng_for(1101, K)
