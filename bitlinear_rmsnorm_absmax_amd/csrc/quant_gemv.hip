@@ -11,8 +11,9 @@
 // first kQuantThreads threads (the quantiser's own layout); a workgroup of
 // WAVES waves multiplies WAVES * R rows, so wider workgroups repeat the
 // quantisation fewer times:
-//   1. each wave queues the loads of its first weight units, so the weight
-//      stream is in flight during the quantisation;
+//   1. the quantiser threads issue the loads of the row's first chunks, then
+//      (after a barrier) each wave queues the loads of its first weight units,
+//      so the weight stream is in flight during the quantisation;
 //   2. absmax (and the float64 sum of squares) over the row in the chunking
 //      and reduction order of quant_rows_kernel: the codes and gamma are
 //      bit-identical to bitlinear_quant_act's;
@@ -60,41 +61,60 @@ __global__ __launch_bounds__(WAVES * kWave) void quant_gemv_kernel(
     const int units = WR >> 2;   // 16-byte units per row (K % 64 == 0)
     const uint32_t* wrow = wp + (int64_t)n0 * WR;
 
-    // weight unit u of the wave's rows; rows past N read as zero codes
+    // weight unit u of the wave's rows; rows past N and units past the row
+    // read as zero codes.  The loads are unconditional (clamped onto the last
+    // row / unit, then zeroed), so the compiler counts them exactly and waits
+    // for the row chunks issued before them without waiting for them.
     auto load_unit = [&](int u, uint32_t (&w)[R][4]) {
+        const int uc = min(u, units - 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if (u < units && n0 + r < N) {
-                const v4u v = __builtin_nontemporal_load(
-                    reinterpret_cast<const v4u*>(wrow + (uint32_t)(r * WR + 4 * u)));
-                w[r][0] = v.x; w[r][1] = v.y; w[r][2] = v.z; w[r][3] = v.w;
-            } else {
-                w[r][0] = w[r][1] = w[r][2] = w[r][3] = 0u;
-            }
+            const int64_t rc = (int64_t)min(n0 + r, N - 1) - n0;
+            const v4u v = __builtin_nontemporal_load(
+                reinterpret_cast<const v4u*>(wrow + rc * WR + 4 * uc));
+            const bool ok = u < units && n0 + r < N;
+            w[r][0] = ok ? v.x : 0u; w[r][1] = ok ? v.y : 0u;
+            w[r][2] = ok ? v.z : 0u; w[r][3] = ok ? v.w : 0u;
         }
     };
+    // absmax (+ sum of squares) exactly as the quantiser's pass over row 0.
+    // The row's first chunks (and their gains) are loaded before any weight
+    // load is issued: a compute unit returns loads in issue order, so the
+    // quantisation then runs while the weights stream in, instead of after.
+    const int nchunk = K / 16;
+    float cache[kQuantCache][16];
+    float gcache[RMS ? kQuantCache : 1][16];
+    auto load_gain = [&](int c, float g16[16]) {
+        const float4* pg = reinterpret_cast<const float4*>(gain + (int64_t)c * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 g = pg[i];
+            g16[4 * i] = g.x; g16[4 * i + 1] = g.y; g16[4 * i + 2] = g.z; g16[4 * i + 3] = g.w;
+        }
+    };
+    if (quantiser) {
+#pragma unroll
+        for (int i = 0; i < kQuantCache; ++i) {
+            const int c = tid + i * kQuantThreads;
+            if (c < nchunk) {
+                load_chunk<S>(src, 0, K, c, cache[i]);
+                if constexpr (RMS) load_gain(c, gcache[i]);
+            }
+        }
+    }
+    __syncthreads();  // every wave's weight loads queue behind the row's
     uint32_t wcur[R][4];
     load_unit(lane, wcur);
 
-    // absmax (+ sum of squares) exactly as the quantiser's pass over row 0
-    const int nchunk = K / 16;
-    float cache[kQuantCache][16];
     float amax = 0.0f;
     double ss = 0.0;
-    auto prepare = [&](int c, float v[16]) {
-        load_chunk<S>(src, 0, K, c, v);
+    auto process = [&](float v[16], const float g16[16]) {
         if constexpr (RMS) {
-            const float4* pg = reinterpret_cast<const float4*>(gain + (int64_t)c * 16);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 g = pg[i];
-                const float gg[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float xv = v[4 * i + j];
-                    ss += (double)xv * (double)xv;
-                    v[4 * i + j] = gg[j] * xv;
-                }
+            for (int e = 0; e < 16; ++e) {
+                const float xv = v[e];
+                ss += (double)xv * (double)xv;
+                v[e] = g16[e] * xv;
             }
         }
 #pragma unroll
@@ -104,11 +124,13 @@ __global__ __launch_bounds__(WAVES * kWave) void quant_gemv_kernel(
 #pragma unroll
         for (int i = 0; i < kQuantCache; ++i) {
             const int c = tid + i * kQuantThreads;
-            if (c < nchunk) prepare(c, cache[i]);
+            if (c < nchunk) process(cache[i], gcache[RMS ? i : 0]);
         }
         for (int c = tid + kQuantCache * kQuantThreads; c < nchunk; c += kQuantThreads) {
-            float v[16];
-            prepare(c, v);
+            float v[16], g16[16];
+            load_chunk<S>(src, 0, K, c, v);
+            if constexpr (RMS) load_gain(c, g16);
+            process(v, g16);
         }
     }
     block_reduce<kQWaves>(amax, ss, RMS);
