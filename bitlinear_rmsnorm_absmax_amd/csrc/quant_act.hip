@@ -39,9 +39,11 @@ __device__ __forceinline__ void store_codes(int8_t* q, int64_t row, int K, int c
 // H_OUT: also write the fp32 values being quantised (the SiLU*up product).
 // THREADS: kQuantThreads, or wider for rows without RMSNorm (their only
 // reduction is a max, exact in any order, so gamma and the codes do not
-// depend on how the chunks are dealt).
+// depend on how the chunks are dealt).  Plain fp32 / bf16 rows are held to
+// 64 VGPRs (8 waves a SIMD), so 2048 rows of 256 threads run in one round
+// (bf16, K = 4096: 68 -> 56 VGPRs, 7.05 -> 6.88 us).
 template <Src S, bool RMS, bool H_OUT, int THREADS = kQuantThreads>
-__global__ __launch_bounds__(THREADS) void quant_rows_kernel(
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu((S == Src::F32 || S == Src::BF16) && !RMS ? 8 : 1))) void quant_rows_kernel(
     RowSrc src, int K, const float* __restrict__ gain, float eps, float* __restrict__ h_out,
     int8_t* __restrict__ q, float* __restrict__ gamma_out) {
     const int64_t row = blockIdx.x;
