@@ -242,14 +242,15 @@ WIDE_GEMM_CASES = [(257, 22053, 128), (256, 32769, 256), (300, 22016, 384), (384
 
 
 # At most 256 tiles of 64 x 128 and K % 256 == 0: 64-row tiles with two K
-# groups per workgroup (ragged M, a last row tile with one row, ragged N).
+# groups per workgroup (ragged M, a last row tile with one row, ragged N);
+# K >= 4608 in a multiple of 3 steps of 128: three K groups.
 SMALL_TILE_GEMM_CASES = [(64, 3000, 2560), (65, 1000, 768), (96, 2000, 1536), (300, 700, 1536),
-                         (512, 257, 256)]
+                         (512, 257, 256), (65, 300, 9216), (100, 1000, 4608), (300, 1536, 6912)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL_TILE_GEMM_CASES)
 def test_gemm_small_tiles_parity(dev, M, N, K):
-    assert -(-M // 64) * -(-N // 128) <= 256 and K % 256 == 0
+    assert -(-M // 64) * -(-N // 128) <= 256 and (K % 256 == 0 or K % 384 == 0)
     x, w, beta = workloads.random_case(950 + M + K, M, N, K, table=workloads.TERNARY_HALF_ZERO)
     x = x.copy()
     x[M - 1] = 0.0  # zero token in the last row tile
