@@ -110,7 +110,7 @@ def forward_kernel(M: int, K: int, N: int) -> str:
     if M >= 256 and -(-M // 128) * -(-N // 256) >= 256:
         return "gemm_pipe_kernel"   # 128 x 256 tiles
     if -(-M // 64) * -(-N // 128) <= 256 and K % 256 == 0:
-        return "gemm_dma_kernel"    # 64 x 128 tiles, two K groups
+        return "gemm_dma_kernel"    # 64 x 128 tiles, two or three K groups
     return "gemm_pipe_kernel"       # 128 x 128 tiles
 
 

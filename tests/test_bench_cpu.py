@@ -95,3 +95,32 @@ def test_traffic_summary_rejects_a_run_without_the_copy(tmp_path, monkeypatch):
                               workload=1))()
     with pytest.raises(SystemExit):
         bench.traffic_write(args)
+
+
+def test_kernel_labels_follow_the_dispatch():
+    """The roofline line names the kernel the library's dispatch picks."""
+    bench = load_bench()
+    # 1-bit: the LDS decode kernel from 5 tokens, and from 2 at K >= 4096
+    assert bench.forward1_kernel(16, 4096) == "decode_lds_kernel"
+    assert bench.forward1_kernel(4, 4096) == "decode_lds_kernel"
+    assert bench.forward1_kernel(4, 2048) == "gemv1_kernel"
+    assert bench.forward1_kernel(1, 8192) == "gemv1_kernel"
+    # base-3: one pass on MFMA for 2..16 tokens whose staged block fits
+    # 144 KB (16 tokens: K = 8960 fits, K = 8976 does not)
+    assert bench.forward3_kernel(16, 8960) == "gemv3_mfma_kernel"
+    assert bench.forward3_kernel(16, 8976) == "gemv3_kernel"
+    assert bench.forward3_kernel(1, 4096) == "gemv3_kernel"
+    assert bench.forward3_kernel(2, 4096) == "gemv3_mfma_kernel"
+    assert bench.forward3_kernel(17, 1024) == "gemv3_kernel"
+    # 2-bit: GEMV for one token, the LDS decode kernel at decode sizes, GEMM
+    assert bench.forward_kernel(1, 4096, 11008) == "gemv_valu_kernel"
+    assert bench.forward_kernel(16, 4096, 11008) == "decode_lds_kernel"
+
+
+def test_traffic_digest_covers_existing_sources():
+    bench = load_bench()
+    csrc = os.path.join(ROOT, "bitlinear_rmsnorm_absmax_amd", "csrc")
+    for f in bench.TRAFFIC_SOURCES:
+        assert os.path.exists(os.path.join(csrc, f)), f
+    d = bench.kernel_source_digest()
+    assert len(d) == 16 and d == bench.kernel_source_digest()
