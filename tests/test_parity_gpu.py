@@ -1127,3 +1127,48 @@ def test_graph_replays_match_eager(dev):
         for b, r in zip(got, ref):
             for k, v in b.items():
                 np.testing.assert_array_equal(host(v).view(np.uint8), r[k].view(np.uint8), err_msg=k)
+
+
+def test_graph_replays_widened_paths(dev):
+    """The widened products captured in one HIP graph -- base-3 on MFMA (16
+    tokens), 1-bit on the LDS decode kernel, the grouped decode (G = 4), the
+    vector GEMV with K split over two waves, the GEMM with three K groups:
+    each of three replays (outputs cleared and synchronised in between)
+    reproduces the eager outputs bit for bit."""
+    rng = workloads.rng_for(1310)
+    K, N = 4096, 700
+    w = workloads.ternary(rng, N, K, workloads.TERNARY_UNIFORM)
+    p3, _ = bl.pack_weights3(to_dev(w, dev))
+    p1, _ = bl.pack_weights1(to_dev(np.where(w >= 0, 1, -1).astype(np.int8), dev))
+    pg = pack_grouped(w, 4, dev)
+    beta_g = to_dev(np.array([0.02, 0.03, 0.04, 0.05], np.float32), dev)
+    q16, g16 = bl.quant_act(to_dev(rng.standard_normal((16, K)).astype(np.float32), dev))
+    qg, gg = bl.quant_act_grouped(to_dev(rng.standard_normal((16, K)).astype(np.float32), dev), 4)
+    w_long = gpu_pack(workloads.ternary(rng, 2560, 6912, workloads.TERNARY_HALF_ZERO), dev)
+    q1, g1 = bl.quant_act(to_dev(rng.standard_normal((1, 6912)).astype(np.float32), dev))
+    w_k3 = gpu_pack(workloads.ternary(rng, 1000, 4608, workloads.TERNARY_UNIFORM), dev)
+    qm, gm = bl.quant_act(to_dev(rng.standard_normal((100, 4608)).astype(np.float32), dev))
+
+    def run():
+        return [bl.forward3(q16, g16, p3, 0.02, want_acc=True),
+                bl.forward1(q16, g16, p1, 0.02, want_acc=True),
+                bl.forward_grouped(qg, gg, pg, beta_g),
+                bl.forward(q1, g1, w_long, 0.02, want_acc=True),
+                bl.forward(qm, gm, w_k3, 0.02, path=bl.PATH_GEMM, want_acc=True)]
+
+    ref = [[host(t) for t in outs] for outs in run()]
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        got = run()
+    for _ in range(3):
+        for outs in got:
+            for t in outs:
+                t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for outs, r in zip(got, ref):
+            for t, rt in zip(outs, r):
+                np.testing.assert_array_equal(host(t).view(np.uint8), rt.view(np.uint8))
