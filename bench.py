@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the ternary BitLinear hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--configs 1,2,3,4]
 
 A step is one pass of the path over one batch of synthetic input: for every
 token count M of the workload, the activation quantisation
@@ -14,10 +14,16 @@ Inputs are seeded synthetic draws (workloads.py), resident in HBM before the
 timed region.  The packed weights rotate through at least 512 MB of copies so
 that consecutive steps cannot be served from the 256 MB Infinity Cache.
 The K timed steps are one replay of a HIP graph holding all K of them, so
-host launch overhead does not pace the GPU.  Per-call kernel durations come from a second
-pass: for each call of the step, a HIP graph of that call alone, once per
-weight copy, replayed between two HIP events on the stream the kernels run on;
-the dominant forward call gives the roofline.
+host launch overhead does not pace the GPU.  Per-call durations come from two
+further passes: the back-to-back time (a HIP graph of that call alone, once
+per weight copy, replayed between two events), and per-launch durations (each
+launch between two events on the stream it runs on, all queued behind a spin
+kernel so that they run back to back): mean, median, p10 and p90.  The
+dominant forward call's mean per-launch duration gives the roofline; the
+floors are an empty launch and a read-only pass over the same weight bytes.
+The headline workload is the large-shape sweep (K=8192, N=28672, M in
+{1, 8, 64, 512}); the other four workloads are measured the same way into the
+line's "configs" record.
 
 Prints ONE JSON line.
 """
@@ -50,9 +56,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--workload", type=int, default=5, choices=sorted(workloads.WORKLOADS),
+                    help="the headline workload (default 5: the large-shape sweep K=8192 "
+                         "N=28672, M in {1, 8, 64, 512}, the largest that fits one GPU)")
+    ap.add_argument("--configs", default="1,2,3,4",
+                    type=lambda v: [] if v in ("", "none") else [int(c) for c in v.split(",")],
+                    help="workloads measured as sub-records under 'configs' (none: skip)")
+    ap.add_argument("--sub-steps", type=int, default=50, help="timed steps of each sub-record")
+    ap.add_argument("--per-launch", type=int, default=50,
+                    help="event-bracketed launches per call for the per-launch statistics")
     ap.add_argument("--no-rotate", action="store_true", help="one weight copy (warm cache)")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graphs")
     ap.add_argument("--unfused", action="store_true",
@@ -134,30 +148,6 @@ class RunAll:
         return True
 
 
-class RunOne:
-    """Runs only the call `name`; the first run records the start event."""
-
-    def __init__(self, torch, name):
-        self.torch = torch
-        self.name = name
-        self.e0 = torch.cuda.Event(enable_timing=True)
-        self.e1 = torch.cuda.Event(enable_timing=True)
-        self.started = False
-
-    def __call__(self, name, *a, **kw):
-        if name != self.name:
-            return False
-        if not self.started:
-            self.e0.record(self.torch.cuda.current_stream())
-            self.started = True
-        return True
-
-    def avg_us(self, launches):
-        self.e1.record(self.torch.cuda.current_stream())
-        self.torch.cuda.synchronize()
-        return self.e0.elapsed_time(self.e1) * 1e3 / launches
-
-
 # ----------------------------------------------------------------------------- plan
 
 class Layer:
@@ -174,9 +164,8 @@ class Layer:
             self.copies += [packed.clone() for _ in range(n - 1)]
 
 
-def build_plan(args, torch, bl, dev):
+def build_plan(args, torch, bl, dev, wid):
     """Returns (ops, meta, keepalive): ops(step_idx, timer) launches one step."""
-    wid = args.workload
     wl = workloads.WORKLOADS[wid]
     rotate = not args.no_rotate
     lib = bl.lib
@@ -312,17 +301,18 @@ def build_plan(args, torch, bl, dev):
 
 # ----------------------------------------------------------------------------- traffic
 
-# The sources of the calls whose traffic is recorded (the decode step: the
-# quantiser, the fused one-token call, the skinny dispatch and the LDS decode
-# kernel) with the shared headers and the ABI's dispatch.
-TRAFFIC_SOURCES = ("api.cpp", "device_common.h", "internal.h", "quant_rows.h", "quant_act.hip",
-                   "quant_gemv.hip", "skinny_mfma.hip", "decode_lds.hip", "gemv_valu.hip")
+# The traffic summaries are valid only for the kernel sources they were taken
+# on: every source file of the library (kernels, shared headers, the ABI's
+# dispatch) enters the digest.
+def _library_sources():
+    csrc = os.path.join(ROOT, "bitlinear_rmsnorm_absmax_amd", "csrc")
+    return sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp")))
 
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bitlinear_rmsnorm_absmax_amd", "csrc")
-    for f in TRAFFIC_SOURCES:
+    for f in _library_sources():
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -443,54 +433,77 @@ def traffic_write(args):
 
 # ----------------------------------------------------------------------------- cpu baseline
 
-def cpu_baseline(args, seconds: float):
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wid: int, seconds: float, threads: int = 0):
     """The oracle (plain C loops, OpenMP over outputs) on the same workload,
-    whole steps, for about ``seconds`` of CPU time."""
+    whole steps, for about ``seconds`` of CPU time; ``threads`` > 0 pins the
+    oracle's thread count (1: the one-core timing), 0 leaves it at the
+    host's cores."""
     import oracle
-    wid = args.workload
     wl = workloads.WORKLOADS[wid]
-    if wl.glu_f:
-        wg, wu, wd = workloads.glu_weights(wid)
-        betas = workloads.glu_betas(wid)
-        gain = np.ones(wl.K, np.float32)
-        xs = [workloads.workload_activations(wid, M) for M in wl.ms]
-        wbytes = (wg.size + wu.size + wd.size) // 4 * len(wl.ms)
+    default_threads = oracle.num_threads()
+    if threads > 0:
+        oracle.set_num_threads(threads)
+    try:
+        nthr = oracle.num_threads()
+        if wl.glu_f:
+            wg, wu, wd = workloads.glu_weights(wid)
+            betas = workloads.glu_betas(wid)
+            gain = np.ones(wl.K, np.float32)
+            ms = list(wl.ms) if threads != 1 else [m for m in wl.ms if m == 1]
+            xs = [workloads.workload_activations(wid, M) for M in ms]
+            wbytes = (wg.size + wu.size + wd.size) // 4 * len(ms)
 
-        def step():
-            for x in xs:
-                oracle.glu(x, wg, wu, wd, betas, gain, wl.rms_eps)
-        desc = "GLU chain"
-    else:
-        w = workloads.workload_weights(wid)
-        beta = workloads.workload_beta(wid)
-        xs = []
-        for M in wl.ms:
-            x = workloads.workload_activations(wid, M)
-            xs.append(oracle.bf16_to_f32(x) if wl.act == "normal_bf16" else x)
-        rows = w.shape[0]
-        # large workloads: a bounded slice of output rows (same K, same M sweep)
-        est = sum(x.shape[0] for x in xs) * w.size * 1.5e-9  # ~1.5 ns per MAC and thread
-        if est / max(oracle.num_threads(), 1) > seconds:
-            rows = max(64, int(rows * seconds * oracle.num_threads() / est / 3))
-            w = np.ascontiguousarray(w[:rows])
-        wbytes = w.size // 4 * len(wl.ms)
+            def step():
+                for x in xs:
+                    oracle.glu(x, wg, wu, wd, betas, gain, wl.rms_eps)
+            desc = "GLU chain"
+        else:
+            w = workloads.workload_weights(wid)
+            beta = workloads.workload_beta(wid)
+            ms = list(wl.ms)
+            xs = []
+            for M in ms:
+                x = workloads.workload_activations(wid, M)
+                xs.append(oracle.bf16_to_f32(x) if wl.act == "normal_bf16" else x)
+            rows = w.shape[0]
+            # large workloads: a bounded slice of output rows (same K, same M sweep)
+            est = sum(x.shape[0] for x in xs) * w.size * 1.5e-9  # ~1.5 ns per MAC and thread
+            if est / max(nthr, 1) > seconds:
+                rows = max(64, int(rows * seconds * nthr / est / 3))
+                w = np.ascontiguousarray(w[:rows])
+            wbytes = w.size // 4 * len(ms)
 
-        def step():
-            for x in xs:
-                q, g = oracle.quant_act(x)
-                oracle.forward(q, g, w, beta)
-        desc = f"whole steps over {rows} of {wl.N} output rows"
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        step()
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or el / n * (n + 1) > 3 * seconds:
-            break
+            def step():
+                for x in xs:
+                    q, g = oracle.quant_act(x)
+                    oracle.forward(q, g, w, beta)
+            desc = f"whole steps over {rows} of {wl.N} output rows"
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            step()
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or el / n * (n + 1) > 3 * seconds:
+                break
+    finally:
+        oracle.set_num_threads(default_threads)
     return dict(value=round(wbytes * n / el / 1e9, 4), unit="packed-W GB/s",
-                cores=oracle.num_threads(), kind="oracle",
-                sample=f"{n} x ({desc}), M={list(wl.ms)}, {el:.1f} s")
+                cores=nthr, kind="oracle", cpu_model=cpu_model(),
+                host_cores=len(os.sched_getaffinity(0)),
+                sample=f"{n} x ({desc}), M={ms}, {el:.1f} s")
 
 
 # ----------------------------------------------------------------------------- ternarize
@@ -915,7 +928,194 @@ def bench_base3(args, torch, bl, dev):
     print(json.dumps(line), flush=True)
 
 
+# ----------------------------------------------------------------------------- timing
+
+SPIN_CYCLES = 20_000_000   # ~8-10 ms of shader clock: the host queues all launches meanwhile
+
+
+def launch_stats(torch, s, launch, n):
+    """Per-launch durations of ``launch(i)``, i = 0..n-1: each launch sits
+    between two timing events on stream ``s``; a spin kernel ahead of them
+    holds the stream until the host has queued every launch, so the GPU runs
+    them back to back and each event pair brackets exactly one launch (the
+    events also keep consecutive launches from overlapping).  Returns mean,
+    median, p10, p90 in microseconds."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(SPIN_CYCLES)
+        for i in range(n):
+            ev[i][0].record(s)
+            launch(i)
+            ev[i][1].record(s)
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return dict(avg_us=float(d.mean()), median_us=float(np.median(d)),
+                p10_us=float(np.percentile(d, 10)), p90_us=float(np.percentile(d, 90)),
+                launches=n)
+
+
+def floors(torch, bl, dev, s, nbytes, n=50):
+    """The empty-launch floor and a read-only pass over ``nbytes`` (weight
+    copies rotated as the layer's own calls rotate them)."""
+    lib = bl.lib
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    nb = nbytes // 16 * 16
+    copies = max(1, math.ceil(ROTATE_BYTES / max(nb, 1)))
+    buf = torch.empty((copies, nb), dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+
+    def empty(i):
+        if lib.bitlinear_floor_empty(torch.cuda.current_stream(dev).cuda_stream) != 0:
+            raise RuntimeError(bl.last_error())
+
+    def read(i):
+        if lib.bitlinear_floor_stream_read(buf[i % copies].data_ptr(), nb, sink.data_ptr(),
+                                           torch.cuda.current_stream(dev).cuda_stream) != 0:
+            raise RuntimeError(bl.last_error())
+
+    read(0)
+    e = launch_stats(torch, s, empty, n)
+    r = launch_stats(torch, s, read, n)
+    del buf
+    return dict(empty_launch_us=round(e["median_us"], 3), stream_read_us=round(r["median_us"], 3),
+                stream_read_p10_us=round(r["p10_us"], 3), stream_read_p90_us=round(r["p90_us"], 3),
+                stream_read_bytes=nb,
+                stream_read_GBs=round(nb / (r["median_us"] * 1e-6) / 1e9, 1),
+                stream_read_frac_of_peak=round(nb / (r["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+
+
+def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headline):
+    """One workload: the K-step graph time, every call's back-to-back time
+    (a graph of that call alone, once per weight copy) and its per-launch
+    event-bracketed durations, the dominant forward call's roofline and the
+    same-byte floors.  Returns a dict (the bench line's body)."""
+    ops, meta, keep = build_plan(args, torch, bl, dev, wid)
+    rec = RunAll()
+    ops(0, rec)  # first launch of every kernel; records the calls of a step
+    torch.cuda.synchronize()
+    print(f"# workload {meta['workload']}: M={meta['M']} K={meta['K']} N={meta['N']}, "
+          f"{meta['weight_copies']} weight copies", file=sys.stderr, flush=True)
+    ncopy = meta["weight_copies"]
+    s = torch.cuda.Stream(device=dev)
+
+    def steps_graph(first, count):
+        """One HIP graph of `count` consecutive steps (step i uses weight copy
+        i mod ncopy): a single replay launches them all, so the host does not
+        pace the GPU between steps."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(first, first + count):
+                ops(i, RunAll())
+        return g
+
+    if args.eager:
+        for i in range(warmup):
+            ops(i, RunAll())
+    elif warmup > 0:
+        steps_graph(0, warmup).replay()
+    timed = None if args.eager else steps_graph(warmup, steps)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    if timed is not None:
+        timed.replay()
+    else:
+        for i in range(warmup, warmup + steps):
+            ops(i, RunAll())
+    e1.record()
+    torch.cuda.synchronize()
+    del timed
+    ms_step = e0.elapsed_time(e1) / steps
+    print(f"# timed {steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+
+    kern = {}
+    for name, per_step in rec.calls.items():
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for c in range(ncopy):
+                ops(c, lambda n, *a, **kw: n == name)
+        reps = max(1, math.ceil(steps / ncopy))
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        b2b = e0.elapsed_time(e1) * 1e3 / (reps * ncopy * per_step)
+        del g
+        st = launch_stats(torch, s, lambda i, name=name: ops(i, lambda n, *a, **kw: n == name),
+                          per_launch)
+        st = {k: v / per_step if k.endswith("_us") else v for k, v in st.items()}
+        kern[name] = dict(b2b_us=b2b, per_step=per_step, **st, **rec.info.get(name, {}))
+    print("# per-call GPU time (us, per-launch mean | back-to-back): " +
+          ", ".join(f"{k} {v['avg_us']:.2f} | {v['b2b_us']:.2f}" for k, v in kern.items()),
+          file=sys.stderr, flush=True)
+
+    fwd = {k: v for k, v in kern.items() if "alg_bytes" in v}
+    dom = max(fwd, key=lambda k: fwd[k]["avg_us"] * fwd[k]["per_step"])
+    d = fwd[dom]
+    floor = floors(torch, bl, dev, s, d["wbytes"], per_launch)
+    traffic = read_traffic(meta["workload"], dom)
+    roof = roofline_of(d, traffic, floor)
+    per_call = {}
+    for k, v in kern.items():
+        e = dict(avg_us=round(v["avg_us"], 3), median_us=round(v["median_us"], 3),
+                 p10_us=round(v["p10_us"], 3), p90_us=round(v["p90_us"], 3),
+                 b2b_us=round(v["b2b_us"], 3), per_step=v["per_step"])
+        if "alg_bytes" in v:
+            r = roofline_of(v, read_traffic(meta["workload"], k), None)
+            e.update(kernel=v["kernel"],
+                     packed_w_GBs=round(v["wbytes"] / (v["avg_us"] * 1e-6) / 1e9, 1),
+                     alg_GBs=round(v["alg_bytes"] / (v["avg_us"] * 1e-6) / 1e9, 1),
+                     int8_eq_TOPS=round(v["ops"] / (v["avg_us"] * 1e-6) / 1e12, 2),
+                     bound=r["bound"], frac=r["frac"])
+        per_call[k] = e
+    value = meta["weight_bytes_per_step"] / (ms_step * 1e-3) / 1e9
+    del keep
+    torch.cuda.empty_cache()
+    return dict(
+        value=round(value, 2), ms_per_step=round(ms_step, 5), steps=steps, warmup=warmup,
+        config={"workload": meta["workload"], "M": meta["M"], "K": meta["K"], "N": meta["N"],
+                "weight_copies": meta["weight_copies"],
+                "timing": "eager" if args.eager else "hip_graph_of_all_timed_steps",
+                "fusion": "separate calls" if args.unfused else
+                "one-token quant_forward; GLU gate+up stacked",
+                "int8_eq_TOPS_per_step": round(meta["ops_per_step"] / (ms_step * 1e-3) / 1e12, 3),
+                "hbm_frac_per_step": round(value / HBM_PEAK_GBS, 4)},
+        roofline=roof, floor=floor, per_call=per_call)
+
+
+def roofline_of(d, traffic, floor):
+    """Roofline of one forward call from its per-launch mean duration: int8
+    MFMA for 512 tokens and more (2*M*N*K ops), HBM bytes otherwise (packed W
+    + x_q + gamma + y, + the fp32/bf16 rows a fused call reads)."""
+    us = d["avg_us"]
+    if d["M"] >= 512:
+        tops = d["ops"] / (us * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=round(tops, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
+                    frac=round(tops / INT8_PEAK_TOPS, 4), traffic=traffic)
+    else:
+        gbs = d["alg_bytes"] / (us * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic)
+        if floor:
+            roof["frac_of_stream_read"] = round(floor["stream_read_us"] / us, 4)
+    roof.update(call=None, kernel=d["kernel"], avg_launch_us=round(us, 3),
+                median_launch_us=round(d["median_us"], 3), p10_launch_us=round(d["p10_us"], 3),
+                p90_launch_us=round(d["p90_us"], 3), b2b_launch_us=round(d["b2b_us"], 3),
+                launches=d["launches"], alg_bytes_per_launch=d["alg_bytes"],
+                ops_per_launch=d["ops"])
+    return roof
+
+
 # ----------------------------------------------------------------------------- main
+
+METRIC = "BitLinear ternary GEMV/GEMM: packed-W GB/s (% HBM peak), int8-eq TOPS"
+
 
 def main():
     args = parse()
@@ -949,132 +1149,47 @@ def main():
         return
     if args.traffic_probe:
         args.no_rotate = True
-    ops, meta, keep = build_plan(args, torch, bl, dev)
-    if args.traffic_probe:
+        ops, meta, keep = build_plan(args, torch, bl, dev, args.workload)
         traffic_probe(args, torch, ops, dev)
         return
-    rec = RunAll()
-    ops(0, rec)  # first launch of every kernel; records the calls of a step
-    torch.cuda.synchronize()
-    print(f"# workload {meta['workload']}: M={meta['M']} K={meta['K']} N={meta['N']}, "
-          f"{meta['weight_copies']} weight copies", file=sys.stderr, flush=True)
 
-    ncopy = meta["weight_copies"]
-    s = torch.cuda.Stream(device=dev)
-
-    def steps_graph(first, count):
-        """One HIP graph of `count` consecutive steps (step i uses weight copy
-        i mod ncopy): a single replay launches them all, so the host does not
-        pace the GPU between steps."""
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=s):
-            for i in range(first, first + count):
-                ops(i, RunAll())
-        return g
-
-    def run_steps(first, count):
-        if count <= 0:
-            return
-        if args.eager:
-            for i in range(first, first + count):
-                ops(i, RunAll())
-        else:
-            steps_graph(first, count).replay()
-
-    run_steps(0, args.warmup)
-    timed = None if args.eager else steps_graph(args.warmup, args.steps)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    if timed is not None:
-        timed.replay()
-    else:
-        run_steps(args.warmup, args.steps)
-    e1.record()
-    torch.cuda.synchronize()
-    del timed
-    ms_step = e0.elapsed_time(e1) / args.steps
-    print(f"# timed {args.steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
-
-    # per-call durations: each call launched back to back, one launch per
-    # weight copy, replayed from one HIP graph (eager: from the host)
-    kern = {}
-    for name, per_step in rec.calls.items():
-        if args.eager:
-            t = RunOne(torch, name)
-            for i in range(args.steps):
-                ops(args.warmup + i, t)
-            avg = t.avg_us(args.steps * per_step)
-        else:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                for c in range(ncopy):
-                    ops(c, lambda n, *a, **kw: n == name)
-            reps = max(1, math.ceil(args.steps / ncopy))
-            g.replay()
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(reps):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            avg = e0.elapsed_time(e1) * 1e3 / (reps * ncopy * per_step)
-            del g
-        kern[name] = dict(avg_us=avg, per_step=per_step, **rec.info.get(name, {}))
-    print("# per-call GPU time (us): " + ", ".join(f"{k} {v['avg_us']:.2f}" for k, v in kern.items()),
-          file=sys.stderr, flush=True)
-
-    fwd = {k: v for k, v in kern.items() if "alg_bytes" in v}
-    dom = max(fwd, key=lambda k: fwd[k]["avg_us"] * fwd[k]["per_step"])
-    d = fwd[dom]
-    traffic = read_traffic(meta["workload"], dom)
-    if d["M"] >= 512:
-        tops = d["ops"] / (d["avg_us"] * 1e-6) / 1e12
-        roof = dict(bound="mfma", achieved=round(tops, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
-                    frac=round(tops / INT8_PEAK_TOPS, 4), traffic=traffic)
-    else:
-        gbs = d["alg_bytes"] / (d["avg_us"] * 1e-6) / 1e9
-        roof = dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic)
-    roof.update(call=dom, kernel=d["kernel"], avg_launch_us=round(d["avg_us"], 3),
-                alg_bytes_per_launch=d["alg_bytes"], ops_per_launch=d["ops"])
-
-    cpu = cpu_baseline(args, args.cpu_seconds) if args.cpu_seconds > 0 else None
-
-    value = meta["weight_bytes_per_step"] / (ms_step * 1e-3) / 1e9
-    per_call = {}
-    for k, v in kern.items():
-        e = dict(avg_us=round(v["avg_us"], 3), per_step=v["per_step"])
-        if "alg_bytes" in v:
-            e.update(kernel=v["kernel"],
-                     packed_w_GBs=round(v["wbytes"] / (v["avg_us"] * 1e-6) / 1e9, 1),
-                     alg_GBs=round(v["alg_bytes"] / (v["avg_us"] * 1e-6) / 1e9, 1),
-                     int8_eq_TOPS=round(v["ops"] / (v["avg_us"] * 1e-6) / 1e12, 2))
-        per_call[k] = e
+    head = measure_workload(args, torch, bl, dev, args.workload, args.steps, args.warmup,
+                            args.per_launch, True)
+    dom = max((k for k, v in head["per_call"].items() if "kernel" in v),
+              key=lambda k: head["per_call"][k]["avg_us"] * head["per_call"][k]["per_step"])
+    head["roofline"]["call"] = dom
+    sub = {}
+    for wid in args.configs:
+        if wid == args.workload:
+            continue
+        r = measure_workload(args, torch, bl, dev, wid, args.sub_steps, max(2, args.warmup // 4),
+                             args.per_launch, False)
+        r["roofline"]["call"] = max((k for k, v in r["per_call"].items() if "kernel" in v),
+                                    key=lambda k: r["per_call"][k]["avg_us"] *
+                                    r["per_call"][k]["per_step"])
+        if wid in (1, 2, 4) and args.cpu_seconds > 0:
+            r["cpu_baseline_1core"] = cpu_baseline(wid, min(3.0, args.cpu_seconds), threads=1)
+        sub[str(wid)] = r
+    cpu = cpu_baseline(args.workload, args.cpu_seconds) if args.cpu_seconds > 0 else None
     line = {
-        "metric": "BitLinear ternary GEMV/GEMM: packed-W GB/s (% HBM peak), int8-eq TOPS",
-        "value": round(value, 2),
+        "metric": METRIC,
+        "value": head["value"],
         "unit": "packed-W GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": meta["workload"], "M": meta["M"], "K": meta["K"], "N": meta["N"],
-                   "weight_copies": meta["weight_copies"],
-                   "timing": "eager" if args.eager else "hip_graph_of_all_timed_steps",
-                   "fusion": "separate calls" if args.unfused else
-                   "one-token quant_forward; GLU gate+up stacked",
-                   "int8_eq_TOPS_per_step": round(meta["ops_per_step"] / (ms_step * 1e-3) / 1e12, 3),
-                   "hbm_frac_per_step": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": roof,
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "floor": head["floor"],
         "cpu_baseline": cpu,
-        "per_call": per_call,
+        "per_call": head["per_call"],
+        "configs": sub,
     }
     print(json.dumps(line), flush=True)
 

@@ -35,7 +35,11 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 // Largest M handled by one grid dimension of the GEMM (65535 row tiles of 128).
 constexpr int64_t kMaxM = 65535LL * 128;
-constexpr int64_t kMaxN = (1LL << 31) - 1;
+// Largest N (and weight-row count of the packing calls).  The launchers and
+// kernels take N as int and round it up to their tile widths (at most a few
+// hundred columns) or add a tile offset to a row index, so N stays 2^30 below
+// INT_MAX; 2^30 rows are 4 GiB of packed weights even at K = 16.
+constexpr int64_t kMaxN = 1LL << 30;
 
 bitlinear_status_t check_k(const char* fn, const char* name, int64_t K) {
     if (K < 0 || K % 16 != 0 || K > BITLINEAR_MAX_K)
@@ -492,6 +496,22 @@ bitlinear_status_t bitlinear_forward3(const int8_t* x_q, const float* gamma, int
     return from_hip(bl::launch_forward3(x_q, gamma, (int)M, (int)K, w_packed3, (int)N, beta, y, acc,
                                         stream),
                     fn);
+}
+
+bitlinear_status_t bitlinear_floor_empty(hipStream_t stream) {
+    return from_hip(bl::launch_floor_empty(stream), "bitlinear_floor_empty");
+}
+
+bitlinear_status_t bitlinear_floor_stream_read(const void* p, int64_t bytes, uint32_t* sink,
+                                               hipStream_t stream) {
+    const char* fn = "bitlinear_floor_stream_read";
+    if (bytes < 0 || bytes % 16 != 0)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: bytes=%lld must be >= 0 and a multiple of 16", fn,
+                    (long long)bytes);
+    BL_TRY(need(fn, "p", p, bytes > 0, 16));
+    BL_TRY(need(fn, "sink", sink, bytes > 0, 4));
+    if (bytes == 0) return ok();
+    return from_hip(bl::launch_floor_stream_read(p, bytes, sink, stream), fn);
 }
 
 const char* bitlinear_last_error(void) { return g_err; }

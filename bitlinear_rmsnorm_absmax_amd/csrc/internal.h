@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
 
 namespace bl {
@@ -60,7 +61,7 @@ hipError_t launch_pack(const int8_t* w, int64_t N, int64_t K, uint32_t* packed, 
 // y (and acc when non-NULL) = 0 for K == 0.
 hipError_t launch_fill_zero(float* y, int32_t* acc, int64_t count, hipStream_t s);
 
-// Path 1: VALU dot4 GEMV, M <= 8.
+// Path 1: VALU dot4 GEMV, M <= 4 (the ABI's limit; one pass over the weights).
 // Forward launchers: y == nullptr stores only the accumulators (acc).
 hipError_t launch_gemv_valu(const int8_t* xq, const float* gamma, int M, int K,
                             const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
@@ -122,7 +123,9 @@ hipError_t launch_quant_act_grouped(const void* x, int bf16, int64_t M, int64_t 
 hipError_t launch_group_sum(const int32_t* acc, const float* gamma, const float* beta, int64_t M,
                             int64_t N, int64_t G, float* y, hipStream_t s);
 // Base-3 weights (1.6 bits): packing [N][ceil(K/80)][16 bytes] and the
-// decode product on the vector ALUs (passes of up to four tokens).
+// decode product: 2..16 tokens on int8 MFMA with the activation block staged
+// in LDS (gemv3_mfma_kernel), one token -- and blocks too large for LDS, in
+// passes of up to four tokens -- on the vector ALUs (gemv3_kernel).
 hipError_t launch_pack3(const int8_t* w, int64_t N, int64_t K, uint32_t* packed3, int* bad_count,
                         hipStream_t s);
 hipError_t launch_forward3(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
@@ -133,5 +136,10 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
 hipError_t launch_gemm_mfma(const int8_t* xq, const float* gamma, int M, int K,
                             const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                             hipStream_t s);
+
+// Measurement floors (floor.hip): an empty kernel, and a read-only pass over
+// `bytes` (a multiple of 16) at p (16-byte aligned).
+hipError_t launch_floor_empty(hipStream_t s);
+hipError_t launch_floor_stream_read(const void* p, int64_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace bl

@@ -22,7 +22,8 @@
  *    before anything is launched (nothing is written on a validation error),
  *    and the launch itself.  A fault inside a kernel surfaces at the caller's
  *    next synchronisation, as usual in HIP.
- *  - Sizes are int64_t; M, N, K may be 0 (empty work).  K, the reduction
+ *  - Sizes are int64_t; M, N, K may be 0 (empty work).  N (weight rows) is
+ *    at most 2^30.  K, the reduction
  *    length, must be a multiple of 16 and at most 131072, so |acc| <= 127*K
  *    < 2^24 and fl32(acc) is exact.
  *  - Pointers to int8 / packed data and to the activations x must be 16-byte
@@ -353,11 +354,30 @@ bitlinear_status_t bitlinear_pack_weights3(const int8_t* w, int64_t N, int64_t K
 
 /* bitlinear_forward on base-3 weights: the same acc, y and argument rules,
  * with w_packed3 the bitlinear_pack_weights3 layout (16-byte aligned).  A
- * decode product on the vector ALUs: tokens go in passes of up to four, each
- * a pass over the weights; for many tokens use the 2-bit layout. */
+ * decode product: 2..16 tokens whose activation block fits in LDS run in one
+ * pass over the weights on int8 MFMA (the base-3 bytes decoded to codes in
+ * registers); one token, and larger blocks in passes of up to four tokens,
+ * on the vector ALUs.  For many tokens use the 2-bit layout. */
 bitlinear_status_t bitlinear_forward3(const int8_t* x_q, const float* gamma, int64_t M, int64_t K,
                                       const uint32_t* w_packed3, int64_t N, float beta, float* y,
                                       int32_t* acc, hipStream_t stream);
+
+/*
+ * Measurement floors.  Not steps of the layer: the two references a roofline
+ * report needs next to the layer's kernels on the same device -- the duration
+ * of a launch that does nothing, and of a read-only pass over the same number
+ * of bytes a product streams (the weight matrix), with the coalesced 16-byte
+ * loads the decode kernels issue.
+ *
+ * bitlinear_floor_empty: launches one empty workgroup on `stream`.
+ * bitlinear_floor_stream_read: reads `bytes` (>= 0, a multiple of 16) at p
+ *   (device, 16-byte aligned) once.  sink: device uint32 [1]; stored only if
+ *   the xor of all the 32-bit words read equals 0x9E3779B9 (it keeps the
+ *   loads from being optimised away), so its content carries no meaning.
+ */
+bitlinear_status_t bitlinear_floor_empty(hipStream_t stream);
+bitlinear_status_t bitlinear_floor_stream_read(const void* p, int64_t bytes, uint32_t* sink,
+                                               hipStream_t stream);
 
 /* Text of the last non-OK status on this thread ("" if none). */
 const char* bitlinear_last_error(void);

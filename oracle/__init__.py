@@ -61,6 +61,7 @@ def _load() -> ctypes.CDLL:
             "oracle_pack3": [_c_p, _i64, _i64, _c_p],
             "oracle_unpack3": [_c_p, _i64, _i64, _c_p],
             "oracle_num_threads": [],
+            "oracle_set_num_threads": [ctypes.c_int],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -68,6 +69,7 @@ def _load() -> ctypes.CDLL:
         lib.oracle_pack.restype = ctypes.c_int64
         lib.oracle_accumulate.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_ternarize.restype = ctypes.c_double
         lib.oracle_binarize.restype = ctypes.c_double
         lib.oracle_pack1.restype = ctypes.c_int64
@@ -335,3 +337,8 @@ def glu(x: np.ndarray, w_gate, w_up, w_down, betas, rms_gain, rms_eps: float = 1
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's parallel loops (started from this thread)."""
+    _load().oracle_set_num_threads(int(n))

@@ -242,6 +242,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Thread count of the parallel loops started from the calling thread (timing
+ * of the baseline on one core); n <= 0 is ignored. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Pairwise sum of |x[a..b)| in double: a run of one entry is its value; a
  * longer run splits after the largest power of two below its length. */
 static double pairwise_abs(const float* x, int64_t a, int64_t b) {

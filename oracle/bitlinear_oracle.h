@@ -97,6 +97,7 @@ void oracle_unpack1(const uint32_t* packed, int64_t N, int64_t K, int8_t* w);
 
 /* Number of OpenMP threads the accumulate loop runs on. */
 int oracle_num_threads(void);
+void oracle_set_num_threads(int n);
 
 /* Base-3 packing, 1.6 bits per weight ([U] Ternäres Gewichtssystem: about
  * 1.58 bits carry three states; 3^5 = 243 fits a byte).  Ternary w int8

@@ -24,6 +24,7 @@ def test_every_declared_symbol_is_exported():
         "bitlinear_binarize", "bitlinear_pack_weights1", "bitlinear_forward1",
         "bitlinear_quant_act_grouped", "bitlinear_forward_grouped", "bitlinear_ternarize_grouped",
         "bitlinear_forward_grouped_one_launch", "bitlinear_pack_weights3", "bitlinear_forward3",
+        "bitlinear_floor_empty", "bitlinear_floor_stream_read",
         "bitlinear_last_error", "bitlinear_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -390,3 +391,94 @@ def _f3(xq=FAKE, g=FAKE, M=1, K=160, w=FAKE, N=1, beta=1.0, y=FAKE, acc=None):
 def test_forward3_rejects(kw, status, msg):
     assert _f3(**kw) == status
     assert msg in bl.last_error()
+
+
+# ------------------------------------------------------------------ binding buffer checks
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+@pytest.mark.parametrize("call,msg", [
+    # caller-supplied outputs of the wrong length or dtype are refused before any pointer
+    # reaches the library (CPU tensors: the shape check runs before the device check)
+    (lambda t: bl.quant_act(_t((2, 32), t.float32), out=(_t((2, 16), t.int8), _t((2,), t.float32))),
+     "x_q has shape (2, 16), expected (2, 32)"),
+    (lambda t: bl.quant_act(_t((2, 32), t.float32), out=(_t((2, 32), t.int8), _t((1,), t.float32))),
+     "gamma has shape (1,), expected (2,)"),
+    (lambda t: bl.quant_act(_t((2, 32), t.float32), out=(_t((2, 32), t.uint8), _t((2,), t.float32))),
+     "x_q has dtype"),
+    (lambda t: bl.quant_act(_t((2, 32), t.float32), rms_gain=_t((16,), t.float32)),
+     "rms_gain has shape (16,), expected (32,)"),
+    (lambda t: bl.forward(_t((3, 32), t.int8), _t((2,), t.float32), _t((5, 2), t.int32), 1.0),
+     "gamma has shape (2,), expected (3,)"),
+    (lambda t: bl.forward(_t((3, 32), t.int8), _t((3,), t.float32), _t((5, 2), t.int32), 1.0,
+                          out=_t((3, 4), t.float32)),
+     "out has shape (3, 4), expected (3, 5)"),
+    (lambda t: bl.forward(_t((3, 32), t.int8), _t((3,), t.float32), _t((5, 2), t.int32), 1.0,
+                          acc_out=_t((3, 5), t.float32)),
+     "acc_out has dtype"),
+    (lambda t: bl.forward(_t((3, 32), t.int8), _t((3,), t.float32), _t((5, 2), t.int32), 1.0,
+                          acc_out=_t((2, 5), t.int32)),
+     "acc_out has shape (2, 5), expected (3, 5)"),
+    (lambda t: bl.quant_forward(_t((1, 32), t.float32), _t((5, 2), t.int32), 1.0,
+                                out=(_t((1, 4), t.float32), _t((1, 32), t.int8), _t((1,), t.float32))),
+     "y has shape (1, 4), expected (1, 5)"),
+    (lambda t: bl.quant_forward(_t((1, 32), t.float32), _t((5, 2), t.int32), 1.0,
+                                rms_gain=_t((33,), t.float32)),
+     "rms_gain has shape (33,), expected (32,)"),
+    (lambda t: bl.silu_mul_quant(_t((2, 32), t.float32), _t((2, 16), t.float32)),
+     "up has shape (2, 16), expected (2, 32)"),
+    (lambda t: bl.silu_mul_quant_acc(_t((2, 64), t.int32), _t((3,), t.float32), 1.0, 1.0),
+     "gamma has shape (3,), expected (2,)"),
+    (lambda t: bl.forward1(_t((2, 64), t.int8), _t((1,), t.float32), _t((4, 2), t.int32), 1.0),
+     "gamma has shape (1,), expected (2,)"),
+    (lambda t: bl.forward3(_t((2, 80), t.int8), _t((4,), t.float32), _t((4, 4), t.int32), 1.0),
+     "gamma has shape (4,), expected (2,)"),
+    (lambda t: bl.forward_grouped(_t((2, 3, 64), t.int8), _t((2, 2), t.float32),
+                                  _t((2, 5, 4), t.int32), _t((2,), t.float32)),
+     "gamma has shape (2, 2), expected (2, 3)"),
+    (lambda t: bl.forward_grouped(_t((2, 3, 64), t.int8), _t((2, 3), t.float32),
+                                  _t((2, 5, 4), t.int32), _t((3,), t.float32)),
+     "beta has shape (3,), expected (2,)"),
+    (lambda t: bl.forward(_t((3, 2, 16), t.int8), _t((3,), t.float32), _t((5, 1), t.int32), 1.0),
+     "x_q must be 2-D"),
+])
+def test_binding_rejects_mis_sized_buffers(call, msg):
+    import torch
+    with pytest.raises(ValueError, match=msg.replace("(", r"\(").replace(")", r"\)")):
+        call(torch)
+
+
+def test_binding_refuses_host_tensors_of_the_right_shape():
+    import torch
+    with pytest.raises(ValueError, match="must be a GPU tensor"):
+        bl.quant_act(torch.zeros((2, 32), dtype=torch.float32))
+
+
+def test_row_count_limit_keeps_launcher_arithmetic_in_int():
+    """N is capped at 2^30 so every launcher's int rounding of N up to a tile
+    width, and every row index plus a tile offset, stays below INT_MAX."""
+    lim = 1 << 30
+    for fn in ("bitlinear_forward_path",):
+        # at the limit: nothing to do with M = 0, so validation passes without a launch
+        assert _fwd(xq=None, g=None, w=None, y=None, M=0, N=lim) == bl.OK
+        assert _fwd(M=0, N=lim + 1) == bl.ERR_SHAPE
+        assert f"N={lim + 1}" in bl.last_error()
+    assert bl.lib.bitlinear_pack_weights(FAKE, lim + 1, 16, FAKE, None, None) == bl.ERR_SHAPE
+    assert bl.lib.bitlinear_forward1(FAKE, FAKE, 0, 64, FAKE, lim + 1, F(1.0), FAKE, None,
+                                     None) == bl.ERR_SHAPE
+    assert bl.lib.bitlinear_forward3(FAKE, FAKE, 0, 16, FAKE, lim + 1, F(1.0), FAKE, None,
+                                     None) == bl.ERR_SHAPE
+    assert bl.lib.bitlinear_quant_forward(FAKE, 0, 0, 64, None, F(0.0), FAKE, lim + 1, F(1.0), FAKE,
+                                          FAKE, FAKE, None, None) == bl.ERR_SHAPE
+
+
+def test_floor_stream_read_rejects():
+    assert bl.lib.bitlinear_floor_stream_read(FAKE, 24, FAKE, None) == bl.ERR_SHAPE
+    assert bl.lib.bitlinear_floor_stream_read(FAKE, -16, FAKE, None) == bl.ERR_SHAPE
+    assert bl.lib.bitlinear_floor_stream_read(None, 32, FAKE, None) == bl.ERR_NULL
+    assert bl.lib.bitlinear_floor_stream_read(FAKE + 8, 32, FAKE, None) == bl.ERR_ALIGN
+    assert bl.lib.bitlinear_floor_stream_read(FAKE, 32, None, None) == bl.ERR_NULL
+    assert bl.lib.bitlinear_floor_stream_read(None, 0, None, None) == bl.OK

@@ -117,10 +117,11 @@ def test_kernel_labels_follow_the_dispatch():
     assert bench.forward_kernel(16, 4096, 11008) == "decode_lds_kernel"
 
 
-def test_traffic_digest_covers_existing_sources():
+def test_traffic_digest_covers_every_library_source():
     bench = load_bench()
     csrc = os.path.join(ROOT, "bitlinear_rmsnorm_absmax_amd", "csrc")
-    for f in bench.TRAFFIC_SOURCES:
-        assert os.path.exists(os.path.join(csrc, f)), f
+    srcs = bench._library_sources()
+    assert set(srcs) == {f for f in os.listdir(csrc) if f.endswith((".hip", ".h", ".cpp"))}
+    assert "gemm_dma.hip" in srcs and "api.cpp" in srcs and "mfma_epilogue.h" in srcs
     d = bench.kernel_source_digest()
     assert len(d) == 16 and d == bench.kernel_source_digest()
