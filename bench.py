@@ -91,6 +91,10 @@ def parse():
                     help="launch every call of one step once, then a plain copy kernel of "
                          f"{COPY_BYTES} bytes, write the launch order to JSON and exit "
                          "(run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "COMMAND"),
+                    help="no GPU: write profiles/kernels_<workload>.md from a rocprofv3 "
+                         "--kernel-trace run of COMMAND (a bench.py command line with the same "
+                         "step, warmup, per-launch and config arguments as this one)")
     ap.add_argument("--traffic-write", nargs=3, metavar=("JSON", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn the two counter runs of --traffic-probe into "
                          "profiles/traffic_<workload>.md")
@@ -429,6 +433,103 @@ def traffic_write(args):
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print(path)
+
+
+# ----------------------------------------------------------------------------- trace summary
+
+def _phase_counts(wid, steps, warmup, per_launch, ncopy):
+    """Launches of one call in a bench run, in order: the first step, the
+    warmup graph, the timed graph, the back-to-back graph (its first replay,
+    then the timed replays) and the per-launch event pairs."""
+    reps = max(1, math.ceil(steps / ncopy))
+    return [("first", 1), ("warmup", warmup), ("timed steps", steps),
+            ("back-to-back first", ncopy), ("back-to-back", reps * ncopy),
+            ("per-launch events", per_launch)]
+
+
+def trace_summary(args):
+    """profiles/kernels_<workload>.md from a `rocprofv3 --kernel-trace --stats`
+    run of bench.py: per kernel and grid, every dispatch's duration (mean,
+    median, p10, p90) and, where the count matches one workload's launch
+    pattern, the same split by bench phase."""
+    import csv
+    import glob
+    d, cmd = args.trace_summary
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one kernel_trace.csv under {d}, found {files}")
+    rows = list(csv.DictReader(open(files[0])))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    # each workload's measurement ends with its floor kernels, so the runs of
+    # floor dispatches cut the trace into the workloads, in bench order
+    wids = [args.workload] + [c for c in args.configs if c != args.workload]
+    wi, in_floor = 0, False
+    groups = {}
+    for r in rows:
+        name = r["Kernel_Name"].replace("(anonymous namespace)::", "").replace("void ", "")
+        name = name[:name.index(">(") + 1] if ">(" in name else name.split("(")[0]
+        is_floor = "floor_" in name
+        if in_floor and not is_floor and "bl::" in name:
+            wi += 1
+        in_floor = is_floor or (in_floor and "bl::" not in name)
+        w = wids[min(wi, len(wids) - 1)]
+        key = (workloads.WORKLOADS[w].name, name, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+        groups.setdefault(key, []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+
+    def stats(v):
+        a = np.array(v)
+        return (f"{len(a)} | {a.mean():.2f} | {np.median(a):.2f} | "
+                f"{np.percentile(a, 10):.2f} | {np.percentile(a, 90):.2f}")
+
+    def pattern(wid, count):
+        """the launch pattern of a call of workload wid with `count` dispatches"""
+        head = wid == args.workload
+        steps = args.steps if head else args.sub_steps
+        warm = args.warmup if head else max(2, args.warmup // 4)
+        for ncopy in range(1, 1024):
+            pat = _phase_counts(wid, steps, warm, args.per_launch, ncopy)
+            if sum(c for _, c in pat) == count:
+                return pat
+        return None
+
+    lines = [f"# Kernel trace: `{cmd}`", "",
+             "Command (repository root; `cd /tmp && export TMPDIR=/tmp` first, paths relative to "
+             "the repository):", "", "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace -o bench -- "
+             f"{cmd}",
+             f"python3 bench.py --trace-summary gpurun_out/trace \"{cmd}\"", "```", "",
+             "Durations in microseconds from the kernel trace (end - start of each dispatch), per "
+             "workload (in bench order; each one's floor kernels close it), kernel and grid size.", "",
+             "| workload | kernel | grid | workgroup | dispatches | mean | median | p10 | p90 |",
+             "|---|---|---:|---:|---:|---:|---:|---:|---:|"]
+    order = sorted(groups.items(), key=lambda kv: (wids.index(next(
+        w for w in wids if workloads.WORKLOADS[w].name == kv[0][0])), -sum(kv[1])))
+    for (wname, name, grid, wg), v in order:
+        if "bl::" not in name:
+            continue
+        lines.append(f"| {wname} | `{name}` | {grid} | {wg} | {stats(v)} |")
+    lines += ["", "By bench phase (library calls of the measured steps: the timed steps graph, "
+              "the back-to-back graph that bench.py's avg_launch_us comes from, and the "
+              "per-launch event pairs):", "",
+              "| workload | kernel | grid | phase | dispatches | mean | median | p10 | p90 |",
+              "|---|---|---:|---|---:|---:|---:|---:|---:|"]
+    for (wname, name, grid, wg), v in order:
+        if "bl::" not in name or "floor_" in name:
+            continue
+        wid = next(w for w in wids if workloads.WORKLOADS[w].name == wname)
+        pat = pattern(wid, len(v))
+        if pat is None:
+            continue
+        i = 0
+        for lab, c in pat:
+            if lab in ("timed steps", "back-to-back", "per-launch events") and c > 0:
+                lines.append(f"| {wname} | `{name}` | {grid} | {lab} | {stats(v[i:i + c])} |")
+            i += c
+    out = os.path.join(PROFILES, f"kernels_{workloads.WORKLOADS[args.workload].name}.md")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(out)
 
 
 # ----------------------------------------------------------------------------- cpu baseline
@@ -975,15 +1076,34 @@ def floors(torch, bl, dev, s, nbytes, n=50):
                                            torch.cuda.current_stream(dev).cuda_stream) != 0:
             raise RuntimeError(bl.last_error())
 
+    def b2b(fn):
+        """back-to-back: one graph of one launch per copy, replayed between events"""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for c in range(copies):
+                fn(c)
+        reps = max(1, math.ceil(n / copies))
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * copies)
+
     read(0)
     e = launch_stats(torch, s, empty, n)
     r = launch_stats(torch, s, read, n)
+    eb, rb = b2b(empty), b2b(read)
     del buf
-    return dict(empty_launch_us=round(e["median_us"], 3), stream_read_us=round(r["median_us"], 3),
-                stream_read_p10_us=round(r["p10_us"], 3), stream_read_p90_us=round(r["p90_us"], 3),
+    return dict(empty_launch_b2b_us=round(eb, 3), stream_read_b2b_us=round(rb, 3),
+                empty_launch_event_us=round(e["median_us"], 3),
+                stream_read_event_us=round(r["median_us"], 3),
                 stream_read_bytes=nb,
-                stream_read_GBs=round(nb / (r["median_us"] * 1e-6) / 1e9, 1),
-                stream_read_frac_of_peak=round(nb / (r["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+                stream_read_GBs=round(nb / (rb * 1e-6) / 1e9, 1),
+                stream_read_frac_of_peak=round(nb / (rb * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
 
 
 def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headline):
@@ -1056,22 +1176,24 @@ def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headl
           file=sys.stderr, flush=True)
 
     fwd = {k: v for k, v in kern.items() if "alg_bytes" in v}
-    dom = max(fwd, key=lambda k: fwd[k]["avg_us"] * fwd[k]["per_step"])
+    dom = max(fwd, key=lambda k: fwd[k]["b2b_us"] * fwd[k]["per_step"])
     d = fwd[dom]
     floor = floors(torch, bl, dev, s, d["wbytes"], per_launch)
     traffic = read_traffic(meta["workload"], dom)
     roof = roofline_of(d, traffic, floor)
     per_call = {}
     for k, v in kern.items():
-        e = dict(avg_us=round(v["avg_us"], 3), median_us=round(v["median_us"], 3),
-                 p10_us=round(v["p10_us"], 3), p90_us=round(v["p90_us"], 3),
-                 b2b_us=round(v["b2b_us"], 3), per_step=v["per_step"])
+        e = dict(avg_us=round(v["b2b_us"], 3), per_step=v["per_step"],
+                 per_launch_events=dict(mean_us=round(v["avg_us"], 3),
+                                        median_us=round(v["median_us"], 3),
+                                        p10_us=round(v["p10_us"], 3), p90_us=round(v["p90_us"], 3)))
         if "alg_bytes" in v:
             r = roofline_of(v, read_traffic(meta["workload"], k), None)
+            us = v["b2b_us"]
             e.update(kernel=v["kernel"],
-                     packed_w_GBs=round(v["wbytes"] / (v["avg_us"] * 1e-6) / 1e9, 1),
-                     alg_GBs=round(v["alg_bytes"] / (v["avg_us"] * 1e-6) / 1e9, 1),
-                     int8_eq_TOPS=round(v["ops"] / (v["avg_us"] * 1e-6) / 1e12, 2),
+                     packed_w_GBs=round(v["wbytes"] / (us * 1e-6) / 1e9, 1),
+                     alg_GBs=round(v["alg_bytes"] / (us * 1e-6) / 1e9, 1),
+                     int8_eq_TOPS=round(v["ops"] / (us * 1e-6) / 1e12, 2),
                      bound=r["bound"], frac=r["frac"])
         per_call[k] = e
     value = meta["weight_bytes_per_step"] / (ms_step * 1e-3) / 1e9
@@ -1090,10 +1212,14 @@ def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headl
 
 
 def roofline_of(d, traffic, floor):
-    """Roofline of one forward call from its per-launch mean duration: int8
-    MFMA for 512 tokens and more (2*M*N*K ops), HBM bytes otherwise (packed W
-    + x_q + gamma + y, + the fp32/bf16 rows a fused call reads)."""
-    us = d["avg_us"]
+    """Roofline of one forward call from its average launch duration (the
+    back-to-back time: HIP events around a graph of that call's launches on
+    its stream, divided by the launch count): int8 MFMA for 512 tokens and
+    more (2*M*N*K ops), HBM bytes otherwise (packed W + x_q + gamma + y, + the
+    fp32/bf16 rows a fused call reads).  The per-launch event statistics ride
+    along; each of those launches also carries the event pair's own cost
+    (about 2 us, see the floor's empty launch)."""
+    us = d["b2b_us"]
     if d["M"] >= 512:
         tops = d["ops"] / (us * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(tops, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
@@ -1103,12 +1229,13 @@ def roofline_of(d, traffic, floor):
         roof = dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic)
         if floor:
-            roof["frac_of_stream_read"] = round(floor["stream_read_us"] / us, 4)
+            roof["frac_of_stream_read"] = round(floor["stream_read_b2b_us"] / us, 4)
     roof.update(call=None, kernel=d["kernel"], avg_launch_us=round(us, 3),
-                median_launch_us=round(d["median_us"], 3), p10_launch_us=round(d["p10_us"], 3),
-                p90_launch_us=round(d["p90_us"], 3), b2b_launch_us=round(d["b2b_us"], 3),
-                launches=d["launches"], alg_bytes_per_launch=d["alg_bytes"],
-                ops_per_launch=d["ops"])
+                per_launch_events=dict(mean_us=round(d["avg_us"], 3),
+                                       median_us=round(d["median_us"], 3),
+                                       p10_us=round(d["p10_us"], 3), p90_us=round(d["p90_us"], 3),
+                                       launches=d["launches"]),
+                alg_bytes_per_launch=d["alg_bytes"], ops_per_launch=d["ops"])
     return roof
 
 
@@ -1121,6 +1248,9 @@ def main():
     args = parse()
     if args.traffic_write:
         traffic_write(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is a "

@@ -37,6 +37,8 @@ class DynLdsOptIn {
 
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, const float* gain,
                             float eps, int8_t* q, float* gamma, hipStream_t s);
+// Workgroups per row launch_quant_act uses (1: one workgroup per row).
+int quant_split_ways(int64_t M, int64_t K);
 
 // Fused quantisation + one-token product (quant_gemv.hip): M == 1,
 // K % 64 == 0, K <= kFusedMaxK (the codes are staged in LDS), N <= kFusedMaxN.

@@ -146,9 +146,29 @@ def test_quant_act_bit_exact(dev, dt, M, K, act):
         xf = x
         xd = to_dev(x, dev)
     q_ref, g_ref = oracle.quant_act(xf)
-    q, g = bl.quant_act(xd)
+    gq, gg = Guard((M, K), torch.int8, dev), Guard((M,), torch.float32, dev)
+    q, g = bl.quant_act(xd, out=(gq.t, gg.t))
+    gq.check(f"x_q M={M} K={K}")
+    gg.check(f"gamma M={M} K={K}")
     np.testing.assert_array_equal(host(q), q_ref)
     np.testing.assert_array_equal(host(g), g_ref)
+
+
+@pytest.mark.parametrize("M,K", [(1, 8192), (8, 8192), (64, 8192), (127, 4096), (4, 4096)])
+def test_split_quantiser_matches_one_workgroup_rows(dev, M, K):
+    """Few long rows run P workgroups per row; a stacked batch of 128 rows or
+    more runs one workgroup per row.  The same rows quantised both ways (with
+    and without RMSNorm) give the same codes and bit-identical gamma."""
+    x = workloads.workload_activations(5, M, K) if K == 8192 else \
+        workloads.random_case(230 + M, M, 1, K)[0]
+    pad = np.zeros((128, K), np.float32)
+    pad[:M] = x
+    gain = to_dev(workloads.rng_for(231, K).uniform(0.5, 2.0, K).astype(np.float32), dev)
+    for gn in (None, gain):
+        q1, g1 = bl.quant_act(to_dev(x, dev), gn, 1e-6)
+        q2, g2 = bl.quant_act(to_dev(pad, dev), gn, 1e-6)
+        np.testing.assert_array_equal(host(q1), host(q2)[:M])
+        np.testing.assert_array_equal(host(g1).view(np.uint32), host(g2)[:M].view(np.uint32))
 
 
 @pytest.mark.parametrize("M,K,gain_kind", [(1, 2560, "unit"), (512, 2560, "unit"), (6, 1040, "rand"),
