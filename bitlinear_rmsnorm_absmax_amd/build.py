@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbitlinear.so")
 
-SOURCES = ["api.cpp", "quant_act.hip", "pack.hip", "gemv_valu.hip", "skinny_mfma.hip",
+SOURCES = ["api.cpp", "shapes.cpp", "quant_act.hip", "pack.hip", "gemv_valu.hip", "skinny_mfma.hip",
            "decode_lds.hip", "gemm_mfma.hip", "gemm_dma.hip", "ternarize.hip", "binary.hip",
            "grouped.hip", "base3.hip", "quant_gemv.hip", "floor.hip"]
 

@@ -74,16 +74,6 @@ __global__ __launch_bounds__(kB3Threads) void pack3_kernel(const int8_t* __restr
     }
 }
 
-// Sum over the 64 lanes of a wave; the result is wave-uniform.
-__device__ __forceinline__ int wave_reduce_dpp3(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
 // Codes of one packed word: c[i] = digit i of bytes 0..3 (weights 4i .. 4i+3).
 __device__ __forceinline__ void decode_word(uint32_t w, int c[5]) {
     uint32_t lo = w & 0x00FF00FFu;         // bytes 0 and 2, one per 16-bit lane
@@ -171,7 +161,7 @@ __global__ __launch_bounds__(kB3Threads) void gemv3_kernel(const int8_t* __restr
         const float sc = (row < M) ? out_scale(beta, gamma[row]) : 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int tot = wave_reduce_dpp3(part[r][m] - spart[m]);
+            const int tot = wave_sum_dpp(part[r][m] - spart[m]);
             const int n = n0 + r;
             if (lane == 0 && n < N && row < M) {
                 if (y) y[(int64_t)row * N + n] = (float)tot * sc;
@@ -284,7 +274,7 @@ __global__ __launch_bounds__(kB3Waves * kWave) void gemv3_mfma_kernel(
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
         if (m < M) {
-            const int sm = wave_reduce_dpp3(spart[m]);
+            const int sm = wave_sum_dpp(spart[m]);
             if (lane == 0) s_wave[wv][m] = sm;
         }
     }

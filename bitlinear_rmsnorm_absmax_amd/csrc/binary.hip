@@ -82,16 +82,6 @@ __global__ __launch_bounds__(kB1Threads) void pack1_kernel(const int8_t* __restr
     }
 }
 
-// Sum over the 64 lanes of a wave; the result is wave-uniform.
-__device__ __forceinline__ int wave_reduce_dpp1(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
 // Decode product on 1-bit weights (K % 64 == 0).  A wave owns R consecutive weight rows;
 // lane l streams the 8-byte units (2 words = 64 weights) l, l+64, ... of each
 // row (512 contiguous bytes per wave-wide load) and the 64 activation bytes
@@ -163,7 +153,7 @@ __global__ __launch_bounds__(kB1Threads) void gemv1_kernel(const int8_t* __restr
         const float sc = (row < M) ? out_scale(beta, gamma[row]) : 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int tot = wave_reduce_dpp1(2 * part[r][m] - spart[m]);
+            const int tot = wave_sum_dpp(2 * part[r][m] - spart[m]);
             const int n = n0 + r;
             if (lane == 0 && n < N && row < M) {
                 y[(int64_t)row * N + n] = (float)tot * sc;

@@ -43,16 +43,7 @@
 namespace bl {
 namespace {
 
-constexpr int kDecWaves = 8;
-constexpr int kDecLdsMax = 160 * 1024;
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
-                                     16, 0, 0);
-#endif
-}
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt and expcnt any
 constexpr int vm_wait_imm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | (0xF << 8); }
@@ -261,12 +252,6 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     }
 }
 
-// LDS bytes: the activation block rounded up to whole 1 KB copies, the
-// reduction buffer, and 16 activation sums and 16 output scales per group.
-int decode_a_bytes(int M, int K) { return ((M * K + 1023) / 1024) * 1024; }
-size_t decode_lds_bytes(int M, int K, int ntw, int G = 1) {
-    return (size_t)decode_a_bytes(M, K) + (size_t)kDecWaves * ntw * 4 * kWave * 4 + 2 * 16 * 4 * (size_t)G;
-}
 
 template <int CT, int NTW, int B, bool ONEBIT, int G>
 hipError_t launch_ctb(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
@@ -310,17 +295,6 @@ hipError_t launch_ct_groups(const int8_t* xq, const float* gamma, int M, int K, 
     return hipErrorInvalidValue;
 }
 
-// K parts of the widths below, widest first: <8,2> 2, <4,2> 4, <2,1> 4, <1,1> 8.
-// Grouped launches need KS % G == 0 and (K/256) % KS == 0 so that every wave's
-// K range lies inside one group.
-int grouped_width(int tiles, int G, int nchunks) {
-    const int ct[4] = {8, 4, 2, 1}, ks[4] = {2, 4, 4, 8}, min_tiles[4] = {8 * 200, 4 * 200, 2 * 200, 0};
-    int pick = -1;
-    for (int i = 3; i >= 0; --i)  // the widest fitting config that still leaves >= 200 workgroups
-        if (ks[i] % G == 0 && nchunks % ks[i] == 0 && (pick < 0 || tiles >= min_tiles[i])) pick = i;
-    return pick < 0 ? -1 : ct[pick];
-}
-
 template <bool ONEBIT>
 hipError_t launch_widths(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
                          int N, float beta, float* y, int32_t* acc, hipStream_t s) {
@@ -338,18 +312,6 @@ hipError_t launch_widths(const int8_t* xq, const float* gamma, int M, int K, con
 }
 
 }  // namespace
-
-bool decode_lds_supports(int M, int K, int N) {
-    return M >= 1 && M <= 16 && K >= 256 && K % 256 == 0 && N > 0 &&
-           decode_lds_bytes(M, K, 2) <= (size_t)kDecLdsMax;
-}
-
-bool decode_lds_grouped_supports(int M, int K, int G, int N) {
-    if ((G != 2 && G != 4 && G != 8) || M < 1 || M > 16 || N <= 0 || K % 256 != 0 || K % G != 0 || (K / G) % 256 != 0)
-        return false;
-    return grouped_width((N + 15) / 16, G, K >> 8) > 0 &&
-           decode_lds_bytes(M, K, 2, G) <= (size_t)kDecLdsMax;
-}
 
 hipError_t launch_decode_lds_grouped(const int8_t* xq, const float* gamma, int M, int K, int G,
                                      const uint32_t* wp, int N, const float* beta_g, float* y,

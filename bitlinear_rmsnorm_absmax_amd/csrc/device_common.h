@@ -66,6 +66,29 @@ __device__ __forceinline__ double wave_sum_d(double v) {
     return v;
 }
 
+// Sum of an int over the 64 lanes of a wave with DPP row operations (quad
+// permutes, then rotations by 4 and 8 inside each row of 16 lanes) and the
+// four row results read back with v_readlane; the result is wave-uniform.
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
+// Copy 16 bytes per lane from global memory straight into LDS at
+// lds_wave_base + 16 * lane (global_load_lds_dwordx4; the base is
+// wave-uniform and goes to M0).  The builtin exists only in the device pass;
+// the host pass compiles kernels to launch stubs and must not see it.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
+                                     16, 0, 0);
+#endif
+}
+
 __device__ __forceinline__ int wave_sum_i(int v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -38,17 +38,6 @@ constexpr int kXcds = 8;
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int bswz(int col, int h) { return h ^ ((col >> 3) & 1); }
 
-// Copy 16 bytes per lane from global memory straight into LDS at
-// lds_wave_base + 16 * lane (the base is wave-uniform and goes to M0).
-// The builtin only exists in the device pass; the host pass compiles the
-// kernel to a launch stub and must not see it.
-__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave_base) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base,
-                                     16, 0, 0);
-#endif
-}
-
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= lgkm, expcnt any
 constexpr int waitcnt_imm(int vm, int lgkm) {

@@ -24,16 +24,6 @@ namespace {
 constexpr int kGvThreads = 256;
 constexpr int kGvWaves = kGvThreads / kWave;
 
-// Sum over the 64 lanes of a wave; the result is wave-uniform.
-__device__ __forceinline__ int wave_reduce_dpp(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
 // KS > 1 (few rows): the KS waves of a group share its R rows, wave ks taking
 // the units ks*64 + lane, (ks + KS)*64 + lane, ...; their exact int32 partial
 // sums meet in LDS and the group's first wave stores.
@@ -143,7 +133,7 @@ __global__ __launch_bounds__(kGvThreads) void gemv_valu_kernel(
 #pragma unroll
     for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int r = 0; r < R; ++r) tots[r][m] = wave_reduce_dpp(part[r][m] - spart[m]);
+        for (int r = 0; r < R; ++r) tots[r][m] = wave_sum_dpp(part[r][m] - spart[m]);
     if constexpr (KS > 1) {
         if (lane == 0) {
 #pragma unroll

@@ -242,17 +242,6 @@ __global__ void zero_gamma_kernel(float* gamma, int64_t M) {
 
 }  // namespace
 
-// Workgroups per row of the split quantiser: enough to put about 256
-// workgroups on the chip when the rows are few, each keeping at least 32
-// chunks (512 elements) of its own; 1 (the one-workgroup-per-row kernel) from
-// 128 rows up or for short rows.
-int quant_split_ways(int64_t M, int64_t K) {
-    if (M <= 0 || M >= 128) return 1;
-    const int64_t by_rows = 256 / M;
-    const int64_t by_len = (K / 16) / 32;
-    return (int)std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(by_rows, by_len), 64));
-}
-
 hipError_t launch_quant_act(const void* x, int bf16, int64_t M, int64_t K, const float* gain,
                             float eps, int8_t* q, float* gamma, hipStream_t s) {
     if (M == 0) return hipSuccess;

@@ -33,15 +33,6 @@ namespace {
 constexpr int kQWaves = kQuantThreads / kWave;  // waves that quantise
 constexpr int kFgRows = 4;                       // weight rows per wave
 
-__device__ __forceinline__ int wave_reduce_rows(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
-    v += __builtin_amdgcn_update_dpp(0, v, 0x124, 0xF, 0xF, false);  // row_ror:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);  // row_ror:8
-    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
-           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
-}
-
 template <Src S, bool RMS, int WAVES>
 __global__ __launch_bounds__(WAVES * kWave) void quant_gemv_kernel(
     RowSrc src, int K, const float* __restrict__ gain, float eps, const uint32_t* __restrict__ wp,
@@ -220,7 +211,7 @@ __global__ __launch_bounds__(WAVES * kWave) void quant_gemv_kernel(
     int av = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const int tot = wave_reduce_rows(part[r]) - S_tot;
+        const int tot = wave_sum_dpp(part[r]) - S_tot;
         if (lane == r) av = tot;
     }
     const int n = n0 + lane;
@@ -266,9 +257,6 @@ int fg_waves(int N) {
 
 }  // namespace
 
-bool quant_gemv_supports(int M, int K, int N) {
-    return M == 1 && K > 0 && K % 64 == 0 && K <= kFusedMaxK && N > 0 && N <= kFusedMaxN;
-}
 
 hipError_t launch_quant_gemv(const void* x, bool bf16, int K, const float* gain, float eps,
                              const uint32_t* wp, int N, float beta, float* y, int32_t* acc,

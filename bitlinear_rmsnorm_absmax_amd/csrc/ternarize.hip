@@ -169,10 +169,6 @@ hipError_t launch_pairwise_mean(const float* W, int64_t L, int64_t N, int64_t K,
     return hipGetLastError();
 }
 
-size_t pairwise_scratch_bytes(int64_t L, int group) {
-    const int64_t n = (L + group - 1) / group;
-    return (size_t)8 * (size_t)(n + (n > 64 ? (n + 63) / 64 : 0));
-}
 
 hipError_t launch_ternarize(const float* W, int64_t N, int64_t K, uint32_t* packed, int8_t* codes,
                             float* beta32, double* beta64, hipStream_t s) {

@@ -38,9 +38,12 @@ def build() -> str:
 def _load() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
+        # ORACLE_LIB: another build of the same source (the sanitizer run of
+        # the pin tests loads an AddressSanitizer / UBSan build through it)
+        path = os.environ.get("ORACLE_LIB", _LIB_PATH)
+        if path == _LIB_PATH and not os.path.exists(_LIB_PATH):
             build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        lib = ctypes.CDLL(path)
         sig = {
             "oracle_bf16_to_f32": [_c_p, _i64, _c_p],
             "oracle_quant_act": [_c_p, _i64, _i64, _c_p, _c_p],
