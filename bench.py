@@ -95,9 +95,9 @@ def parse():
                     help="no GPU: write profiles/kernels_<workload>.md from a rocprofv3 "
                          "--kernel-trace run of COMMAND (a bench.py command line with the same "
                          "step, warmup, per-launch and config arguments as this one)")
-    ap.add_argument("--traffic-write", nargs=3, metavar=("JSON", "FETCH_DIR", "WRITE_DIR"),
-                    help="no GPU: turn the two counter runs of --traffic-probe into "
-                         "profiles/traffic_<workload>.md")
+    ap.add_argument("--traffic-write", nargs="+", metavar="PATH",
+                    help="no GPU: JSON FETCH_DIR WRITE_DIR [MFMA_DIR]: turn the counter runs of "
+                         "--traffic-probe into profiles/traffic_<workload>.md")
     return ap.parse_args()
 
 
@@ -337,6 +337,20 @@ def read_traffic(workload_name: str, call: str):
     return float(m_val.group(1))
 
 
+def read_mfma_util(workload_name: str, call: str):
+    """Matrix-pipe utilisation of `call` from the committed counter summary,
+    only if it was taken on the current kernel sources (else None)."""
+    path = os.path.join(PROFILES, f"traffic_{workload_name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"source_digest:\s*(\w+)", text)
+    m_val = re.search(rf"mfma_util\[{re.escape(call)}\]:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_val or m_src.group(1) != kernel_source_digest():
+        return None
+    return float(m_val.group(1))
+
+
 def traffic_probe(args, torch, ops, dev):
     """One eager step (every call once, in step order), then the calibration
     copy: an elementwise kernel that reads COPY_BYTES and writes COPY_BYTES."""
@@ -344,15 +358,24 @@ def traffic_probe(args, torch, ops, dev):
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     seq = []
-    ops(0, lambda name, *a, **kw: seq.append(name) or True)
+    rec = RunAll()
+
+    def run(name, *a, **kw):
+        seq.append(name)
+        return rec(name, *a, **kw)
+    ops(0, run)
     torch.neg(src, out=dst)
     torch.cuda.synchronize()
+    info = {k: dict(ops=v["ops"], alg_bytes=v["alg_bytes"]) for k, v in rec.info.items()}
     with open(args.traffic_probe, "w") as f:
         json.dump(dict(workload=workloads.WORKLOADS[args.workload].name, calls=seq,
-                       copy_bytes=COPY_BYTES, copy_kernel="neg"), f)
+                       copy_bytes=COPY_BYTES, copy_kernel="neg", info=info), f)
 
 
-def _counter_rows(d: str, counter: str):
+def _counter_rows(d: str, counter: str, reduce: str = "sum"):
+    """[(kernel name, value)] per dispatch, in dispatch order: the counter's
+    instances summed (or their maximum, for per-engine clocks like
+    GRBM_GUI_ACTIVE)."""
     import csv
     import glob
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -364,9 +387,15 @@ def _counter_rows(d: str, counter: str):
             if r["Counter_Name"] != counter:
                 continue
             did = int(r["Dispatch_Id"])
-            name, v = per.get(did, (r["Kernel_Name"], 0.0))
-            per[did] = (name, v + float(r["Counter_Value"]))
+            name, v = per.get(did, (r["Kernel_Name"], None))
+            x = float(r["Counter_Value"])
+            v = x if v is None else (v + x if reduce == "sum" else max(v, x))
+            per[did] = (name, v)
     return [per[k] for k in sorted(per)]
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+SIMD_NUM = 256 * 4
 
 
 def traffic_write(args):
@@ -374,7 +403,8 @@ def traffic_write(args):
     --traffic-probe: the last dispatches of each run are the probe's step and
     its copy; the counters (KiB per dispatch) are scaled by what they read for
     the copy of known size."""
-    probe_json, fdir, wdir = args.traffic_write
+    probe_json, fdir, wdir = args.traffic_write[:3]
+    mdir = args.traffic_write[3] if len(args.traffic_write) > 3 else None
     probe = json.load(open(probe_json))
     calls = probe["calls"]
 
@@ -388,9 +418,13 @@ def traffic_write(args):
             raise SystemExit(f"counter run holds {len(lib)} library dispatches, "
                              f"the probe made {len(calls)}")
         for call, (name, _) in zip(calls, lib):
-            want = ("quant_gemv" if call.startswith("quant_forward") else
-                    "quant_rows" if call.startswith(("quant", "silu")) else "_kernel")
-            if want not in name or (call.startswith("forward") and "quant_rows" in name):
+            if call.startswith("quant_forward"):
+                ok = "quant_gemv" in name or "quant_" in name
+            elif call.startswith(("quant", "silu")):
+                ok = "quant_rows" in name or "quant_split" in name
+            else:
+                ok = "_kernel" in name and "quant_" not in name
+            if not ok:
                 raise SystemExit(f"dispatch {name} does not match call {call}")
         return lib, rows[copies[-1]]
 
@@ -410,8 +444,11 @@ def traffic_write(args):
              f"python3 bench.py --workload {args.workload} --traffic-probe gpurun_out/probe.json",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- "
              f"python3 bench.py --workload {args.workload} --traffic-probe gpurun_out/probe.json",
+             *([f"rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d "
+                f"gpurun_out/pmc_mfma -o run -- python3 bench.py --workload {args.workload} "
+                "--traffic-probe gpurun_out/probe.json"] if mdir else []),
              f"python3 bench.py --workload {args.workload} --traffic-write gpurun_out/probe.json "
-             "gpurun_out/pmc_fetch gpurun_out/pmc_write",
+             "gpurun_out/pmc_fetch gpurun_out/pmc_write" + (" gpurun_out/pmc_mfma" if mdir else ""),
              "```", "",
              f"Calibration: an elementwise negation of {cb} bytes (reads {cb}, writes {cb}) "
              f"reads FETCH_SIZE {fcopy[1]:.0f} KiB and WRITE_SIZE {wcopy[1]:.0f} KiB; "
@@ -427,8 +464,29 @@ def traffic_write(args):
         short = short[:short.index(">(") + 1] if ">(" in short else short.split("(")[0]
         lines.append(f"| {call} | `{short}` | {fv:.0f} | {wv:.0f} | {b:.4g} |")
         vals.append((call, b))
+    mvals = []
+    if mdir:
+        mo = pick(_counter_rows(mdir, MFMA_COUNTERS[0]))[0]
+        mb = pick(_counter_rows(mdir, MFMA_COUNTERS[1]))[0]
+        mg = pick(_counter_rows(mdir, MFMA_COUNTERS[2], "max"))[0]
+        info = probe.get("info", {})
+        lines += ["", "MFMA counters (third run of the probe: `--pmc " + " ".join(MFMA_COUNTERS) +
+                  "`): int8 MFMA operations (SQ_INSTS_VALU_MFMA_MOPS_I8 x 512, against the "
+                  "algorithmic 2*M*N*K; the kernels pad M to their MFMA tile), matrix-pipe "
+                  f"utilisation SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {SIMD_NUM} SIMDs).", "",
+                  "| call | MFMA ops | 2*M*N*K | MFMA busy cycles (sum) | GRBM_GUI_ACTIVE | MFMA util |",
+                  "|---|---:|---:|---:|---:|---:|"]
+        for call, (_, ops), (_, busy), (_, gui) in zip(calls, mo, mb, mg):
+            if ops <= 0:
+                continue
+            alg = info.get(call, {}).get("ops", 0)
+            util = busy / (gui * SIMD_NUM) if gui > 0 else 0.0
+            lines.append(f"| {call} | {ops * 512:.4g} | {alg:.4g} | {busy:.4g} | {gui:.4g} | "
+                         f"{100 * util:.1f} % |")
+            mvals.append((call, util))
     lines += ["", f"source_digest: {kernel_source_digest()}", ""]
     lines += [f"traffic_bytes_per_launch[{c}]: {b:.6g}" for c, b in vals]
+    lines += [f"mfma_util[{c}]: {u:.4f}" for c, u in mvals]
     path = os.path.join(PROFILES, f"traffic_{wl.name}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -1181,6 +1239,8 @@ def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headl
     floor = floors(torch, bl, dev, s, d["wbytes"], per_launch)
     traffic = read_traffic(meta["workload"], dom)
     roof = roofline_of(d, traffic, floor)
+    if roof["bound"] == "mfma":
+        roof["mfma_util_counter"] = read_mfma_util(meta["workload"], dom)
     per_call = {}
     for k, v in kern.items():
         e = dict(avg_us=round(v["b2b_us"], 3), per_step=v["per_step"],

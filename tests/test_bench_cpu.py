@@ -125,3 +125,49 @@ def test_traffic_digest_covers_every_library_source():
     assert "gemm_dma.hip" in srcs and "api.cpp" in srcs and "mfma_epilogue.h" in srcs
     d = bench.kernel_source_digest()
     assert len(d) == 16 and d == bench.kernel_source_digest()
+
+
+def test_mfma_counters_give_utilisation(tmp_path, monkeypatch):
+    """The MFMA pass: ops = MOPS x 512, utilisation = busy cycles summed over
+    SIMDs / (GRBM_GUI_ACTIVE, the maximum over its instances, x 1024)."""
+    bench = load_bench()
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    calls = ["quant_act_M512", "forward_M512"]
+    probe = tmp_path / "probe.json"
+    probe.write_text(json.dumps(dict(workload="sweep_k8192_n28672", calls=calls,
+                                     copy_bytes=bench.COPY_BYTES, copy_kernel="neg",
+                                     info={"forward_M512": dict(ops=240518168576, alg_bytes=1)})))
+    kib = bench.COPY_BYTES / 1024
+    seq = [("void bl::quant_rows_kernel<0, false, false>(int)", [1.0]),
+           ("void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", [1.0]),
+           ("void at::native::neg_kernel(int)", [kib])]
+    write_csv(tmp_path / "f", "FETCH_SIZE", seq)
+    write_csv(tmp_path / "w", "WRITE_SIZE", seq)
+    d = tmp_path / "m"
+    os.makedirs(d)
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, FIELDS)
+        w.writeheader()
+        rows = [(1, "void bl::quant_rows_kernel<0, false, false>(int)", "SQ_INSTS_VALU_MFMA_MOPS_I8", [0.0]),
+                (1, "void bl::quant_rows_kernel<0, false, false>(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [0.0]),
+                (1, "void bl::quant_rows_kernel<0, false, false>(int)", "GRBM_GUI_ACTIVE", [10.0, 10.0]),
+                (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "SQ_INSTS_VALU_MFMA_MOPS_I8",
+                 [240518168576 / 512 / 2] * 2),
+                (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [51200.0] * 10),
+                (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "GRBM_GUI_ACTIVE", [1000.0, 990.0]),
+                (3, "void at::native::neg_kernel(int)", "SQ_INSTS_VALU_MFMA_MOPS_I8", [0.0]),
+                (3, "void at::native::neg_kernel(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [0.0]),
+                (3, "void at::native::neg_kernel(int)", "GRBM_GUI_ACTIVE", [5.0])]
+        for did, name, cn, vals in rows:
+            for v in vals:
+                row = {k: 0 for k in FIELDS}
+                row.update(Dispatch_Id=did, Kernel_Name=name, Counter_Name=cn, Counter_Value=f"{v:.6f}")
+                w.writerow(row)
+    args = type("A", (), dict(traffic_write=[str(probe), str(tmp_path / "f"), str(tmp_path / "w"), str(d)],
+                              workload=5))()
+    bench.traffic_write(args)
+    # 10 x 51200 busy cycles / (1000 x 1024) = 0.5
+    assert bench.read_mfma_util("sweep_k8192_n28672", "forward_M512") == pytest.approx(0.5)
+    assert bench.read_mfma_util("sweep_k8192_n28672", "quant_act_M512") is None
+    text = (tmp_path / "traffic_sweep_k8192_n28672.md").read_text()
+    assert "| forward_M512 | 2.405e+11 | 2.405e+11 |" in text
