@@ -374,8 +374,8 @@ def traffic_probe(args, torch, ops, dev):
 
 def _counter_rows(d: str, counter: str, reduce: str = "sum"):
     """[(kernel name, value)] per dispatch, in dispatch order: the counter's
-    instances summed (or their maximum, for per-engine clocks like
-    GRBM_GUI_ACTIVE)."""
+    instances summed, or (reduce="duration") the dispatch's duration in
+    microseconds from its timestamps."""
     import csv
     import glob
     files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
@@ -388,14 +388,24 @@ def _counter_rows(d: str, counter: str, reduce: str = "sum"):
                 continue
             did = int(r["Dispatch_Id"])
             name, v = per.get(did, (r["Kernel_Name"], None))
-            x = float(r["Counter_Value"])
-            v = x if v is None else (v + x if reduce == "sum" else max(v, x))
+            if reduce == "duration":
+                v = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            else:
+                x = float(r["Counter_Value"])
+                v = x if v is None else v + x
             per[did] = (name, v)
     return [per[k] for k in sorted(per)]
 
 
+# SQ_VALU_MFMA_BUSY_CYCLES counts, per SIMD, the cycles its matrix pipe is
+# occupied: one 32x32x32 int8 MFMA (65536 operations) occupies it 32 cycles,
+# so the busy cycles are the operations / 2048 per SIMD, independent of
+# stalls; the utilisation is those cycles over the dispatch's duration at the
+# 2.4 GHz peak engine clock (GRBM_GUI_ACTIVE is recorded too; under counter
+# collection it also counts the collection's own cycles).
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_I8", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
 SIMD_NUM = 256 * 4
+PEAK_CLOCK_MHZ = 2400.0
 
 
 def traffic_write(args):
@@ -468,20 +478,24 @@ def traffic_write(args):
     if mdir:
         mo = pick(_counter_rows(mdir, MFMA_COUNTERS[0]))[0]
         mb = pick(_counter_rows(mdir, MFMA_COUNTERS[1]))[0]
-        mg = pick(_counter_rows(mdir, MFMA_COUNTERS[2], "max"))[0]
+        md = pick(_counter_rows(mdir, MFMA_COUNTERS[1], "duration"))[0]
         info = probe.get("info", {})
         lines += ["", "MFMA counters (third run of the probe: `--pmc " + " ".join(MFMA_COUNTERS) +
                   "`): int8 MFMA operations (SQ_INSTS_VALU_MFMA_MOPS_I8 x 512, against the "
-                  "algorithmic 2*M*N*K; the kernels pad M to their MFMA tile), matrix-pipe "
-                  f"utilisation SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {SIMD_NUM} SIMDs).", "",
-                  "| call | MFMA ops | 2*M*N*K | MFMA busy cycles (sum) | GRBM_GUI_ACTIVE | MFMA util |",
+                  "algorithmic 2*M*N*K; decode kernels pad M to their 16-row MFMA tile), the "
+                  "matrix pipe's busy cycles per SIMD (SQ_VALU_MFMA_BUSY_CYCLES summed over "
+                  f"{SIMD_NUM} SIMDs / {SIMD_NUM}: operations / 2048 per SIMD, independent of "
+                  "stalls), the dispatch's duration in the same run, and the utilisation: busy "
+                  f"cycles / (duration x {PEAK_CLOCK_MHZ / 1000:.1f} GHz peak clock).", "",
+                  "| call | MFMA ops | 2*M*N*K | busy cycles per SIMD | duration us | MFMA util at peak clock |",
                   "|---|---:|---:|---:|---:|---:|"]
-        for call, (_, ops), (_, busy), (_, gui) in zip(calls, mo, mb, mg):
+        for call, (_, ops), (_, busy), (_, dur) in zip(calls, mo, mb, md):
             if ops <= 0:
                 continue
             alg = info.get(call, {}).get("ops", 0)
-            util = busy / (gui * SIMD_NUM) if gui > 0 else 0.0
-            lines.append(f"| {call} | {ops * 512:.4g} | {alg:.4g} | {busy:.4g} | {gui:.4g} | "
+            per_simd = busy / SIMD_NUM
+            util = per_simd / (dur * PEAK_CLOCK_MHZ) if dur > 0 else 0.0
+            lines.append(f"| {call} | {ops * 512:.4g} | {alg:.4g} | {per_simd:.4g} | {dur:.2f} | "
                          f"{100 * util:.1f} % |")
             mvals.append((call, util))
     lines += ["", f"source_digest: {kernel_source_digest()}", ""]

@@ -128,8 +128,8 @@ def test_traffic_digest_covers_every_library_source():
 
 
 def test_mfma_counters_give_utilisation(tmp_path, monkeypatch):
-    """The MFMA pass: ops = MOPS x 512, utilisation = busy cycles summed over
-    SIMDs / (GRBM_GUI_ACTIVE, the maximum over its instances, x 1024)."""
+    """The MFMA pass: ops = MOPS x 512, utilisation = busy cycles per SIMD
+    (summed over the 1024 SIMDs / 1024) / (dispatch duration x 2.4 GHz)."""
     bench = load_bench()
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     calls = ["quant_act_M512", "forward_M512"]
@@ -153,7 +153,7 @@ def test_mfma_counters_give_utilisation(tmp_path, monkeypatch):
                 (1, "void bl::quant_rows_kernel<0, false, false>(int)", "GRBM_GUI_ACTIVE", [10.0, 10.0]),
                 (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "SQ_INSTS_VALU_MFMA_MOPS_I8",
                  [240518168576 / 512 / 2] * 2),
-                (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [51200.0] * 10),
+                (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [61440.0] * 1024),
                 (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "GRBM_GUI_ACTIVE", [1000.0, 990.0]),
                 (3, "void at::native::neg_kernel(int)", "SQ_INSTS_VALU_MFMA_MOPS_I8", [0.0]),
                 (3, "void at::native::neg_kernel(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [0.0]),
@@ -161,12 +161,13 @@ def test_mfma_counters_give_utilisation(tmp_path, monkeypatch):
         for did, name, cn, vals in rows:
             for v in vals:
                 row = {k: 0 for k in FIELDS}
-                row.update(Dispatch_Id=did, Kernel_Name=name, Counter_Name=cn, Counter_Value=f"{v:.6f}")
+                row.update(Dispatch_Id=did, Kernel_Name=name, Counter_Name=cn, Counter_Value=f"{v:.6f}",
+                           Start_Timestamp=1000000, End_Timestamp=1000000 + (51200 if did == 2 else 1000))
                 w.writerow(row)
     args = type("A", (), dict(traffic_write=[str(probe), str(tmp_path / "f"), str(tmp_path / "w"), str(d)],
                               workload=5))()
     bench.traffic_write(args)
-    # 10 x 51200 busy cycles / (1000 x 1024) = 0.5
+    # 61440 busy cycles per SIMD / (51.2 us x 2400 cycles per us) = 0.5
     assert bench.read_mfma_util("sweep_k8192_n28672", "forward_M512") == pytest.approx(0.5)
     assert bench.read_mfma_util("sweep_k8192_n28672", "quant_act_M512") is None
     text = (tmp_path / "traffic_sweep_k8192_n28672.md").read_text()
