@@ -35,6 +35,24 @@ constexpr int BK = 128;
 
 constexpr int kXcds = 8;
 
+// Block -> output tile.  The hardware deals consecutive workgroups to the eight
+// XCDs in turn; renumbering puts each XCD's workgroups on consecutive tiles,
+// and the tiles run row tiles fastest, so the row tiles of one column range --
+// all the workgroups that read those packed weight columns -- share one XCD's
+// L2.  Measured against columns fastest (the tiles of one row range per XCD,
+// each weight column then fetched by several XCDs), bit-identical output:
+// M = 512, K = 8192, N = 28672 142.8 -> 140.1 us; M = 2048, K = 4096,
+// N = 11008 125.6 -> 123.1 us; M = 64 31.6 -> 31.4 us.  Returns m0, sets n0.
+__device__ __forceinline__ int tile_origin(int blk, int tiles_n, int tiles_total, int BM, int BN,
+                                           int& n0) {
+    int b = blk;
+    const int full = (tiles_total / kXcds) * kXcds;
+    if (b < full) b = (b % kXcds) * (full / kXcds) + b / kXcds;
+    const int tiles_m = tiles_total / tiles_n;
+    n0 = (b / tiles_m) * BN;
+    return (b % tiles_m) * BM;
+}
+
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int bswz(int col, int h) { return h ^ ((col >> 3) & 1); }
 
@@ -84,11 +102,8 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     char* ring = lds + kgrp * STAGES * C::kStageBytes;
     const int l32 = lane & 31, h = lane >> 5;
 
-    int b = blockIdx.x;
-    const int full = (tiles_total / kXcds) * kXcds;
-    if (b < full) b = (b % kXcds) * (full / kXcds) + b / kXcds;
-    const int m0 = (b / tiles_n) * C::BM;
-    const int n0 = (b % tiles_n) * C::BN;
+    int n0;
+    const int m0 = tile_origin(blockIdx.x, tiles_n, tiles_total, C::BM, C::BN, n0);
     const int WR = K >> 4;
     const int KT = K / BK / KSP;  // K steps of each group (K % (BK * KSP) == 0)
 
@@ -273,11 +288,8 @@ void gemm_pipe_kernel(const int8_t* __restrict__ xq, const float* __restrict__ g
     const int wm = wv / WN, wn = wv % WN;
     const int l32 = lane & 31, h = lane >> 5;
 
-    int b = blockIdx.x;
-    const int full = (tiles_total / kXcds) * kXcds;
-    if (b < full) b = (b % kXcds) * (full / kXcds) + b / kXcds;
-    const int m0 = (b / tiles_n) * C::BM;
-    const int n0 = (b % tiles_n) * C::BN;
+    int n0;
+    const int m0 = tile_origin(blockIdx.x, tiles_n, tiles_total, C::BM, C::BN, n0);
     const int WR = K >> 4;
     const int KT = K / BK;
 
