@@ -182,9 +182,9 @@ def build_plan(args, torch, bl, dev, wid):
             raise RuntimeError(bl.last_error())
 
     def fused(M, K, N):
-        # bitlinear_quant_forward runs as one kernel for one token, K % 64 == 0,
-        # K <= 16384, N <= 16384 (--unfused times the two calls instead)
-        return not args.unfused and M == 1 and K % 64 == 0 and K <= 16384 and N <= 16384
+        # bitlinear_quant_forward as one kernel (one token; --unfused times the
+        # two calls instead)
+        return not args.unfused and lib.bitlinear_quant_forward_one_launch(M, K, N) == 1
 
     meta = {"workload": wl.name, "K": wl.K, "N": wl.N, "M": list(wl.ms)}
     if wl.glu_f:

@@ -44,6 +44,7 @@ _SIGNATURES = {
     "bitlinear_forward_grouped": [_vp, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
     "bitlinear_ternarize_grouped": [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp],
     "bitlinear_forward_grouped_one_launch": [_i64, _i64, _i64, _i64],
+    "bitlinear_quant_forward_one_launch": [_i64, _i64, _i64],
     "bitlinear_pack_weights3": [_vp, _i64, _i64, _vp, _vp, _vp],
     "bitlinear_forward3": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _vp],
     "bitlinear_floor_empty": [_vp],

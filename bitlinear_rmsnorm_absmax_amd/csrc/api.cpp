@@ -428,6 +428,11 @@ bitlinear_status_t bitlinear_forward_grouped(const int8_t* x_q, const float* gam
     return from_hip(bl::launch_group_sum(acc, gamma, beta, M, N, G, y, stream), fn);
 }
 
+int bitlinear_quant_forward_one_launch(int64_t M, int64_t K, int64_t N) {
+    if (M != 1 || K < 1 || K > BITLINEAR_MAX_K || N < 1 || N > kMaxN) return 0;
+    return bl::quant_gemv_supports((int)M, (int)K, (int)N) ? 1 : 0;
+}
+
 int bitlinear_forward_grouped_one_launch(int64_t M, int64_t K, int64_t G, int64_t N) {
     if (M < 1 || M > 16 || N < 1 || N > kMaxN || K < 256 || K > BITLINEAR_MAX_K || G < 2 || G > 8)
         return 0;

@@ -142,6 +142,10 @@ bitlinear_status_t bitlinear_quant_forward(const void* x, bitlinear_dtype_t x_dt
                                            int8_t* x_q, float* gamma, float* y, int32_t* acc,
                                            hipStream_t stream);
 
+/* 1 if bitlinear_quant_forward runs this shape as one kernel, else 0 (the two
+ * calls).  Host-only, no HIP call. */
+int bitlinear_quant_forward_one_launch(int64_t M, int64_t K, int64_t N);
+
 /* bitlinear_forward with an explicit kernel (bitlinear_path_t).  A path that
  * cannot take this M (GEMV: M > 4, SKINNY: M > 64) returns BITLINEAR_ERR_VALUE. */
 bitlinear_status_t bitlinear_forward_path(const int8_t* x_q, const float* gamma, int64_t M,

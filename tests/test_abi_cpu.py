@@ -23,7 +23,7 @@ def test_every_declared_symbol_is_exported():
         "bitlinear_ternarize",
         "bitlinear_binarize", "bitlinear_pack_weights1", "bitlinear_forward1",
         "bitlinear_quant_act_grouped", "bitlinear_forward_grouped", "bitlinear_ternarize_grouped",
-        "bitlinear_forward_grouped_one_launch", "bitlinear_pack_weights3", "bitlinear_forward3",
+        "bitlinear_forward_grouped_one_launch", "bitlinear_quant_forward_one_launch", "bitlinear_pack_weights3", "bitlinear_forward3",
         "bitlinear_floor_empty", "bitlinear_floor_stream_read",
         "bitlinear_last_error", "bitlinear_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
@@ -351,6 +351,18 @@ def _tg(W=FAKE, N=4, K=256, G=2, wp=FAKE, codes=None, b=FAKE, b64=FAKE):
 def test_ternarize_grouped_rejects(kw, status, msg):
     assert _tg(**kw) == status
     assert msg in bl.last_error()
+
+
+def test_quant_forward_one_launch_query():
+    q = bl.lib.bitlinear_quant_forward_one_launch
+    assert q(1, 4096, 11008) == 1
+    assert q(1, 16384, 16384) == 1
+    assert q(1, 64, 1) == 1
+    assert q(1, 8192, 28672) == 0         # past 16384 rows: the two calls
+    assert q(1, 16448, 40) == 0           # the codes of a longer token do not fit the LDS copy
+    assert q(1, 1040, 77) == 0            # K not a multiple of 64
+    assert q(2, 4096, 1000) == 0          # several tokens
+    assert q(1, 0, 10) == 0 and q(1, 64, 0) == 0 and q(1, 64, -1) == 0
 
 
 def test_grouped_one_launch_query():

@@ -1104,7 +1104,8 @@ QFWD_CASES = [(1, 64, 1, "f32", None), (1, 2048, 1000, "bf16", "unit"),
               (1, 16384, 300, "f32", "rand"), (1, 2560, 6912, "f32", "unit"),
               (1, 1024, 4096, "f32", None), (1, 1024, 4097, "bf16", None),
               (1, 512, 8193, "f32", "unit"), (1, 512, 16384, "f32", None),
-              (1, 256, 16385, "f32", None),
+              (1, 256, 16385, "f32", None), (1, 8192, 28672, "f32", None),
+              (1, 4096, 16385, "bf16", "unit"),
               (1, 16448, 40, "f32", None), (1, 1040, 77, "bf16", "rand"),
               (3, 4096, 500, "bf16", "rand"), (16, 2560, 700, "f32", None),
               # 2..4 tokens on the LDS decode route (K >= 4096) at every tile
@@ -1133,6 +1134,8 @@ def test_quant_forward_parity(dev, M, K, N, dt, gain_kind):
     wp = gpu_pack(w, dev)
     outs = dict(y=Guard((M, N), torch.float32, dev), q=Guard((M, K), torch.int8, dev),
                 g=Guard((M,), torch.float32, dev), acc=Guard((M, N), torch.int32, dev))
+    one = M == 1 and K % 64 == 0 and K <= 16384 and N <= 16384
+    assert bl.lib.bitlinear_quant_forward_one_launch(M, K, N) == int(one)
     st = bl.lib.bitlinear_quant_forward(
         xd.data_ptr(), bl.BF16 if dt == "bf16" else bl.F32, M, K, None if gd is None else gd.data_ptr(),
         ctypes.c_float(1e-6), wp.data_ptr(), N, ctypes.c_float(float(beta)), outs["q"].t.data_ptr(),
