@@ -45,6 +45,20 @@ __device__ __forceinline__ v4i unpack_codes(uint32_t w) {
     return r;
 }
 
+// Signed weights w = c - 1 (-1, 0, +1) of packed word `w`, same byte order as
+// unpack_codes: each masked code byte (0, 1, 2) selects byte c of the table
+// 0x000100FF (v_perm_b32), giving 0xFF, 0x00 or 0x01.  A product on these
+// needs no activation-sum correction.
+__device__ __forceinline__ v4i unpack_signed(uint32_t w) {
+    constexpr uint32_t kTable = 0x000100FFu;
+    v4i r;
+    r.x = (int)__builtin_amdgcn_perm(0u, kTable, w & 0x03030303u);
+    r.y = (int)__builtin_amdgcn_perm(0u, kTable, (w >> 2) & 0x03030303u);
+    r.z = (int)__builtin_amdgcn_perm(0u, kTable, (w >> 4) & 0x03030303u);
+    r.w = (int)__builtin_amdgcn_perm(0u, kTable, (w >> 6) & 0x03030303u);
+    return r;
+}
+
 // Sum of the 16 signed bytes of a v4i.
 __device__ __forceinline__ int byte_sum16(v4i a, int acc) {
     acc = __builtin_amdgcn_sdot4(a.x, 0x01010101, acc, false);

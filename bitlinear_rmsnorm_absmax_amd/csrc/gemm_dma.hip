@@ -1,9 +1,11 @@
 // Prefill GEMM on int8 MFMA with an LDS ring fed by direct global->LDS loads
 // (K a multiple of 128).
 //
-// Arithmetic as in the other forward kernels (unite.ai BitNet.cpp article, 3.
-// BitLinear-Betrieb): v_mfma_i32_32x32x32_i8 on the 2-bit codes c = w + 1 and
-// acc = D - S_m, S_m the sum of the token's int8 activations.
+// Arithmetic (unite.ai BitNet.cpp article, 3. BitLinear-Betrieb):
+// v_mfma_i32_32x32x32_i8; the ring kernel multiplies the signed weights
+// w = c - 1 (unpack_signed), so acc = D directly, while the pipelined kernel
+// multiplies the 2-bit codes c = w + 1 and removes acc = D - S_m with S_m the
+// sum of the token's int8 activations.  Both are exact integer sums.
 //
 // Pipeline: the activation tile (BM rows x 128 bytes) and packed weight tile
 // (BN columns x 8 words) of each K step are copied straight from global
@@ -21,9 +23,9 @@
 // Layout and operand mapping follow gemm_mfma.hip: activation rows of 128
 // bytes with chunk c stored at c ^ ((row & 7) ^ ((row >> 3) & 1)); weight
 // columns of 32 bytes with halves swapped when bit 3 of the column is set;
-// MFMA kk (0..3) of lane half h covers packed word 4h + kk.  S_m is summed
-// from the activation fragments the waves already hold, the K range split
-// between the WN waves that share a row.
+// MFMA kk (0..3) of lane half h covers packed word 4h + kk.  In the pipelined
+// kernel S_m is summed from the activation fragments the waves already hold,
+// the K range split between the WN waves that share a row.
 #include "device_common.h"
 #include "internal.h"
 #include "mfma_epilogue.h"
@@ -146,9 +148,6 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int t = 0; t < TN; ++t) acc[i][t] = v16i{};
-    int s_part[TM];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) s_part[i] = 0;
 
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p) issue(min(p, KT - 1), p);
@@ -180,12 +179,15 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
             }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
+            // signed weights: measured against the codes with in-loop row sums,
+            // bit-identical, M = 64, K = 8192, N = 28672 32.0 -> 30.2 us; M = 96,
+            // K = 4096, N = 11008 17.3 -> 16.3 us; M = 512, K = 6912, N = 2560
+            // 24.5 -> 23.7 us (the pipelined kernel below loses 2-5 % with them)
             v4i bf[TN];
 #pragma unroll
-            for (int t = 0; t < TN; ++t) bf[t] = unpack_codes(wq[t][kk]);
+            for (int t = 0; t < TN; ++t) bf[t] = unpack_signed(wq[t][kk]);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
-                if (kk % WN == wn) s_part[i] = byte_sum16(af[kk][i], s_part[i]);
 #pragma unroll
                 for (int t = 0; t < TN; ++t)
                     acc[i][t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kk][i], bf[t], acc[i][t], 0, 0, 0);
@@ -201,12 +203,11 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     // int per lane and register) to group 0, whose waves own the epilogue
     constexpr int kAccInts = C::kWaves * TM * TN * 16 * kWave;  // one group's accumulators
     int* red = reinterpret_cast<int*>(lds);
-    int* Sp = reinterpret_cast<int*>(lds) + (KSP > 1 ? kAccInts : 0);  // [KSP*WN][BM] partial row sums
-    int* S = Sp + KSP * WN * C::BM;          // [BM]
+    int* S = reinterpret_cast<int*>(lds) + (KSP > 1 ? kAccInts : 0);  // [BM], all 0 (no offset)
     float* Ssc = reinterpret_cast<float*>(S + C::BM);
-    static_assert(KSP == 1 || (int64_t)(kAccInts + (KSP * WN + 2) * C::BM) * 4 <=
-                                  (int64_t)KSP * STAGES * C::kStageBytes,
-                  "the accumulator exchange fits the rings");
+    static_assert((int64_t)((KSP > 1 ? kAccInts : 0) + 2 * C::BM) * 4 <=
+                      (int64_t)KSP * STAGES * C::kStageBytes,
+                  "the accumulator exchange and the row tables fit the rings");
     if constexpr (KSP > 1) {
         for (int g = 1; g < KSP; ++g) {
             if (kgrp == g) {
@@ -231,13 +232,7 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
             __syncthreads();
         }
     }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int sv = s_part[i] + __shfl_xor(s_part[i], 32, kWave);
-        if (h == 0) Sp[(kgrp * WN + wn) * C::BM + wm * TM * 32 + 32 * i + l32] = sv;
-    }
-    __syncthreads();
-    epilogue_tables(Sp, KSP * WN, C::BM, m0, M, gamma, beta, S, Ssc, tid, KSP * C::kThreads);
+    epilogue_tables(nullptr, 0, C::BM, m0, M, gamma, beta, S, Ssc, tid, KSP * C::kThreads);
     __syncthreads();
     if (kgrp == 0)
         store_tiles<TM, TN>(acc, S, Ssc, wm * TM * 32, wn * TN * 32, m0, n0, M, N, y, acc_out, lane);
