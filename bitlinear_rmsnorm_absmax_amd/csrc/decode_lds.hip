@@ -201,20 +201,28 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
         // a stream of batches, the next one's loads issued before the current
         // one is multiplied (a wave keeps at most 2 B NTW loads in flight, so
         // load issue does not stall on the compute unit's outstanding-request
-        // limit); the loads past the range re-read the last chunk
+        // limit); the loads past the range re-read the last chunk.  Two
+        // batches a trip with no exit in between, and a scheduling barrier
+        // after every step: otherwise the compiler sinks a batch's loads below
+        // the multiplies and rotates the loop so that it waits for all loads
+        // (vmcnt(0)) at its head, and no load is in flight while a batch is
+        // multiplied.
         wvec b0[B][NTW], b1[B][NTW];
+        const int nb = (c_end - c_begin + B - 1) / B;  // batches, > 1 here
         load_batch(c_begin, b0);
         publish();
-        for (int cb = c_begin;;) {
+        int cb = c_begin;
+        for (int i = 0; i + 2 <= nb; i += 2, cb += 2 * B) {
             load_batch(cb + B, b1);
+            __builtin_amdgcn_sched_barrier(0);
             mul_batch(cb, b0);
-            cb += B;
-            if (cb >= c_end) break;
-            load_batch(cb + B, b0);
-            mul_batch(cb, b1);
-            cb += B;
-            if (cb >= c_end) break;
+            __builtin_amdgcn_sched_barrier(0);
+            load_batch(cb + 2 * B, b0);
+            __builtin_amdgcn_sched_barrier(0);
+            mul_batch(cb + B, b1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        if (nb & 1) mul_batch(cb, b0);  // its loads were issued by the last trip
     }
 
     // lane (j, g) holds rows 4g + v of column j
