@@ -125,11 +125,10 @@ def forward_kernel(M: int, K: int, N: int) -> str:
         return "skinny_mfma_kernel"
     if K % 128 != 0:
         return "gemm_mfma_kernel"
-    if M >= 256 and -(-M // 128) * -(-N // 256) >= 256:
-        return "gemm_pipe_kernel"   # 128 x 256 tiles
-    if -(-M // 64) * -(-N // 128) <= 256 and K % 256 == 0:
-        return "gemm_dma_kernel"    # 64 x 128 tiles, two or three K groups
-    return "gemm_pipe_kernel"       # 128 x 128 tiles
+    # the LDS-ring kernel in all three tilings: 128 x 256 (M >= 256 and at
+    # least 256 such tiles), 64 x 128 with two or three K groups (at most 256
+    # such tiles, K % 256 == 0), else 128 x 128
+    return "gemm_dma_kernel"
 
 
 # ----------------------------------------------------------------------------- timers

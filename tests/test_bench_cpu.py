@@ -139,7 +139,7 @@ def test_mfma_counters_give_utilisation(tmp_path, monkeypatch):
                                      info={"forward_M512": dict(ops=240518168576, alg_bytes=1)})))
     kib = bench.COPY_BYTES / 1024
     seq = [("void bl::quant_rows_kernel<0, false, false>(int)", [1.0]),
-           ("void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", [1.0]),
+           ("void bl::gemm_dma_kernel<1, 4, 4, 2, 3, 1>(int)", [1.0]),
            ("void at::native::neg_kernel(int)", [kib])]
     write_csv(tmp_path / "f", "FETCH_SIZE", seq)
     write_csv(tmp_path / "w", "WRITE_SIZE", seq)
@@ -151,10 +151,10 @@ def test_mfma_counters_give_utilisation(tmp_path, monkeypatch):
         rows = [(1, "void bl::quant_rows_kernel<0, false, false>(int)", "SQ_INSTS_VALU_MFMA_MOPS_I8", [0.0]),
                 (1, "void bl::quant_rows_kernel<0, false, false>(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [0.0]),
                 (1, "void bl::quant_rows_kernel<0, false, false>(int)", "GRBM_GUI_ACTIVE", [10.0, 10.0]),
-                (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "SQ_INSTS_VALU_MFMA_MOPS_I8",
+                (2, "void bl::gemm_dma_kernel<1, 4, 4, 2, 3, 1>(int)", "SQ_INSTS_VALU_MFMA_MOPS_I8",
                  [240518168576 / 512 / 2] * 2),
-                (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [61440.0] * 1024),
-                (2, "void bl::gemm_pipe_kernel<1, 4, 4, 2>(int)", "GRBM_GUI_ACTIVE", [1000.0, 990.0]),
+                (2, "void bl::gemm_dma_kernel<1, 4, 4, 2, 3, 1>(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [61440.0] * 1024),
+                (2, "void bl::gemm_dma_kernel<1, 4, 4, 2, 3, 1>(int)", "GRBM_GUI_ACTIVE", [1000.0, 990.0]),
                 (3, "void at::native::neg_kernel(int)", "SQ_INSTS_VALU_MFMA_MOPS_I8", [0.0]),
                 (3, "void at::native::neg_kernel(int)", "SQ_VALU_MFMA_BUSY_CYCLES", [0.0]),
                 (3, "void at::native::neg_kernel(int)", "GRBM_GUI_ACTIVE", [5.0])]

@@ -297,7 +297,7 @@ def test_forward_parity(dev, path, M, N, K):
     assert_y_close(y, y_ref)
 
 
-# The GEMM takes 128 x 256 tiles on its pipelined ring loop once M >= 256 and
+# The GEMM takes 128 x 256 tiles on its ring loop once M >= 256 and
 # there are at least 256 such tiles: ragged M and N, and 1, 2, 3 and 5 K steps
 # of 128 (the prologue's re-reads past the end, and an odd ring rotation).
 WIDE_GEMM_CASES = [(257, 22053, 128), (256, 32769, 256), (300, 22016, 384), (384, 22016, 640)]
@@ -325,7 +325,7 @@ def test_gemm_small_tiles_parity(dev, M, N, K):
 
 
 # Neither of the above (K % 256 == 128, or more than 256 tiles of 64 x 128):
-# 128 x 128 tiles on the pipelined loop.
+# 128 x 128 tiles on the ring loop.
 MID_GEMM_CASES = [(100, 1000, 640), (200, 8300, 256), (129, 4200, 384), (255, 2100, 1152)]
 
 
@@ -360,12 +360,15 @@ def test_gemm_wide_tiles_parity(dev, M, N, K):
 # the LDS-staged decode kernel.  Cases cover its four workgroup widths (column
 # tiles of 16: < 400, >= 400, >= 800, >= 1600 tiles, and the old boundaries
 # 320, 640, 1280), ragged N, the largest K whose activation block fits in LDS
-# at 16 tokens (9216), and a zero token.
+# at 16 tokens (9216), and a zero token.  The streamed form (more than four
+# 256-chunks per wave, batches of two) runs with an odd number of batches and
+# a half-live last batch at (16, 333, 9216), (8, 25600, 6912) and
+# (5, 12800, 8704), with an even number and a half-live last batch at the last.
 DECODE_LDS_CASES = [(5, 1000, 256), (7, 5200, 512), (12, 10300, 1024), (16, 20500, 768),
                     (16, 333, 9216), (9, 2570, 2560), (13, 40, 4096), (6, 17, 256),
                     (2, 3000, 8192), (3, 700, 6912), (4, 129, 6144),
                     (8, 6401, 512), (11, 12800, 256), (9, 25700, 512), (4, 11008, 4096),
-                    (2, 6500, 4096), (3, 40, 4096)]
+                    (2, 6500, 4096), (3, 40, 4096), (8, 25600, 6912), (5, 12800, 8704)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_LDS_CASES)
