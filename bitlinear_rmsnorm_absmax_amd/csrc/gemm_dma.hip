@@ -279,15 +279,20 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
     // 128 x 128 route below: M = 64, K = 8192, N = 28672 47 -> 31 us; M = 96,
     // K = 4096, N = 11008 25 -> 17 us; M = 512, K = 6912, N = 2560 35 -> 24 us;
     // M = 512, K = 2560, N = 2560 18 -> 13 us; with more than 256 such tiles it
-    // loses (M = 200, K = 4096, N = 11008 27 -> 31 us).
+    // loses (M = 200, K = 4096, N = 11008 27 -> 31 us).  Each group's four
+    // waves sit side by side (64 rows x 32 columns each, so every unpacked
+    // weight word feeds two MFMAs); against 2 x 2 waves of 32 x 64, interleaved
+    // A/B, bit-identical: M = 64, K = 8192, N = 28672 30.9 -> 28.6 us; M = 32
+    // 29.1 -> 28.0 us; M = 512, K = 2560, N = 2560 11.3 -> 10.6 us; M = 96,
+    // K = 4096, N = 11008 15.3 both.
     const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
     // long K in a multiple of 3 steps: three K groups (12 waves, 3 a SIMD)
     // shorten each tile's sequence of steps further (M = 512, K = 6912,
-    // N = 2560: 22.8 -> 22.2 us)
+    // N = 2560: 22.8 -> 22.2 us; with the side-by-side waves 21.9 -> 19.5 us)
     if (tiles64 <= 256 && K >= 36 * BK && K % (3 * BK) == 0)
-        return launch_dcfg<2, 2, 1, 2, 3, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return launch_dcfg<1, 4, 2, 1, 3, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     if (tiles64 <= 256 && K % (2 * BK) == 0)
-        return launch_dcfg<2, 2, 1, 2, 3, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return launch_dcfg<1, 4, 2, 1, 3, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     // else 128 x 128 tiles (2 x 2 waves of 64 x 64)
     return launch_dcfg<2, 2, 2, 2, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
