@@ -140,6 +140,16 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
         }
     };
 
+    // the output scale's inputs of (group, row) tid, loaded before anything
+    // else and used only at publish: issued after the weight loads, their
+    // first use would wait for all of those
+    float g_mine = 0.0f, b_mine = beta;
+    if (tid < 16 * G) {
+        const int gi = tid >> 4, ri = tid & 15;
+        if (ri < M) g_mine = gamma[(int64_t)gi * M + ri];
+        if (beta_g) b_mine = beta_g[gi];
+    }
+
     // 1. activation copies of the whole workgroup, queued ahead of any weight load
     {
         // row = pos / WR and group = k / KG by multiply-high with a reciprocal
@@ -174,10 +184,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
         // inside a row does not change a sum; group gg holds slots
         // gg*KG/16 .. (gg+1)*KG/16 since KG is a multiple of 256)
         // output scales fl32(beta_g * gamma[g][m]) / 128 of every (group, row)
-        if (tid < 16 * G) {
-            const int gi = tid >> 4, ri = tid & 15;
-            Ssc[tid] = ri < M ? out_scale(beta_g ? beta_g[gi] : beta, gamma[(int64_t)gi * M + ri]) : 0.0f;
-        }
+        if (tid < 16 * G) Ssc[tid] = (tid & 15) < M ? out_scale(b_mine, g_mine) : 0.0f;
         // 32 / G lanes per (row, group): lane `sub` of group gg takes the
         // group's pieces sub, sub + 32/G, ...
         constexpr int L = 32 / G;
