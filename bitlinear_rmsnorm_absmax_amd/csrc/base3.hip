@@ -305,16 +305,23 @@ __global__ __launch_bounds__(kB3Waves * kWave) void gemv3_mfma_kernel(
         }
     };
     // a stream of batches, the next one's loads issued before the current one
-    // is multiplied
-    for (int sb = s_begin; sb < s_end;) {
-        if (sb + BATCH < s_end) load_batch(sb + BATCH, b1);
+    // is multiplied: two batches a trip, loads unconditional (clamped onto
+    // the last step, never multiplied) and a scheduling barrier after every
+    // step, so that the compiler neither sinks the loads below the multiplies
+    // nor waits for all of them at the loop head
+    const int nb = max(0, (s_end - s_begin + BATCH - 1) / BATCH);
+    int sb = s_begin;
+    for (int i = 0; i + 2 <= nb; i += 2, sb += 2 * BATCH) {
+        load_batch(sb + BATCH, b1);
+        __builtin_amdgcn_sched_barrier(0);
         mul_batch(sb, b0);
-        sb += BATCH;
-        if (sb >= s_end) break;
-        if (sb + BATCH < s_end) load_batch(sb + BATCH, b0);
-        mul_batch(sb, b1);
-        sb += BATCH;
+        __builtin_amdgcn_sched_barrier(0);
+        load_batch(sb + 2 * BATCH, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mul_batch(sb + BATCH, b1);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    if (nb & 1) mul_batch(sb, b0);  // its loads were issued by the last trip (or before the loop)
 
     // lane (j, g) holds tokens 4g + v of column j
 #pragma unroll
