@@ -198,39 +198,32 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
         for (int o = L / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
         if (sub == 0) Ssum[gg * 16 + r] = sum;
     };
-    if (c_end - c_begin <= B) {
-        // one batch
-        wvec bw[B][NTW];
-        load_batch(c_begin, bw);
-        publish();
-        mul_batch(c_begin, bw);
-    } else {
-        // a stream of batches, the next one's loads issued before the current
-        // one is multiplied (a wave keeps at most 2 B NTW loads in flight, so
-        // load issue does not stall on the compute unit's outstanding-request
-        // limit); the loads past the range re-read the last chunk.  Two
-        // batches a trip with no exit in between, and a scheduling barrier
-        // after every step: otherwise the compiler sinks a batch's loads below
-        // the multiplies and rotates the loop so that it waits for all loads
-        // (vmcnt(0)) at its head, and no load is in flight while a batch is
-        // multiplied.
-        wvec b0[B][NTW], b1[B][NTW];
-        const int nb = (c_end - c_begin + B - 1) / B;  // batches, > 1 here
-        load_batch(c_begin, b0);
-        publish();
-        int cb = c_begin;
-        for (int i = 0; i + 2 <= nb; i += 2, cb += 2 * B) {
-            load_batch(cb + B, b1);
-            __builtin_amdgcn_sched_barrier(0);
-            mul_batch(cb, b0);
-            __builtin_amdgcn_sched_barrier(0);
-            load_batch(cb + 2 * B, b0);
-            __builtin_amdgcn_sched_barrier(0);
-            mul_batch(cb + B, b1);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        if (nb & 1) mul_batch(cb, b0);  // its loads were issued by the last trip
+    // a stream of batches, the next one's loads issued before the current one
+    // is multiplied (a wave keeps at most 2 B NTW loads in flight, so load
+    // issue does not stall on the compute unit's outstanding-request limit);
+    // loads past the range re-read the last chunk.  Two batches a trip with
+    // no exit in between, and a scheduling barrier after every step:
+    // otherwise the compiler sinks a batch's loads below the multiplies and
+    // rotates the loop so that it waits for all loads (vmcnt(0)) at its head,
+    // and no load is in flight while a batch is multiplied.  One batch is the
+    // same code with no trip: a separate branch for it got a vmcnt(0) before
+    // its weight loads, which then waited for the activation copies.
+    wvec b0[B][NTW], b1[B][NTW];
+    const int nb = max((c_end - c_begin + B - 1) / B, 0);  // batches of this wave
+    load_batch(c_begin, b0);
+    publish();
+    int cb = c_begin;
+    for (int i = 0; i + 2 <= nb; i += 2, cb += 2 * B) {
+        load_batch(cb + B, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mul_batch(cb, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_batch(cb + 2 * B, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mul_batch(cb + B, b1);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    if (nb & 1) mul_batch(cb, b0);  // its loads were issued by the last trip (or before the loop)
 
     // lane (j, g) holds rows 4g + v of column j
 #pragma unroll
