@@ -103,8 +103,9 @@ def parse():
 
 def forward1_kernel(M: int, K: int) -> str:
     """The kernel bitlinear_forward1 runs for M tokens (its dispatch, for the
-    bench shapes: K % 256 == 0 and the activation block fits LDS)."""
-    return "decode_lds_kernel" if M >= 5 or (M >= 2 and K >= 4096) else "gemv1_kernel"
+    bench shapes, whose activation block fits LDS)."""
+    decode = (M >= 5 or (M >= 2 and K >= 4096)) and K % 512 == 0
+    return "decode_lds_kernel" if decode else "gemv1_kernel"
 
 
 def forward3_kernel(M: int, K: int) -> str:

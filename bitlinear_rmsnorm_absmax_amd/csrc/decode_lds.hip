@@ -54,10 +54,14 @@ __device__ __forceinline__ void fence_code() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// ONEBIT: 1-bit weights ([N][K/32], entry 4j + b of a word at bit 8b + j):
-// lane (j, g) loads words 8c + 2g, 8c + 2g + 1 of chunk c (the same 64 K
-// positions as the 2-bit words 16c + 4g .. +3), and MFMA s takes bits
-// 4(s%2) .. +3 of word s/2.
+// ONEBIT: 1-bit weights ([N][K/32], entry 4j + b of a word at bit 8b + j),
+// K % 512 == 0: the unit of a load is 512 inputs (16 words a row) instead of
+// 256, so that a lane still loads 16 bytes: lane (j, g) loads words
+// 16u + 4g .. +3 of unit u (K positions 512u + 128g .. +127), and MFMA
+// s = 0..7 of the unit takes bits 4(s%2) .. +3 of word s/2, the 16 inputs at
+// 512u + 128g + 16s, with the activation piece 32u + 8g + s.  (Loads of 8
+// bytes, one 256-input chunk each, ran 8 tokens at K = 8192, N = 28672 in
+// 15.6 us, no faster than the 2-bit weights at twice the bytes.)
 template <int CT, int NTW, int B, bool ONEBIT, int G>
 __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
@@ -66,7 +70,9 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     constexpr int CG = CT / NTW;         // column groups of a workgroup
     constexpr int KS = kDecWaves / CG;   // K ranges per column group
     static_assert(KS % G == 0, "every wave's K range lies inside one group");
-    typedef typename std::conditional<ONEBIT, v2u, v4u>::type wvec;
+    typedef v4u wvec;
+    constexpr int kUnitLog = ONEBIT ? 9 : 8;  // inputs per load unit: 512 (1-bit) or 256
+    constexpr int kSteps = ONEBIT ? 8 : 4;    // MFMAs per unit
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* As = smem;                                       // activations, a_bytes
     int* red = reinterpret_cast<int*>(smem + a_bytes);     // [8 waves][NTW][4][64]
@@ -79,7 +85,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int cg = wv % CG, kp = wv / CG;
     const int j = lane & 15, g = lane >> 4;
     const int WR = K >> 4;          // 16-byte pieces per activation row (= 2-bit words per row)
-    const int nchunks = K >> 8;
+    const int nchunks = K >> kUnitLog;  // load units
     const int n_base = blockIdx.x * (16 * CT) + cg * 16 * NTW;
 
     const int cpw = (nchunks + KS - 1) / KS;
@@ -100,7 +106,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const uint32_t* wrow[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
-        wrow[t] = wp + ((int64_t)gw * N + min(n_base + 16 * t + j, N - 1)) * WRWG + (ONEBIT ? 2 : 4) * g;
+        wrow[t] = wp + ((int64_t)gw * N + min(n_base + 16 * t + j, N - 1)) * WRWG + 4 * g;
     // A-operand row of lane j; rows past M repeat row M-1 (never stored)
     const int arow = min(j, M - 1);
     const char* arow_p = As + arow * K;
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 #pragma unroll
             for (int t = 0; t < NTW; ++t)
                 bw[i][t] = __builtin_nontemporal_load(reinterpret_cast<const wvec*>(
-                    wrow[t] + (ONEBIT ? 8 : 16) * (min(cb + i, last) - gw * cpg)));
+                    wrow[t] + 16 * (min(cb + i, last) - gw * cpg)));
     };
     auto mul_batch = [&](int cb, const wvec (&bw)[B][NTW]) {
 #pragma unroll
@@ -120,8 +126,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
             const bool live = cb + i < c_end;
             const int c = min(cb + i, last);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int p = 16 * c + 4 * g + s;
+            for (int s = 0; s < kSteps; ++s) {
+                const int p = ONEBIT ? 32 * c + 8 * g + s : 16 * c + 4 * g + s;
                 const v4i a = *reinterpret_cast<const v4i*>(arow_p + 16 * (p ^ axor));
 #pragma unroll
                 for (int t = 0; t < NTW; ++t) {
@@ -275,15 +281,19 @@ hipError_t launch_ctb(const int8_t* xq, const float* gamma, int M, int K, const 
     return hipGetLastError();
 }
 
-// Batch: a wave's whole K range in one batch when it has at most 4 chunks,
-// else a stream of 2-chunk batches (measured at K = 2560 .. 8192: larger
+// Batch: a wave's whole K range in one batch when it has at most 4 load units,
+// else a stream of 2-unit batches (measured at K = 2560 .. 8192: larger
 // batches stall load issue, a 2-chunk stream is 15 % faster at K = 8192).
 template <int CT, int NTW, bool ONEBIT, int G = 1>
 hipError_t launch_ct(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
                      float beta, float* y, int32_t* acc, hipStream_t s,
                      const float* beta_g = nullptr) {
     constexpr int KS = kDecWaves * NTW / CT;
-    const int cpw = ((K >> 8) + KS - 1) / KS;
+    const int cpw = ((K >> (ONEBIT ? 9 : 8)) + KS - 1) / KS;  // load units a wave
+    // one batch no larger than the wave's units (a larger one re-reads the
+    // last unit and multiplies zero codes for the rest)
+    if (cpw <= 1) return launch_ctb<CT, NTW, 1, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    if (cpw <= 2) return launch_ctb<CT, NTW, 2, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
     if (cpw <= 4) return launch_ctb<CT, NTW, 4, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
     return launch_ctb<CT, NTW, 2, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
 }

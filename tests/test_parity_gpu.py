@@ -765,13 +765,15 @@ def test_pack_weights1_parity(dev):
     assert int(host(bad)[0]) == 2
 
 
-# 1 token, 2..4 tokens below K = 4096, and K % 256 != 0: vector-ALU kernel;
-# 5..16 tokens (2..4 from K = 4096) with K % 256 == 0: the LDS-staged MFMA kernel
-# in its 1-bit form (all four workgroup widths); 17 and 20 tokens: several
-# vector-ALU passes
+# 1 token, 2..4 tokens below K = 4096, and K % 512 != 0: vector-ALU kernel;
+# 5..16 tokens (2..4 from K = 4096) with K % 512 == 0: the LDS-staged MFMA kernel
+# in its 1-bit form (all four workgroup widths, one and several load units a
+# wave, an odd number of batches at K = 6656 with 1600 tiles); 17 and 20 tokens:
+# several vector-ALU passes
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (2, 17, 192), (3, 1000, 4096), (4, 333, 2560),
                                    (5, 640, 1024), (9, 100, 64), (1, 11008, 4096),
                                    (7, 5200, 512), (12, 10300, 1024), (16, 20500, 768),
+                                   (16, 20500, 1536), (8, 25600, 6656), (6, 700, 9216),
                                    (16, 333, 8192), (17, 200, 512), (20, 96, 320),
                                    (4, 11008, 4096), (2, 6500, 8192), (3, 40, 4096)])
 def test_forward1_parity(dev, M, N, K):
