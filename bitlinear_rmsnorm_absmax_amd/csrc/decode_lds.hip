@@ -1,4 +1,4 @@
-// Decode product for a few tokens (5 <= M <= 16) on int8 MFMA, activations
+// Decode product for a few tokens (M <= 16) on int8 MFMA, activations
 // staged in LDS; 2-bit ternary weights, or 1-bit weights (ONEBIT).
 //
 // Arithmetic as in the other forward kernels (unite.ai BitNet.cpp article, 3.
@@ -28,9 +28,9 @@
 //      flight, then the MFMAs, each waiting only for its own weight registers.
 // Chunks past a wave's range multiply all-zero codes.
 //
-// Work split: a workgroup of 8 waves owns CT column tiles of 16; a wave owns
-// NTW of them and one of KS = 8 * NTW / CT contiguous K ranges (256-K
-// chunks).  Partial sums of the KS waves of a tile meet in LDS.
+// Work split: a workgroup of 8 waves owns CT column tiles of 16 / H rows; a
+// wave owns NTW of them and one of KS = 8 * NTW / CT contiguous K ranges
+// (256 H-input units).  Partial sums of the KS waves of a tile meet in LDS.
 //
 // LDS layout of the activations: row r holds its K bytes as 16-byte pieces,
 // piece p stored at slot p ^ (r & 15) of the row, so the 16 rows read by one
@@ -62,7 +62,19 @@ __device__ __forceinline__ void fence_code() {
 // 512u + 128g + 16s, with the activation piece 32u + 8g + s.  (Loads of 8
 // bytes, one 256-input chunk each, ran 8 tokens at K = 8192, N = 28672 in
 // 15.6 us, no faster than the 2-bit weights at twice the bytes.)
-template <int CT, int NTW, int B, bool ONEBIT, int G>
+//
+// H > 1 (2-bit weights, one group, M <= 16 / H): an MFMA tile holds RT = 16 / H
+// weight rows, each over H K parts, so that a load instruction reads RT rows x
+// 64 H contiguous bytes (8 x 128 B or 4 x 256 B, which stream at 5.9-6.0 TB/s
+// where 16 rows x 64 B with the rows spread over neighbouring lanes reach
+// 4.7).  A row i = h + H m holds token m over K part h, B column j = h + H r
+// holds tile row r over part h, and lane (j, g) takes the 16-byte pieces
+// 4 (h + H g) + s of each 64 H-byte unit for both operands (the row of a lane
+// pair or quad is contiguous in memory).  D[h + H m][h' + H r] is the product
+// of token m and row r over part h when h == h' (the other blocks mix parts
+// and are not used); token m's sum over row r is the sum of the H diagonal
+// blocks, which the epilogue adds from the partials in LDS.
+template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1>
 __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
     const uint32_t* wp, int N, float beta, float* __restrict__ y, int32_t* __restrict__ acc_out,
@@ -70,9 +82,13 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     constexpr int CG = CT / NTW;         // column groups of a workgroup
     constexpr int KS = kDecWaves / CG;   // K ranges per column group
     static_assert(KS % G == 0, "every wave's K range lies inside one group");
+    static_assert(H == 1 || ((H == 2 || H == 4) && !ONEBIT && G == 1), "K parts: 2-bit weights, one group");
     typedef v4u wvec;
-    constexpr int kUnitLog = ONEBIT ? 9 : 8;  // inputs per load unit: 512 (1-bit) or 256
-    constexpr int kSteps = ONEBIT ? 8 : 4;    // MFMAs per unit
+    constexpr int kHLog = H == 4 ? 2 : H == 2 ? 1 : 0;
+    constexpr int RT = 16 / H;                            // weight rows of a tile
+    constexpr int kUnitLog = ONEBIT ? 9 : 8 + kHLog;      // inputs per load unit: 512 (1-bit) or 256 H
+    constexpr int kUnitWords = 16 * H;                    // packed words of a row per unit
+    constexpr int kSteps = ONEBIT ? 8 : 4;                // MFMAs per unit
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* As = smem;                                       // activations, a_bytes
     int* red = reinterpret_cast<int*>(smem + a_bytes);     // [8 waves][NTW][4][64]
@@ -84,9 +100,10 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int cg = wv % CG, kp = wv / CG;
     const int j = lane & 15, g = lane >> 4;
+    const int h = j & (H - 1), jr = j >> kHLog;  // K part and tile row (token) of lane j
     const int WR = K >> 4;          // 16-byte pieces per activation row (= 2-bit words per row)
     const int nchunks = K >> kUnitLog;  // load units
-    const int n_base = blockIdx.x * (16 * CT) + cg * 16 * NTW;
+    const int n_base = blockIdx.x * (RT * CT) + cg * RT * NTW;
 
     const int cpw = (nchunks + KS - 1) / KS;
     const int c_begin = kp * cpw;
@@ -101,14 +118,15 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     v4i acc[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[t] = v4i{0, 0, 0, 0};
-    // lane (j, g): column j of each tile, packed words 16c + 4g .. +3 of chunk c;
-    // columns past N are clamped onto the last one (never stored)
+    // lane (j, g): row jr of each tile, packed words 16 H c + 4 (h + H g) .. +3
+    // of unit c (H == 1: column j, words 16c + 4g); rows past N are clamped
+    // onto the last one (never stored)
     const uint32_t* wrow[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
-        wrow[t] = wp + ((int64_t)gw * N + min(n_base + 16 * t + j, N - 1)) * WRWG + 4 * g;
-    // A-operand row of lane j; rows past M repeat row M-1 (never stored)
-    const int arow = min(j, M - 1);
+        wrow[t] = wp + ((int64_t)gw * N + min(n_base + RT * t + jr, N - 1)) * WRWG + 4 * (h + H * g);
+    // A-operand token of lane j; tokens past M repeat token M-1 (never stored)
+    const int arow = min(jr, M - 1);
     const char* arow_p = As + arow * K;
     const int axor = arow & 15;
 
@@ -118,7 +136,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 #pragma unroll
             for (int t = 0; t < NTW; ++t)
                 bw[i][t] = __builtin_nontemporal_load(reinterpret_cast<const wvec*>(
-                    wrow[t] + 16 * (min(cb + i, last) - gw * cpg)));
+                    wrow[t] + kUnitWords * (min(cb + i, last) - gw * cpg)));
     };
     auto mul_batch = [&](int cb, const wvec (&bw)[B][NTW]) {
 #pragma unroll
@@ -127,7 +145,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
             const int c = min(cb + i, last);
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
-                const int p = ONEBIT ? 32 * c + 8 * g + s : 16 * c + 4 * g + s;
+                const int p = ONEBIT ? 32 * c + 8 * g + s : 16 * H * c + 4 * (h + H * g) + s;
                 const v4i a = *reinterpret_cast<const v4i*>(arow_p + 16 * (p ^ axor));
 #pragma unroll
                 for (int t = 0; t < NTW; ++t) {
@@ -237,7 +255,29 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[((wv * NTW + t) * 4 + v) * kWave + lane] = acc[t][v];
     __syncthreads();
-    if (kp == 0) {
+    if constexpr (H > 1) {
+        // output (token m, tile row r) of tile t: the diagonal blocks
+        // D[h + H m][h + H r], h < H, held by lane (h + H r) + 16 ((h + H m) / 4)
+        // at register (h + H m) % 4 of every K range's partial
+        if (kp == 0 && lane < RT * RT) {
+            const int m = lane / RT, r = lane % RT;
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+                const int col = n_base + RT * t + r;
+                if (m >= M || col >= N) continue;
+                int d = 0;
+#pragma unroll
+                for (int hh = 0; hh < H; ++hh) {
+                    const int i = hh + H * m, src = hh + H * r + 16 * (i >> 2), v = i & 3;
+#pragma unroll
+                    for (int k2 = 0; k2 < KS; ++k2) d += red[(((k2 * CG + cg) * NTW + t) * 4 + v) * kWave + src];
+                }
+                const int a = d - Ssum[m];
+                if (acc_out) acc_out[(int64_t)m * N + col] = a;
+                if (y) y[(int64_t)m * N + col] = (float)a * Ssc[m];
+            }
+        }
+    } else if (kp == 0) {
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
             const int col = n_base + 16 * t + j;
@@ -267,16 +307,17 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 }
 
 
-template <int CT, int NTW, int B, bool ONEBIT, int G>
+template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1>
 hipError_t launch_ctb(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
                       float beta, float* y, int32_t* acc, hipStream_t s, const float* beta_g) {
     static DynLdsOptIn opt_in;
     const hipError_t e = opt_in.ensure(
-        reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT, G>), kDecLdsMax);
+        reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT, G, H>), kDecLdsMax);
     if (e != hipSuccess) return e;
-    const int blocks = (N + 16 * CT - 1) / (16 * CT);
-    decode_lds_kernel<CT, NTW, B, ONEBIT, G><<<dim3(blocks), dim3(kDecWaves * kWave),
-                                               decode_lds_bytes(M, K, NTW, G), s>>>(
+    constexpr int rows = 16 / H * CT;  // weight rows of a workgroup
+    const int blocks = (N + rows - 1) / rows;
+    decode_lds_kernel<CT, NTW, B, ONEBIT, G, H><<<dim3(blocks), dim3(kDecWaves * kWave),
+                                                  decode_lds_bytes(M, K, NTW, G), s>>>(
         xq, gamma, M, K, wp, N, beta, y, acc, decode_a_bytes(M, K), beta_g);
     return hipGetLastError();
 }
@@ -284,18 +325,19 @@ hipError_t launch_ctb(const int8_t* xq, const float* gamma, int M, int K, const 
 // Batch: a wave's whole K range in one batch when it has at most 4 load units,
 // else a stream of 2-unit batches (measured at K = 2560 .. 8192: larger
 // batches stall load issue, a 2-chunk stream is 15 % faster at K = 8192).
-template <int CT, int NTW, bool ONEBIT, int G = 1>
+template <int CT, int NTW, bool ONEBIT, int G = 1, int H = 1>
 hipError_t launch_ct(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
                      float beta, float* y, int32_t* acc, hipStream_t s,
                      const float* beta_g = nullptr) {
     constexpr int KS = kDecWaves * NTW / CT;
-    const int cpw = ((K >> (ONEBIT ? 9 : 8)) + KS - 1) / KS;  // load units a wave
+    constexpr int unit_log = ONEBIT ? 9 : H == 4 ? 10 : H == 2 ? 9 : 8;
+    const int cpw = ((K >> unit_log) + KS - 1) / KS;  // load units a wave
     // one batch no larger than the wave's units (a larger one re-reads the
     // last unit and multiplies zero codes for the rest)
-    if (cpw <= 1) return launch_ctb<CT, NTW, 1, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
-    if (cpw <= 2) return launch_ctb<CT, NTW, 2, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
-    if (cpw <= 4) return launch_ctb<CT, NTW, 4, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
-    return launch_ctb<CT, NTW, 2, ONEBIT, G>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    if (cpw <= 1) return launch_ctb<CT, NTW, 1, ONEBIT, G, H>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    if (cpw <= 2) return launch_ctb<CT, NTW, 2, ONEBIT, G, H>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    if (cpw <= 4) return launch_ctb<CT, NTW, 4, ONEBIT, G, H>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    return launch_ctb<CT, NTW, 2, ONEBIT, G, H>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
 }
 
 // Grouped launch of one width: G as a template argument (2, 4 or 8, at most
@@ -347,7 +389,24 @@ hipError_t launch_decode_lds_grouped(const int8_t* xq, const float* gamma, int M
 hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
                              const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                              hipStream_t s) {
-    return launch_widths<false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    // up to 8 tokens (K % 512 == 0): two K parts per tile, 8 rows x 128 B a
+    // load, one tile a wave over the whole K.  Widest workgroup that leaves
+    // >= 200 workgroups of 128 rows or >= 150 of 64 rows, else 32 rows
+    // (measured, bit-identical to one part: 8 tokens at K = 8192, N = 28672
+    // 15.9 -> 12.0-12.5 us; 2..8 tokens at K = 4096, N = 11008 5.7-6.3 ->
+    // 4.8-5.1 us; 5 tokens at K = 2560, N = 6912 5.6 -> 4.1 us)
+    if (M <= 8 && K % 512 == 0) {
+        if (N / 128 >= 200) return launch_ct<16, 2, false, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        if (N / 64 >= 150) return launch_ct<8, 1, false, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return launch_ct<4, 1, false, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    }
+    // 9..16 tokens: one 16-row tile a wave (16 tokens at K = 8192, N = 28672
+    // 16.6 -> 15.8 us, at K = 4096, N = 11008 6.9 -> 6.7 us against two tiles)
+    const int tiles = (N + 15) / 16;
+    if (tiles >= 8 * 200) return launch_ct<8, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (tiles >= 4 * 200) return launch_ct<4, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (tiles >= 2 * 200) return launch_ct<2, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    return launch_ct<1, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
 
 hipError_t launch_decode_lds1(const int8_t* xq, const float* gamma, int M, int K,

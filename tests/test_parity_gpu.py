@@ -368,7 +368,11 @@ DECODE_LDS_CASES = [(5, 1000, 256), (7, 5200, 512), (12, 10300, 1024), (16, 2050
                     (16, 333, 9216), (9, 2570, 2560), (13, 40, 4096), (6, 17, 256),
                     (2, 3000, 8192), (3, 700, 6912), (4, 129, 6144),
                     (8, 6401, 512), (11, 12800, 256), (9, 25700, 512), (4, 11008, 4096),
-                    (2, 6500, 4096), (3, 40, 4096), (8, 25600, 6912), (5, 12800, 8704)]
+                    (2, 6500, 4096), (3, 40, 4096), (8, 25600, 6912), (5, 12800, 8704),
+                    # two K parts per tile (up to 8 tokens, K % 512 == 0) on each
+                    # workgroup width (128, 64 and 32 rows), with ragged row tails
+                    (8, 25700, 1024), (3, 26000, 2048), (8, 9700, 512), (6, 150, 1536),
+                    (7, 9631, 2560)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_LDS_CASES)
@@ -384,8 +388,9 @@ def test_decode_lds_parity(dev, M, N, K):
     assert_y_close(y, y_ref)
 
 
-def test_decode_lds_extreme_codes(dev):
-    M, N, K = 16, 700, 9216
+@pytest.mark.parametrize("M", [16, 8])
+def test_decode_lds_extreme_codes(dev, M):
+    N, K = 700, 9216
     q = np.full((M, K), 127, np.int8)
     q[1::2] = -127
     w = np.ones((N, K), np.int8)
