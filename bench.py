@@ -117,9 +117,10 @@ def forward3_kernel(M: int, K: int) -> str:
 
 def forward_kernel(M: int, K: int, N: int) -> str:
     """Kernel that bitlinear_forward picks (the library's dispatch)."""
-    if M == 1:
-        return "gemv_valu_kernel"
     lds_fits = K % 256 == 0 and ((M * K + 1023) // 1024) * 1024 + 16384 + 128 <= 160 * 1024
+    if M == 1:
+        one_token_decode = K >= 4096 and K % 512 == 0 and N // 64 >= 150 and lds_fits
+        return "decode_lds_kernel" if one_token_decode else "gemv_valu_kernel"
     if (5 <= M <= 16 or (2 <= M <= 4 and K >= 4096)) and lds_fits:
         return "decode_lds_kernel"
     if M <= 16 or (M <= 32 and not (-(-N // 128) >= 128 and K % 256 == 0)):

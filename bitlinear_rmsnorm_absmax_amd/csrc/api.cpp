@@ -79,8 +79,10 @@ hipError_t launch_forward_kernel(const int8_t* x_q, const float* gamma, int64_t 
         // the GEMM's 64-row tiles: K = 8192, N = 28672 at 17..32 tokens 28-30 us
         // against 49-75 us on the skinny kernel; with fewer column tiles the
         // skinny kernel keeps more CUs busy (K = 6912, N = 2560: 10-12 vs 21 us)
+        // one token: the VALU GEMV, or the decode kernel (in the skinny path)
+        // on long rows over many row tiles
         const bool wide_n = (N + 127) / 128 >= 128 && K % 256 == 0;
-        path = (M == 1) ? BITLINEAR_PATH_GEMV
+        path = (M == 1) ? (bl::decode_one_token((int)K, (int)N) ? BITLINEAR_PATH_SKINNY : BITLINEAR_PATH_GEMV)
              : (M <= 16 || (M <= 32 && !wide_n)) ? BITLINEAR_PATH_SKINNY
                                                   : BITLINEAR_PATH_GEMM;
     }

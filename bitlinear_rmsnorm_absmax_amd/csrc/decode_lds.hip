@@ -82,9 +82,10 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     constexpr int CG = CT / NTW;         // column groups of a workgroup
     constexpr int KS = kDecWaves / CG;   // K ranges per column group
     static_assert(KS % G == 0, "every wave's K range lies inside one group");
-    static_assert(H == 1 || ((H == 2 || H == 4) && !ONEBIT && G == 1), "K parts: 2-bit weights, one group");
+    static_assert(H == 1 || ((H == 2 || H == 4 || H == 8 || H == 16) && !ONEBIT && G == 1),
+                  "K parts: 2-bit weights, one group");
     typedef v4u wvec;
-    constexpr int kHLog = H == 4 ? 2 : H == 2 ? 1 : 0;
+    constexpr int kHLog = H == 16 ? 4 : H == 8 ? 3 : H == 4 ? 2 : H == 2 ? 1 : 0;
     constexpr int RT = 16 / H;                            // weight rows of a tile
     constexpr int kUnitLog = ONEBIT ? 9 : 8 + kHLog;      // inputs per load unit: 512 (1-bit) or 256 H
     constexpr int kUnitWords = 16 * H;                    // packed words of a row per unit
@@ -330,7 +331,7 @@ hipError_t launch_ct(const int8_t* xq, const float* gamma, int M, int K, const u
                      float beta, float* y, int32_t* acc, hipStream_t s,
                      const float* beta_g = nullptr) {
     constexpr int KS = kDecWaves * NTW / CT;
-    constexpr int unit_log = ONEBIT ? 9 : H == 4 ? 10 : H == 2 ? 9 : 8;
+    constexpr int unit_log = ONEBIT ? 9 : H == 16 ? 12 : H == 8 ? 11 : H == 4 ? 10 : H == 2 ? 9 : 8;
     const int cpw = ((K >> unit_log) + KS - 1) / KS;  // load units a wave
     // one batch no larger than the wave's units (a larger one re-reads the
     // last unit and multiplies zero codes for the rest)

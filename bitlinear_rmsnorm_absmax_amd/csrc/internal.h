@@ -74,7 +74,7 @@ hipError_t launch_skinny_mfma(const int8_t* xq, const float* gamma, int M, int K
                               const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                               hipStream_t s);
 
-// Decode product with the activation block staged in LDS (5 <= M <= 16,
+// Decode product with the activation block staged in LDS (M <= 16,
 // K % 256 == 0); decode_lds_supports() tells whether a shape fits.  Its
 // shape rules (shapes.cpp): eight waves a workgroup, at most 160 KB of LDS.
 constexpr int kDecWaves = 8;
@@ -83,6 +83,8 @@ int decode_a_bytes(int M, int K);
 size_t decode_lds_bytes(int M, int K, int ntw, int G = 1);
 int grouped_width(int tiles, int G, int nchunks);
 bool decode_lds_supports(int M, int K, int N);
+// Whether one token runs on the decode kernel instead of the VALU GEMV.
+bool decode_one_token(int K, int N);
 hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
                              const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                              hipStream_t s);

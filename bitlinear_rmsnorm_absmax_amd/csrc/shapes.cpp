@@ -50,6 +50,14 @@ bool decode_lds_supports(int M, int K, int N) {
            decode_lds_bytes(M, K, 2, 1) <= (size_t)kDecLdsMax;
 }
 
+// One token on the decode kernel (two K parts per tile) rather than the VALU
+// GEMV: long rows over many row tiles.  Back-to-back times, bit-identical:
+// K = 8192, N = 28672 12.9 -> 11.4 us; K = 4096, N = 11008 5.1 -> 4.8 us; at
+// K = 2560, N = 6912 and K = N = 2048 the two are equal or the GEMV is faster.
+bool decode_one_token(int K, int N) {
+    return K >= 4096 && K % 512 == 0 && N / 64 >= 150 && decode_lds_supports(1, K, N);
+}
+
 bool decode_lds_grouped_supports(int M, int K, int G, int N) {
     if ((G != 2 && G != 4 && G != 8) || M < 1 || M > 16 || N <= 0 || K % 256 != 0 || K % G != 0 ||
         (K / G) % 256 != 0)

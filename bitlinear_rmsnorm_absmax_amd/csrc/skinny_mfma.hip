@@ -175,7 +175,9 @@ hipError_t launch_skinny_mfma(const int8_t* xq, const float* gamma, int M, int K
     // 2560 x 2560: at K = 8192 it takes 16 us for 2..4 tokens against 18..23 us
     // here, at K = 4096, N = 11008 6.1-6.6 us against 6.5-7.3 us; at K = 2560
     // this kernel is as fast or faster below 5 tokens)
-    if ((M >= 5 || (M >= 2 && K >= 4096)) && decode_lds_supports(M, K, N))
+    // (one token too on long rows over many row tiles, decode_one_token)
+    if ((M >= 5 || (M >= 2 && K >= 4096) || (M == 1 && decode_one_token(K, N))) &&
+        decode_lds_supports(M, K, N))
         return launch_decode_lds(xq, gamma, M, K, wp, N, beta, y, acc, s);
     switch ((M + 15) / 16) {
         case 1: return launch_mt<1>(xq, gamma, M, K, wp, N, beta, y, acc, s);

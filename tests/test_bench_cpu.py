@@ -112,8 +112,12 @@ def test_kernel_labels_follow_the_dispatch():
     assert bench.forward3_kernel(1, 4096) == "gemv3_kernel"
     assert bench.forward3_kernel(2, 4096) == "gemv3_mfma_kernel"
     assert bench.forward3_kernel(17, 1024) == "gemv3_kernel"
-    # 2-bit: GEMV for one token, the LDS decode kernel at decode sizes, GEMM
-    assert bench.forward_kernel(1, 4096, 11008) == "gemv_valu_kernel"
+    # 2-bit: GEMV for one token on small shapes, the LDS decode kernel at decode
+    # sizes (one token too on long rows over many row tiles), GEMM
+    assert bench.forward_kernel(1, 2048, 2048) == "gemv_valu_kernel"
+    assert bench.forward_kernel(1, 2560, 6912) == "gemv_valu_kernel"
+    assert bench.forward_kernel(1, 4096, 11008) == "decode_lds_kernel"
+    assert bench.forward_kernel(1, 8192, 28672) == "decode_lds_kernel"
     assert bench.forward_kernel(16, 4096, 11008) == "decode_lds_kernel"
 
 

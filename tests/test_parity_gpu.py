@@ -372,14 +372,17 @@ DECODE_LDS_CASES = [(5, 1000, 256), (7, 5200, 512), (12, 10300, 1024), (16, 2050
                     # two K parts per tile (up to 8 tokens, K % 512 == 0) on each
                     # workgroup width (128, 64 and 32 rows), with ragged row tails
                     (8, 25700, 1024), (3, 26000, 2048), (8, 9700, 512), (6, 150, 1536),
-                    (7, 9631, 2560)]
+                    (7, 9631, 2560),
+                    # one token on the decode kernel (K >= 4096, K % 512 == 0, N / 64 >= 150)
+                    (1, 9700, 4096), (1, 25700, 4608), (1, 9631, 5120)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_LDS_CASES)
 def test_decode_lds_parity(dev, M, N, K):
     x, w, beta = workloads.random_case(700 + M + N, M, N, K, table=workloads.TERNARY_HALF_ZERO)
     x = x.copy()
-    x[1] = 0.0
+    if M > 1:
+        x[1] = 0.0
     q, g, y, acc = run_forward(x, w, beta, dev, bl.PATH_SKINNY)
     q_ref, g_ref = oracle.quant_act(x)
     np.testing.assert_array_equal(q, q_ref)
