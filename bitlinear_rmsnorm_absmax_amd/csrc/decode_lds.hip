@@ -74,7 +74,12 @@ __device__ __forceinline__ void fence_code() {
 // of token m and row r over part h when h == h' (the other blocks mix parts
 // and are not used); token m's sum over row r is the sum of the H diagonal
 // blocks, which the epilogue adds from the partials in LDS.
-template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1>
+// TG > 1 (H == 2): TG groups of 8 tokens, each with its own MFMA and A rows,
+// share every unpacked weight fragment (M <= 8 TG), so 9..16 tokens keep the
+// 8 x 128 B loads.  With one K range per tile (KS == 1) the two diagonal
+// blocks are added in registers (lane 2r + 16 q' and its odd neighbour) and no
+// LDS reduction buffer is allocated.
+template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1, int TG = 1>
 __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
     const uint32_t* wp, int N, float beta, float* __restrict__ y, int32_t* __restrict__ acc_out,
@@ -84,6 +89,9 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     static_assert(KS % G == 0, "every wave's K range lies inside one group");
     static_assert(H == 1 || ((H == 2 || H == 4 || H == 8 || H == 16) && !ONEBIT && G == 1),
                   "K parts: 2-bit weights, one group");
+    static_assert(TG == 1 || (H == 2 && KS == 1), "token groups: two K parts, one K range");
+    constexpr bool kRegEpi = H == 2 && KS == 1;  // diagonal blocks added in registers
+    constexpr int kRedNtw = kRegEpi ? 0 : NTW;   // LDS reduction buffer: [8 waves][kRedNtw][4][64]
     typedef v4u wvec;
     constexpr int kHLog = H == 16 ? 4 : H == 8 ? 3 : H == 4 ? 2 : H == 2 ? 1 : 0;
     constexpr int RT = 16 / H;                            // weight rows of a tile
@@ -92,8 +100,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     constexpr int kSteps = ONEBIT ? 8 : 4;                // MFMAs per unit
     extern __shared__ __attribute__((aligned(16))) char smem[];
     char* As = smem;                                       // activations, a_bytes
-    int* red = reinterpret_cast<int*>(smem + a_bytes);     // [8 waves][NTW][4][64]
-    int* Ssum = red + kDecWaves * NTW * 4 * kWave;         // [G][16] activation sums
+    int* red = reinterpret_cast<int*>(smem + a_bytes);     // [8 waves][kRedNtw][4][64]
+    int* Ssum = red + kDecWaves * kRedNtw * 4 * kWave;     // [G][16] activation sums
     float* Ssc = reinterpret_cast<float*>(Ssum + 16 * G);  // [G][16] output scales
 
     const int tid = threadIdx.x;
@@ -116,9 +124,11 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int gw = G > 1 ? c_begin / cpg : 0;
     const int WRWG = ONEBIT ? (KG >> 5) : (KG >> 4);  // weight words per row of a group
 
-    v4i acc[NTW];
+    v4i acc[TG][NTW];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) acc[t] = v4i{0, 0, 0, 0};
+    for (int q = 0; q < TG; ++q)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[q][t] = v4i{0, 0, 0, 0};
     // lane (j, g): row jr of each tile, packed words 16 H c + 4 (h + H g) .. +3
     // of unit c (H == 1: column j, words 16c + 4g); rows past N are clamped
     // onto the last one (never stored)
@@ -126,10 +136,16 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
         wrow[t] = wp + ((int64_t)gw * N + min(n_base + RT * t + jr, N - 1)) * WRWG + 4 * (h + H * g);
-    // A-operand token of lane j; tokens past M repeat token M-1 (never stored)
-    const int arow = min(jr, M - 1);
-    const char* arow_p = As + arow * K;
-    const int axor = arow & 15;
+    // A-operand token of lane j in each token group; tokens past M repeat
+    // token M-1 (never stored)
+    const char* arow_p[TG];
+    int axor[TG];
+#pragma unroll
+    for (int q = 0; q < TG; ++q) {
+        const int arow = min(RT * q + jr, M - 1);
+        arow_p[q] = As + arow * K;
+        axor[q] = arow & 15;
+    }
 
     auto load_batch = [&](int cb, wvec (&bw)[B][NTW]) {
 #pragma unroll
@@ -147,7 +163,10 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
                 const int p = ONEBIT ? 32 * c + 8 * g + s : 16 * H * c + 4 * (h + H * g) + s;
-                const v4i a = *reinterpret_cast<const v4i*>(arow_p + 16 * (p ^ axor));
+                v4i a[TG];
+#pragma unroll
+                for (int q = 0; q < TG; ++q)
+                    a[q] = *reinterpret_cast<const v4i*>(arow_p[q] + 16 * (p ^ axor[q]));
 #pragma unroll
                 for (int t = 0; t < NTW; ++t) {
                     v4i b;
@@ -159,7 +178,9 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
                     } else {
                         b = unpack_codes(live ? bw[i][t][s] : 0u);
                     }
-                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[t], 0, 0, 0);
+#pragma unroll
+                    for (int q = 0; q < TG; ++q)
+                        acc[q][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[q], b, acc[q][t], 0, 0, 0);
                 }
             }
         }
@@ -250,11 +271,36 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     }
     if (nb & 1) mul_batch(cb, b0);  // its loads were issued by the last trip (or before the loop)
 
+    if constexpr (kRegEpi) {
+        // lane l holds D[4 (l / 16) + v][l % 16]: the block entries of token
+        // m = 2 g' + b of group q and tile row r sit at register 2b of lane
+        // 2r + 16 g' (part 0) and register 2b + 1 of the next lane (part 1)
+        __syncthreads();  // Ssum and Ssc are written (every wave passed publish)
+        const int r = jr;  // = (lane & 15) >> 1
+#pragma unroll
+        for (int q = 0; q < TG; ++q)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+                const int o1 = __shfl_xor(acc[q][t][1], 1, kWave);
+                const int o3 = __shfl_xor(acc[q][t][3], 1, kWave);
+                const int col = n_base + RT * t + r;
+                if (h != 0 || col >= N) continue;
+#pragma unroll
+                for (int b2 = 0; b2 < 2; ++b2) {
+                    const int m = RT * q + 2 * g + b2;
+                    if (m >= M) continue;
+                    const int a = acc[q][t][2 * b2] + (b2 ? o3 : o1) - Ssum[m];
+                    if (acc_out) acc_out[(int64_t)m * N + col] = a;
+                    if (y) y[(int64_t)m * N + col] = (float)a * Ssc[m];
+                }
+            }
+        return;
+    }
     // lane (j, g) holds rows 4g + v of column j
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[((wv * NTW + t) * 4 + v) * kWave + lane] = acc[t][v];
+        for (int v = 0; v < 4; ++v) red[((wv * kRedNtw + t) * 4 + v) * kWave + lane] = acc[0][t][v];
     __syncthreads();
     if constexpr (H > 1) {
         // output (token m, tile row r) of tile t: the diagonal blocks
@@ -271,7 +317,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
                 for (int hh = 0; hh < H; ++hh) {
                     const int i = hh + H * m, src = hh + H * r + 16 * (i >> 2), v = i & 3;
 #pragma unroll
-                    for (int k2 = 0; k2 < KS; ++k2) d += red[(((k2 * CG + cg) * NTW + t) * 4 + v) * kWave + src];
+                    for (int k2 = 0; k2 < KS; ++k2) d += red[(((k2 * CG + cg) * kRedNtw + t) * 4 + v) * kWave + src];
                 }
                 const int a = d - Ssum[m];
                 if (acc_out) acc_out[(int64_t)m * N + col] = a;
@@ -295,7 +341,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
                     int d = 0;
 #pragma unroll
                     for (int k2 = gi * KPG; k2 < (gi + 1) * KPG; ++k2)
-                        d += red[(((k2 * CG + cg) * NTW + t) * 4 + v) * kWave + lane];
+                        d += red[(((k2 * CG + cg) * kRedNtw + t) * 4 + v) * kWave + lane];
                     const int a = (ONEBIT ? 2 * d : d) - Ssum[gi * 16 + row];
                     const float term = (float)a * Ssc[gi * 16 + row];
                     yv = gi == 0 ? term : yv + term;
@@ -308,17 +354,19 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 }
 
 
-template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1>
+template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1, int TG = 1>
 hipError_t launch_ctb(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
                       float beta, float* y, int32_t* acc, hipStream_t s, const float* beta_g) {
     static DynLdsOptIn opt_in;
     const hipError_t e = opt_in.ensure(
-        reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT, G, H>), kDecLdsMax);
+        reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT, G, H, TG>), kDecLdsMax);
     if (e != hipSuccess) return e;
     constexpr int rows = 16 / H * CT;  // weight rows of a workgroup
+    constexpr int red_ntw = (H == 2 && kDecWaves * NTW / CT == 1) ? 0 : NTW;  // no LDS reduction
+    const size_t lds = decode_lds_bytes(M, K, red_ntw, G);
+    if (M > 16 / H * TG || lds > (size_t)kDecLdsMax) return hipErrorInvalidValue;
     const int blocks = (N + rows - 1) / rows;
-    decode_lds_kernel<CT, NTW, B, ONEBIT, G, H><<<dim3(blocks), dim3(kDecWaves * kWave),
-                                                  decode_lds_bytes(M, K, NTW, G), s>>>(
+    decode_lds_kernel<CT, NTW, B, ONEBIT, G, H, TG><<<dim3(blocks), dim3(kDecWaves * kWave), lds, s>>>(
         xq, gamma, M, K, wp, N, beta, y, acc, decode_a_bytes(M, K), beta_g);
     return hipGetLastError();
 }
@@ -326,7 +374,7 @@ hipError_t launch_ctb(const int8_t* xq, const float* gamma, int M, int K, const 
 // Batch: a wave's whole K range in one batch when it has at most 4 load units,
 // else a stream of 2-unit batches (measured at K = 2560 .. 8192: larger
 // batches stall load issue, a 2-chunk stream is 15 % faster at K = 8192).
-template <int CT, int NTW, bool ONEBIT, int G = 1, int H = 1>
+template <int CT, int NTW, bool ONEBIT, int G = 1, int H = 1, int TG = 1>
 hipError_t launch_ct(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
                      float beta, float* y, int32_t* acc, hipStream_t s,
                      const float* beta_g = nullptr) {
@@ -335,10 +383,10 @@ hipError_t launch_ct(const int8_t* xq, const float* gamma, int M, int K, const u
     const int cpw = ((K >> unit_log) + KS - 1) / KS;  // load units a wave
     // one batch no larger than the wave's units (a larger one re-reads the
     // last unit and multiplies zero codes for the rest)
-    if (cpw <= 1) return launch_ctb<CT, NTW, 1, ONEBIT, G, H>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
-    if (cpw <= 2) return launch_ctb<CT, NTW, 2, ONEBIT, G, H>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
-    if (cpw <= 4) return launch_ctb<CT, NTW, 4, ONEBIT, G, H>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
-    return launch_ctb<CT, NTW, 2, ONEBIT, G, H>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    if (cpw <= 1) return launch_ctb<CT, NTW, 1, ONEBIT, G, H, TG>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    if (cpw <= 2) return launch_ctb<CT, NTW, 2, ONEBIT, G, H, TG>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    if (cpw <= 4) return launch_ctb<CT, NTW, 4, ONEBIT, G, H, TG>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    return launch_ctb<CT, NTW, 2, ONEBIT, G, H, TG>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
 }
 
 // Grouped launch of one width: G as a template argument (2, 4 or 8, at most
@@ -401,8 +449,20 @@ hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
         if (N / 64 >= 150) return launch_ct<8, 1, false, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
         return launch_ct<4, 1, false, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     }
-    // 9..16 tokens: one 16-row tile a wave (16 tokens at K = 8192, N = 28672
-    // 16.6 -> 15.8 us, at K = 4096, N = 11008 6.9 -> 6.7 us against two tiles)
+    // 9..16 tokens (K % 512 == 0, many row tiles): two K parts and two token
+    // groups sharing every weight fragment, one K range per tile (a
+    // workgroup holds up to 128 KB of activations, so one per compute unit:
+    // 128-row workgroups once there are >= 200 of them, which then fill the
+    // chip in one round; else 64 rows).  Bit-identical, 16 tokens at K = 8192,
+    // N = 28672 15.7 -> 14.4 us; at K = 4096, N = 11008 6.9 -> 6.0 us; 9..12
+    // tokens there 6.3-6.4 -> 5.6-5.8 us; K = 5120, N = 13824 7.8 -> 6.9 us
+    // (with fewer row tiles, e.g. N = 4000 or 6912, it is no faster)
+    if (K % 512 == 0 && N / 64 >= 150) {
+        if (N / 128 >= 200) return launch_ct<16, 2, false, 1, 2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return launch_ct<8, 1, false, 1, 2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    }
+    // else one 16-row tile a wave (16 tokens at K = 8192, N = 28672 16.6 ->
+    // 15.8 us, at K = 4096, N = 11008 6.9 -> 6.7 us against two tiles)
     const int tiles = (N + 15) / 16;
     if (tiles >= 8 * 200) return launch_ct<8, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     if (tiles >= 4 * 200) return launch_ct<4, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);

@@ -374,7 +374,10 @@ DECODE_LDS_CASES = [(5, 1000, 256), (7, 5200, 512), (12, 10300, 1024), (16, 2050
                     (8, 25700, 1024), (3, 26000, 2048), (8, 9700, 512), (6, 150, 1536),
                     (7, 9631, 2560),
                     # one token on the decode kernel (K >= 4096, K % 512 == 0, N / 64 >= 150)
-                    (1, 9700, 4096), (1, 25700, 4608), (1, 9631, 5120)]
+                    (1, 9700, 4096), (1, 25700, 4608), (1, 9631, 5120),
+                    # 9..16 tokens as two token groups on two-part tiles (K % 512 == 0,
+                    # N / 64 >= 150), 128- and 64-row workgroups, ragged row tails
+                    (16, 25700, 2048), (13, 9650, 1536), (10, 12800, 4608)]
 
 
 @pytest.mark.parametrize("M,N,K", DECODE_LDS_CASES)
@@ -391,9 +394,8 @@ def test_decode_lds_parity(dev, M, N, K):
     assert_y_close(y, y_ref)
 
 
-@pytest.mark.parametrize("M", [16, 8])
-def test_decode_lds_extreme_codes(dev, M):
-    N, K = 700, 9216
+@pytest.mark.parametrize("M,N,K", [(16, 700, 9216), (8, 700, 9216), (16, 9650, 4608)])
+def test_decode_lds_extreme_codes(dev, M, N, K):
     q = np.full((M, K), 127, np.int8)
     q[1::2] = -127
     w = np.ones((N, K), np.int8)
