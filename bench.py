@@ -101,10 +101,11 @@ def parse():
     return ap.parse_args()
 
 
-def forward1_kernel(M: int, K: int) -> str:
+def forward1_kernel(M: int, K: int, N: int) -> str:
     """The kernel bitlinear_forward1 runs for M tokens (its dispatch, for the
     bench shapes, whose activation block fits LDS)."""
-    decode = (M >= 5 or (M >= 2 and K >= 4096)) and K % 512 == 0
+    one_token = M == 1 and K >= 4096 and K % 1024 == 0 and N // 64 >= 150
+    decode = (M >= 5 or (M >= 2 and K >= 4096) or one_token) and K % 512 == 0
     return "decode_lds_kernel" if decode else "gemv1_kernel"
 
 
@@ -830,7 +831,7 @@ def bench_binary(args, torch, bl, dev):
                    "weight_copies": len(copies), "timing": "hip_graph_per_step"},
         "roofline": dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
                          frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, call=dom,
-                         kernel=forward1_kernel(int(dom.split("M")[-1]), K),
+                         kernel=forward1_kernel(int(dom.split("M")[-1]), K, N),
                          avg_launch_us=d["avg_us"],
                          alg_bytes_per_launch=d["alg_bytes"]),
         "cpu_baseline": cpu,

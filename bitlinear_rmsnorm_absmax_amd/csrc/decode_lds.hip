@@ -63,14 +63,15 @@ __device__ __forceinline__ void fence_code() {
 // bytes, one 256-input chunk each, ran 8 tokens at K = 8192, N = 28672 in
 // 15.6 us, no faster than the 2-bit weights at twice the bytes.)
 //
-// H > 1 (2-bit weights, one group, M <= 16 / H): an MFMA tile holds RT = 16 / H
-// weight rows, each over H K parts, so that a load instruction reads RT rows x
-// 64 H contiguous bytes (8 x 128 B or 4 x 256 B, which stream at 5.9-6.0 TB/s
-// where 16 rows x 64 B with the rows spread over neighbouring lanes reach
-// 4.7).  A row i = h + H m holds token m over K part h, B column j = h + H r
-// holds tile row r over part h, and lane (j, g) takes the 16-byte pieces
-// 4 (h + H g) + s of each 64 H-byte unit for both operands (the row of a lane
-// pair or quad is contiguous in memory).  D[h + H m][h' + H r] is the product
+// H > 1 (one group, M <= 16 / H; 1-bit weights H = 2): an MFMA tile holds
+// RT = 16 / H weight rows, each over H K parts, so that a load instruction
+// reads RT rows x 64 H contiguous bytes (8 x 128 B or 4 x 256 B, which stream
+// at 5.9-6.0 TB/s where 16 rows x 64 B with the rows spread over neighbouring
+// lanes reach 4.7).  A row i = h + H m holds token m over K part h, B column
+// j = h + H r holds tile row r over part h, and lane (j, g) loads the 16-byte
+// piece h + H g of each 64 H-byte unit of its row (the row of a lane pair or
+// quad is contiguous in memory); both operands take the K positions of that
+// piece (activation pieces 4 (h + H g) + s, 1-bit: 8 (h + H g) + s).  D[h + H m][h' + H r] is the product
 // of token m and row r over part h when h == h' (the other blocks mix parts
 // and are not used); token m's sum over row r is the sum of the H diagonal
 // blocks, which the epilogue adds from the partials in LDS.
@@ -87,15 +88,15 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     constexpr int CG = CT / NTW;         // column groups of a workgroup
     constexpr int KS = kDecWaves / CG;   // K ranges per column group
     static_assert(KS % G == 0, "every wave's K range lies inside one group");
-    static_assert(H == 1 || ((H == 2 || H == 4 || H == 8 || H == 16) && !ONEBIT && G == 1),
-                  "K parts: 2-bit weights, one group");
+    static_assert(H == 1 || ((H == 2 || H == 4 || H == 8 || H == 16) && G == 1 && (!ONEBIT || H == 2)),
+                  "K parts: one group (1-bit weights: two parts)");
     static_assert(TG == 1 || (H == 2 && KS == 1), "token groups: two K parts, one K range");
     constexpr bool kRegEpi = H == 2 && KS == 1;  // diagonal blocks added in registers
     constexpr int kRedNtw = kRegEpi ? 0 : NTW;   // LDS reduction buffer: [8 waves][kRedNtw][4][64]
     typedef v4u wvec;
     constexpr int kHLog = H == 16 ? 4 : H == 8 ? 3 : H == 4 ? 2 : H == 2 ? 1 : 0;
     constexpr int RT = 16 / H;                            // weight rows of a tile
-    constexpr int kUnitLog = ONEBIT ? 9 : 8 + kHLog;      // inputs per load unit: 512 (1-bit) or 256 H
+    constexpr int kUnitLog = (ONEBIT ? 9 : 8) + kHLog;    // inputs per load unit: 512 H (1-bit) or 256 H
     constexpr int kUnitWords = 16 * H;                    // packed words of a row per unit
     constexpr int kSteps = ONEBIT ? 8 : 4;                // MFMAs per unit
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -162,7 +163,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
             const int c = min(cb + i, last);
 #pragma unroll
             for (int s = 0; s < kSteps; ++s) {
-                const int p = ONEBIT ? 32 * c + 8 * g + s : 16 * H * c + 4 * (h + H * g) + s;
+                const int p = ONEBIT ? 32 * H * c + 8 * (h + H * g) + s : 16 * H * c + 4 * (h + H * g) + s;
                 v4i a[TG];
 #pragma unroll
                 for (int q = 0; q < TG; ++q)
@@ -289,7 +290,8 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
                 for (int b2 = 0; b2 < 2; ++b2) {
                     const int m = RT * q + 2 * g + b2;
                     if (m >= M) continue;
-                    const int a = acc[q][t][2 * b2] + (b2 ? o3 : o1) - Ssum[m];
+                    const int d = acc[q][t][2 * b2] + (b2 ? o3 : o1);
+                    const int a = (ONEBIT ? 2 * d : d) - Ssum[m];
                     if (acc_out) acc_out[(int64_t)m * N + col] = a;
                     if (y) y[(int64_t)m * N + col] = (float)a * Ssc[m];
                 }
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 #pragma unroll
                     for (int k2 = 0; k2 < KS; ++k2) d += red[(((k2 * CG + cg) * kRedNtw + t) * 4 + v) * kWave + src];
                 }
-                const int a = d - Ssum[m];
+                const int a = (ONEBIT ? 2 * d : d) - Ssum[m];
                 if (acc_out) acc_out[(int64_t)m * N + col] = a;
                 if (y) y[(int64_t)m * N + col] = (float)a * Ssc[m];
             }
@@ -379,7 +381,7 @@ hipError_t launch_ct(const int8_t* xq, const float* gamma, int M, int K, const u
                      float beta, float* y, int32_t* acc, hipStream_t s,
                      const float* beta_g = nullptr) {
     constexpr int KS = kDecWaves * NTW / CT;
-    constexpr int unit_log = ONEBIT ? 9 : H == 16 ? 12 : H == 8 ? 11 : H == 4 ? 10 : H == 2 ? 9 : 8;
+    constexpr int unit_log = (ONEBIT ? 9 : 8) + (H == 16 ? 4 : H == 8 ? 3 : H == 4 ? 2 : H == 2 ? 1 : 0);
     const int cpw = ((K >> unit_log) + KS - 1) / KS;  // load units a wave
     // one batch no larger than the wave's units (a larger one re-reads the
     // last unit and multiplies zero codes for the rest)
@@ -404,18 +406,45 @@ hipError_t launch_ct_groups(const int8_t* xq, const float* gamma, int M, int K, 
     return hipErrorInvalidValue;
 }
 
+// Shape routing of the ungrouped decode product (2-bit or 1-bit weights).
 template <bool ONEBIT>
-hipError_t launch_widths(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
-                         int N, float beta, float* y, int32_t* acc, hipStream_t s) {
-    // widest workgroup that still leaves >= 200 workgroups: fewer, wider
-    // groups copy the activation block fewer times, too few leave CUs idle.
-    // Measured on N = 2560 .. 28672, K = 2560 .. 8192, 2 to 16 tokens: at
-    // K = 4096, N = 11008 (688 tiles) 344 workgroups of 2 tiles beat 172 of 4
-    // up to 8 tokens (M = 4: 6.5 vs 7.2 us; M = 8: 6.7 vs 7.2 us) and tie at
-    // 16; at K = 8192, N = 28672 224 groups of 8 tiles beat 448 of 4.
+hipError_t launch_route(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
+                        float beta, float* y, int32_t* acc, hipStream_t s) {
+    // up to 8 tokens (K a multiple of the two-part unit: 512 inputs, 1024 for
+    // 1-bit weights): two K parts per tile, 8 rows x 128 B a load, one tile a
+    // wave over the whole K.  Widest workgroup that leaves >= 200 workgroups
+    // of 128 rows or >= 150 of 64 rows, else 32 rows (measured, bit-identical
+    // to one part: 8 tokens at K = 8192, N = 28672 15.9 -> 12.0-12.5 us, 1-bit
+    // 10.8 -> 9.9 us; 2..8 tokens at K = 4096, N = 11008 5.7-6.3 -> 4.8-5.1 us,
+    // 1-bit 5.0-5.2 -> 4.7-4.8 us; 5 tokens at K = 2560, N = 6912 5.6 -> 4.1 us)
+    constexpr int kPart = ONEBIT ? 1024 : 512;
+    if (M <= 8 && K % kPart == 0) {
+        if (N / 128 >= 200) return launch_ct<16, 2, ONEBIT, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        if (N / 64 >= 150) return launch_ct<8, 1, ONEBIT, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return launch_ct<4, 1, ONEBIT, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    }
+    // 9..16 tokens on 2-bit weights (K % 512 == 0, many row tiles): two K
+    // parts and two token groups sharing every weight fragment, one K range
+    // per tile (a workgroup holds up to 128 KB of activations, so one per
+    // compute unit: 128-row workgroups once there are >= 200 of them, which
+    // then fill the chip in one round; else 64 rows).  Bit-identical, 16
+    // tokens at K = 8192, N = 28672 15.7 -> 14.4 us; at K = 4096, N = 11008
+    // 6.9 -> 6.0 us; 9..12 tokens there 6.3-6.4 -> 5.6-5.8 us; K = 5120,
+    // N = 13824 7.8 -> 6.9 us (with fewer row tiles, e.g. N = 4000 or 6912, it
+    // is no faster; on 1-bit weights it is slower: 16 tokens at K = 8192,
+    // N = 28672 13.0 against 11.2 us)
+    if (!ONEBIT && K % kPart == 0 && N / 64 >= 150) {
+        if (N / 128 >= 200) return launch_ct<16, 2, false, 1, 2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return launch_ct<8, 1, false, 1, 2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    }
+    // else one 16-row tile a wave, the widest workgroup that still leaves
+    // >= 200 workgroups (fewer, wider groups copy the activation block fewer
+    // times, too few leave CUs idle).  Against two tiles a wave: 16 tokens at
+    // K = 8192, N = 28672 16.6 -> 15.8 us, at K = 4096, N = 11008 6.9 -> 6.7 us;
+    // 1-bit 11.4 -> 11.2 us and 6.0 -> 5.3 us
     const int tiles = (N + 15) / 16;
-    if (tiles >= 8 * 200) return launch_ct<8, 2, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    if (tiles >= 4 * 200) return launch_ct<4, 2, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (tiles >= 8 * 200) return launch_ct<8, 1, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    if (tiles >= 4 * 200) return launch_ct<4, 1, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     if (tiles >= 2 * 200) return launch_ct<2, 1, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     return launch_ct<1, 1, ONEBIT>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
@@ -438,42 +467,13 @@ hipError_t launch_decode_lds_grouped(const int8_t* xq, const float* gamma, int M
 hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
                              const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                              hipStream_t s) {
-    // up to 8 tokens (K % 512 == 0): two K parts per tile, 8 rows x 128 B a
-    // load, one tile a wave over the whole K.  Widest workgroup that leaves
-    // >= 200 workgroups of 128 rows or >= 150 of 64 rows, else 32 rows
-    // (measured, bit-identical to one part: 8 tokens at K = 8192, N = 28672
-    // 15.9 -> 12.0-12.5 us; 2..8 tokens at K = 4096, N = 11008 5.7-6.3 ->
-    // 4.8-5.1 us; 5 tokens at K = 2560, N = 6912 5.6 -> 4.1 us)
-    if (M <= 8 && K % 512 == 0) {
-        if (N / 128 >= 200) return launch_ct<16, 2, false, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-        if (N / 64 >= 150) return launch_ct<8, 1, false, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-        return launch_ct<4, 1, false, 1, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    }
-    // 9..16 tokens (K % 512 == 0, many row tiles): two K parts and two token
-    // groups sharing every weight fragment, one K range per tile (a
-    // workgroup holds up to 128 KB of activations, so one per compute unit:
-    // 128-row workgroups once there are >= 200 of them, which then fill the
-    // chip in one round; else 64 rows).  Bit-identical, 16 tokens at K = 8192,
-    // N = 28672 15.7 -> 14.4 us; at K = 4096, N = 11008 6.9 -> 6.0 us; 9..12
-    // tokens there 6.3-6.4 -> 5.6-5.8 us; K = 5120, N = 13824 7.8 -> 6.9 us
-    // (with fewer row tiles, e.g. N = 4000 or 6912, it is no faster)
-    if (K % 512 == 0 && N / 64 >= 150) {
-        if (N / 128 >= 200) return launch_ct<16, 2, false, 1, 2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-        return launch_ct<8, 1, false, 1, 2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    }
-    // else one 16-row tile a wave (16 tokens at K = 8192, N = 28672 16.6 ->
-    // 15.8 us, at K = 4096, N = 11008 6.9 -> 6.7 us against two tiles)
-    const int tiles = (N + 15) / 16;
-    if (tiles >= 8 * 200) return launch_ct<8, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    if (tiles >= 4 * 200) return launch_ct<4, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    if (tiles >= 2 * 200) return launch_ct<2, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    return launch_ct<1, 1, false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    return launch_route<false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
 
 hipError_t launch_decode_lds1(const int8_t* xq, const float* gamma, int M, int K,
                               const uint32_t* wp1, int N, float beta, float* y, int32_t* acc,
                               hipStream_t s) {
-    return launch_widths<true>(xq, gamma, M, K, wp1, N, beta, y, acc, s);
+    return launch_route<true>(xq, gamma, M, K, wp1, N, beta, y, acc, s);
 }
 
 }  // namespace bl

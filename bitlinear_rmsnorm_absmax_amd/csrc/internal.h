@@ -83,8 +83,9 @@ int decode_a_bytes(int M, int K);
 size_t decode_lds_bytes(int M, int K, int ntw, int G = 1);
 int grouped_width(int tiles, int G, int nchunks);
 bool decode_lds_supports(int M, int K, int N);
-// Whether one token runs on the decode kernel instead of the VALU GEMV.
-bool decode_one_token(int K, int N);
+// Whether one token runs on the decode kernel instead of the VALU GEMV
+// (2-bit or 1-bit weights).
+bool decode_one_token(int K, int N, bool onebit = false);
 hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
                              const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                              hipStream_t s);

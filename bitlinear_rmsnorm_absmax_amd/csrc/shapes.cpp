@@ -52,10 +52,13 @@ bool decode_lds_supports(int M, int K, int N) {
 
 // One token on the decode kernel (two K parts per tile) rather than the VALU
 // GEMV: long rows over many row tiles.  Back-to-back times, bit-identical:
-// K = 8192, N = 28672 12.9 -> 11.4 us; K = 4096, N = 11008 5.1 -> 4.8 us; at
-// K = 2560, N = 6912 and K = N = 2048 the two are equal or the GEMV is faster.
-bool decode_one_token(int K, int N) {
-    return K >= 4096 && K % 512 == 0 && N / 64 >= 150 && decode_lds_supports(1, K, N);
+// K = 8192, N = 28672 12.9 -> 11.4 us (1-bit weights 11.0 -> 8.9 us); K = 4096,
+// N = 11008 5.1 -> 4.8 us (1-bit 4.7 -> 4.5 us); at K = 2560, N = 6912 and
+// K = N = 2048 the two are equal or the GEMV is faster.  The two-part unit is
+// 512 inputs of 2-bit or 1024 of 1-bit weights.
+bool decode_one_token(int K, int N, bool onebit) {
+    return K >= 4096 && K % (onebit ? 1024 : 512) == 0 && N / 64 >= 150 &&
+           decode_lds_supports(1, K, N);
 }
 
 bool decode_lds_grouped_supports(int M, int K, int G, int N) {

@@ -101,10 +101,12 @@ def test_kernel_labels_follow_the_dispatch():
     """The roofline line names the kernel the library's dispatch picks."""
     bench = load_bench()
     # 1-bit: the LDS decode kernel from 5 tokens, and from 2 at K >= 4096
-    assert bench.forward1_kernel(16, 4096) == "decode_lds_kernel"
-    assert bench.forward1_kernel(4, 4096) == "decode_lds_kernel"
-    assert bench.forward1_kernel(4, 2048) == "gemv1_kernel"
-    assert bench.forward1_kernel(1, 8192) == "gemv1_kernel"
+    assert bench.forward1_kernel(16, 4096, 11008) == "decode_lds_kernel"
+    assert bench.forward1_kernel(4, 4096, 11008) == "decode_lds_kernel"
+    assert bench.forward1_kernel(4, 2048, 11008) == "gemv1_kernel"
+    assert bench.forward1_kernel(1, 8192, 28672) == "decode_lds_kernel"
+    assert bench.forward1_kernel(1, 8192, 4096) == "gemv1_kernel"
+    assert bench.forward1_kernel(1, 2048, 2048) == "gemv1_kernel"
     # base-3: one pass on MFMA for 2..16 tokens whose staged block fits
     # 144 KB (16 tokens: K = 8960 fits, K = 8976 does not)
     assert bench.forward3_kernel(16, 8960) == "gemv3_mfma_kernel"

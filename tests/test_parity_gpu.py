@@ -785,7 +785,13 @@ def test_pack_weights1_parity(dev):
                                    (7, 5200, 512), (12, 10300, 1024), (16, 20500, 768),
                                    (16, 20500, 1536), (8, 25600, 6656), (6, 700, 9216),
                                    (16, 333, 8192), (17, 200, 512), (20, 96, 320),
-                                   (4, 11008, 4096), (2, 6500, 8192), (3, 40, 4096)])
+                                   (4, 11008, 4096), (2, 6500, 8192), (3, 40, 4096),
+                                   # two K parts per tile (M <= 8, K % 1024 == 0) on
+                                   # 128-row workgroups; one tile a wave on 128-row groups
+                                   (8, 25700, 2048), (9, 25700, 1024),
+                                   # one token on the decode kernel (K >= 4096,
+                                   # K % 1024 == 0, N / 64 >= 150)
+                                   (1, 9700, 4096), (1, 25700, 5120)])
 def test_forward1_parity(dev, M, N, K):
     rng = workloads.rng_for(962, M, N, K)
     w = np.where(rng.random((N, K)) < 0.5, 1, -1).astype(np.int8)
