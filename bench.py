@@ -433,7 +433,7 @@ def traffic_write(args):
             if call.startswith("quant_forward"):
                 ok = "quant_gemv" in name or "quant_" in name
             elif call.startswith(("quant", "silu")):
-                ok = "quant_rows" in name or "quant_split" in name
+                ok = any(k in name for k in ("quant_rows", "quant_split", "quant_f32"))
             else:
                 ok = "_kernel" in name and "quant_" not in name
             if not ok:
@@ -557,14 +557,34 @@ def trace_summary(args):
                 f"{np.percentile(a, 10):.2f} | {np.percentile(a, 90):.2f}")
 
     def pattern(wid, count):
-        """the launch pattern of a call of workload wid with `count` dispatches"""
+        """the launch pattern of the k calls of workload wid that share one
+        kernel and grid, with `count` dispatches in all: (label, dispatches)
+        in trace order.  The steps launch the k calls in turn (first step,
+        warmup and timed graphs hold k dispatches a step); then each call
+        has its own back-to-back graph and per-launch pairs, one call after
+        the other."""
         head = wid == args.workload
         steps = args.steps if head else args.sub_steps
         warm = args.warmup if head else max(2, args.warmup // 4)
-        for ncopy in range(1, 1024):
+        # the weight copies the bench rotates through for this workload
+        # (packed bytes of the largest weight matrix; GLU: the stacked gate
+        # and up rows), tried first, so that a count two readings fit is
+        # read with the right one
+        wl = workloads.WORKLOADS[wid]
+        rows = 2 * wl.glu_f if wl.glu_f else wl.N
+        expect = max(1, math.ceil(ROTATE_BYTES / (rows * wl.K // 4)))
+        tries = [(k, expect) for k in range(1, 5)] + \
+            [(k, n) for k in range(1, 5) for n in range(1, 1024) if n != expect]
+        for k, ncopy in tries:
             pat = _phase_counts(wid, steps, warm, args.per_launch, ncopy)
-            if sum(c for _, c in pat) == count:
+            if count % k or sum(c for _, c in pat) != count // k:
+                continue
+            if k == 1:
                 return pat
+            shared = [(lab if lab != "timed steps" else f"timed steps ({k} calls)", k * c)
+                      for lab, c in pat[:3]]
+            own = [(f"{lab} (call {j + 1} of {k})", c) for j in range(k) for lab, c in pat[3:]]
+            return shared + own
         return None
 
     lines = [f"# Kernel trace: `{cmd}`", "",
@@ -597,7 +617,8 @@ def trace_summary(args):
             continue
         i = 0
         for lab, c in pat:
-            if lab in ("timed steps", "back-to-back", "per-launch events") and c > 0:
+            if lab.startswith(("timed steps", "back-to-back", "per-launch events")) \
+                    and not lab.startswith("back-to-back first") and c > 0:
                 lines.append(f"| {wname} | `{name}` | {grid} | {lab} | {stats(v[i:i + c])} |")
             i += c
     out = os.path.join(PROFILES, f"kernels_{workloads.WORKLOADS[args.workload].name}.md")

@@ -178,3 +178,49 @@ def test_mfma_counters_give_utilisation(tmp_path, monkeypatch):
     assert bench.read_mfma_util("sweep_k8192_n28672", "quant_act_M512") is None
     text = (tmp_path / "traffic_sweep_k8192_n28672.md").read_text()
     assert "| forward_M512 | 2.405e+11 | 2.405e+11 |" in text
+
+
+def test_trace_phases_split_calls_that_share_a_kernel(tmp_path, monkeypatch):
+    """Two calls of one step run the same kernel at the same grid (one and
+    eight tokens on the decode kernel): their timed-steps dispatches are
+    reported together, and each call's back-to-back graph and per-launch
+    pairs on their own, in bench order."""
+    import argparse
+    import math
+    bench = load_bench()
+    import workloads
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    wid, steps, warmup, per_launch = 5, 4, 2, 3
+    wl = workloads.WORKLOADS[wid]
+    ncopy = max(1, math.ceil(bench.ROTATE_BYTES / (wl.N * wl.K // 4)))
+    reps = max(1, math.ceil(steps / ncopy))
+    kern = "void bl::decode_lds_kernel<16, 2, 2, false, 1, 2, 1>(int)"
+    seq = [(kern, 5.0)] * 2 + [(kern, 6.0)] * (2 * warmup) + [(kern, 10.0)] * (2 * steps)
+    for own in (20.0, 30.0):
+        seq += [(kern, 99.0)] * ncopy + [(kern, own)] * (reps * ncopy) + \
+            [(kern, own + 1.0)] * per_launch
+    seq += [("void bl::floor_stream_read_kernel(int)", 1.0), ("void bl::floor_empty_kernel(int)", 1.0)]
+    d = tmp_path / "trace"
+    d.mkdir()
+    with open(d / "run_kernel_trace.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Workgroup_Size_X"])
+        t = 0
+        for name, us in seq:
+            w.writerow([name, t, t + int(us * 1000), 114688, 512])
+            t += int(us * 1000) + 100
+    args = argparse.Namespace(trace_summary=(str(d), "python3 bench.py"), workload=wid, configs=[],
+                              steps=steps, sub_steps=steps, warmup=warmup, per_launch=per_launch)
+    bench.trace_summary(args)
+    text = (tmp_path / f"kernels_{wl.name}.md").read_text()
+    rows = {}
+    for ln in text.splitlines():
+        cols = ln.split("|")
+        if ln.startswith("| ") and "decode_lds" in ln and len(cols) > 7:
+            rows[cols[4].strip()] = cols[5:7]
+    assert rows["timed steps (2 calls)"][0].strip() == str(2 * steps)
+    assert float(rows["timed steps (2 calls)"][1]) == 10.0
+    assert float(rows["back-to-back (call 1 of 2)"][1]) == 20.0
+    assert float(rows["per-launch events (call 1 of 2)"][1]) == 21.0
+    assert float(rows["back-to-back (call 2 of 2)"][1]) == 30.0
+    assert float(rows["per-launch events (call 2 of 2)"][1]) == 31.0
