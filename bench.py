@@ -116,6 +116,15 @@ def forward3_kernel(M: int, K: int) -> str:
     return "gemv3_mfma_kernel" if 2 <= M <= 16 and fits else "gemv3_kernel"
 
 
+def quant_forward_kernel(M: int, K: int, N: int) -> str:
+    """Kernel of bitlinear_quant_forward when it runs as one launch (one
+    token): the MFMA decode kernel on long rows over many row tiles, else the
+    VALU fused kernel."""
+    lds_fits = ((M * K + 1023) // 1024) * 1024 + 16384 + 128 <= 160 * 1024
+    decode = M == 1 and K >= 4096 and K % 512 == 0 and N // 64 >= 150 and lds_fits
+    return "decode_lds_kernel" if decode else "quant_gemv_kernel"
+
+
 def forward_kernel(M: int, K: int, N: int) -> str:
     """Kernel that bitlinear_forward picks (the library's dispatch)."""
     lds_fits = K % 256 == 0 and ((M * K + 1023) // 1024) * 1024 + 16384 + 128 <= 160 * 1024
@@ -224,7 +233,7 @@ def build_plan(args, torch, bl, dev, wid):
                     L = layers[0]
                     if fused(M, D, 2 * Fh):
                         if run(f"quant_forward_rms_gateup_M{M}", M, L.N, L.K, L.wbytes,
-                               4 * M * D + 4 * D, "quant_gemv_kernel"):
+                               4 * M * D + 4 * D, quant_forward_kernel(M, D, 2 * Fh)):
                             check(lib.bitlinear_quant_forward(
                                 b["x"].data_ptr(), bl.F32, M, D, gain.data_ptr(), wl.rms_eps,
                                 L.copies[c].data_ptr(), 2 * Fh, 1.0, b["q"].data_ptr(),
@@ -287,7 +296,7 @@ def build_plan(args, torch, bl, dev, wid):
             M = b["M"]
             if fused(M, K, N):
                 xb = M * K * (2 if b["dt"] == bl.BF16 else 4)
-                if run(f"quant_forward_M{M}", M, N, K, L.wbytes, xb, "quant_gemv_kernel"):
+                if run(f"quant_forward_M{M}", M, N, K, L.wbytes, xb, quant_forward_kernel(M, K, N)):
                     check(lib.bitlinear_quant_forward(b["x"].data_ptr(), b["dt"], M, K, None, 0.0,
                                                       wptr, N, L.beta, b["q"].data_ptr(),
                                                       b["g"].data_ptr(), b["y"].data_ptr(), None,
@@ -431,7 +440,7 @@ def traffic_write(args):
                              f"the probe made {len(calls)}")
         for call, (name, _) in zip(calls, lib):
             if call.startswith("quant_forward"):
-                ok = "quant_gemv" in name or "quant_" in name
+                ok = "quant_gemv" in name or "decode_lds" in name
             elif call.startswith(("quant", "silu")):
                 ok = any(k in name for k in ("quant_rows", "quant_split", "quant_f32"))
             else:

@@ -219,6 +219,12 @@ bitlinear_status_t bitlinear_quant_forward(const void* x, bitlinear_dtype_t x_dt
     if (y && !aligned(y, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: y is not 4-byte aligned", fn);
     if (acc && !aligned(acc, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: acc is not 4-byte aligned", fn);
     if (M == 0) return ok();
+    // one token on long rows over many row tiles: quantised inside the
+    // two-part decode kernel; smaller one-token shapes: the VALU fused kernel
+    if (M == 1 && bl::decode_one_token((int)K, (int)N))
+        return from_hip(bl::launch_quant_decode1(x, x_dtype == BITLINEAR_BF16, (int)K, rms_gain, rms_eps,
+                                                 w_packed, (int)N, beta, y, acc, x_q, gamma, stream),
+                        fn);
     if (bl::quant_gemv_supports((int)M, (int)K, (int)N))
         return from_hip(bl::launch_quant_gemv(x, x_dtype == BITLINEAR_BF16, (int)K, rms_gain,
                                               rms_eps, w_packed, (int)N, beta, y, acc, x_q, gamma,
@@ -432,7 +438,7 @@ bitlinear_status_t bitlinear_forward_grouped(const int8_t* x_q, const float* gam
 
 int bitlinear_quant_forward_one_launch(int64_t M, int64_t K, int64_t N) {
     if (M != 1 || K < 1 || K > BITLINEAR_MAX_K || N < 1 || N > kMaxN) return 0;
-    return bl::quant_gemv_supports((int)M, (int)K, (int)N) ? 1 : 0;
+    return (bl::decode_one_token((int)K, (int)N) || bl::quant_gemv_supports((int)M, (int)K, (int)N)) ? 1 : 0;
 }
 
 int bitlinear_forward_grouped_one_launch(int64_t M, int64_t K, int64_t G, int64_t N) {

@@ -39,11 +39,23 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "quant_rows.h"
 
 namespace bl {
 namespace {
 
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// One token quantised inside the kernel (FQ != 0): the fp32 or bf16 row, the
+// optional RMSNorm gain and epsilon, and where workgroup 0 writes the codes
+// and gamma.
+struct FusedRow {
+    const void* x = nullptr;
+    const float* gain = nullptr;
+    float eps = 0.0f;
+    int8_t* q_out = nullptr;
+    float* gamma_out = nullptr;
+};
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt and expcnt any
 constexpr int vm_wait_imm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | (0xF << 8); }
@@ -80,17 +92,26 @@ __device__ __forceinline__ void fence_code() {
 // 8 x 128 B loads.  With one K range per tile (KS == 1) the two diagonal
 // blocks are added in registers (lane 2r + 16 q' and its odd neighbour) and no
 // LDS reduction buffer is allocated.
-template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1, int TG = 1>
+// FQ != 0 (one token, two K parts): the token arrives unquantised (FQ = 1
+// fp32, 2 bf16; FRMS: RMSNorm first) and every workgroup quantises it into
+// its LDS row, in the chunk order and reduction order of the quantiser
+// (quant_rows.h, the first 256 threads), so gamma and the codes are
+// bit-identical to bitlinear_quant_act's; workgroup 0 also writes them out.
+// The row's first chunks are loaded before the weights (loads of a compute
+// unit return in issue order) and quantised while the first weights land.
+template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1, int TG = 1, int FQ = 0,
+          bool FRMS = false>
 __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
     const uint32_t* wp, int N, float beta, float* __restrict__ y, int32_t* __restrict__ acc_out,
-    int a_bytes, const float* __restrict__ beta_g) {
+    int a_bytes, const float* __restrict__ beta_g, FusedRow fr) {
     constexpr int CG = CT / NTW;         // column groups of a workgroup
     constexpr int KS = kDecWaves / CG;   // K ranges per column group
     static_assert(KS % G == 0, "every wave's K range lies inside one group");
     static_assert(H == 1 || ((H == 2 || H == 4 || H == 8 || H == 16) && G == 1 && (!ONEBIT || H == 2)),
                   "K parts: one group (1-bit weights: two parts)");
     static_assert(TG == 1 || (H == 2 && KS == 1), "token groups: two K parts, one K range");
+    static_assert(FQ == 0 || (H == 2 && TG == 1 && KS == 1 && !ONEBIT), "fused quantisation: one token");
     constexpr bool kRegEpi = H == 2 && KS == 1;  // diagonal blocks added in registers
     constexpr int kRedNtw = kRegEpi ? 0 : NTW;   // LDS reduction buffer: [8 waves][kRedNtw][4][64]
     typedef v4u wvec;
@@ -191,14 +212,80 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     // else and used only at publish: issued after the weight loads, their
     // first use would wait for all of those
     float g_mine = 0.0f, b_mine = beta;
-    if (tid < 16 * G) {
+    if (FQ == 0 && tid < 16 * G) {
         const int gi = tid >> 4, ri = tid & 15;
         if (ri < M) g_mine = gamma[(int64_t)gi * M + ri];
         if (beta_g) b_mine = beta_g[gi];
     }
 
-    // 1. activation copies of the whole workgroup, queued ahead of any weight load
-    {
+    // 1. activation copies of the whole workgroup, queued ahead of any weight
+    //    load (fused quantisation: the first chunks of the token's row)
+    constexpr Src kQS = FQ == 2 ? Src::BF16 : Src::F32;
+    const RowSrc qsrc{fr.x, nullptr};
+    const bool quantiser = FQ != 0 && tid < kQuantThreads;
+    const int qchunks = K / 16;
+    // raw 16-byte vectors of the cached chunks (4 of fp32, 2 of bf16): the
+    // widening to fp32 waits for the load, so it is left to the absmax pass,
+    // after the weight loads have been issued
+    constexpr int kRawVec = FQ == 2 ? 2 : 4;
+    v4u qraw[FQ ? kQuantCache : 1][kRawVec];
+    float gcache[FRMS ? kQuantCache : 1][16];
+    auto raw_chunk = [&](int c, v4u (&r)[kRawVec]) {
+        const v4u* p = reinterpret_cast<const v4u*>(static_cast<const char*>(fr.x) +
+                                                    (int64_t)c * 16 * (FQ == 2 ? 2 : 4));
+#pragma unroll
+        for (int i = 0; i < kRawVec; ++i) r[i] = __builtin_nontemporal_load(p + i);
+    };
+    auto widen = [&](const v4u (&r)[kRawVec], float v[16]) {
+#pragma unroll
+        for (int i = 0; i < kRawVec; ++i) {
+            const uint32_t d[4] = {r[i].x, r[i].y, r[i].z, r[i].w};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                if constexpr (FQ == 2) {
+                    v[8 * i + 2 * jj] = __uint_as_float(d[jj] << 16);  // exact widening
+                    v[8 * i + 2 * jj + 1] = __uint_as_float(d[jj] & 0xFFFF0000u);
+                } else {
+                    v[4 * i + jj] = __uint_as_float(d[jj]);
+                }
+            }
+        }
+    };
+    auto load_gain = [&](int c, float g16[16]) {
+        const float4* pg = reinterpret_cast<const float4*>(fr.gain + (int64_t)c * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 gv = pg[i];
+            g16[4 * i] = gv.x; g16[4 * i + 1] = gv.y; g16[4 * i + 2] = gv.z; g16[4 * i + 3] = gv.w;
+        }
+    };
+    // plain rows (no RMSNorm: the absmax is a max, exact in any order): all
+    // threads take the row as 16-byte pieces dealt round-robin, so every wave
+    // load reads 1 KB contiguous; the first kPlainVec pieces of a thread stay
+    // in registers
+    constexpr int kPlainVec = 4;
+    constexpr int kEpv = FQ == 2 ? 8 : 4;  // entries per 16-byte piece
+    const int npiece = K / kEpv;
+    const v4u* xrow = reinterpret_cast<const v4u*>(fr.x);
+    v4u praw[FQ != 0 && !FRMS ? kPlainVec : 1];
+    if constexpr (FQ != 0 && !FRMS) {
+#pragma unroll
+        for (int i = 0; i < kPlainVec; ++i) {
+            const int idx = min(tid + i * kDecWaves * kWave, npiece - 1);
+            praw[i] = __builtin_nontemporal_load(xrow + idx);
+        }
+    } else if constexpr (FQ != 0) {
+        if (quantiser) {
+#pragma unroll
+            for (int i = 0; i < kQuantCache; ++i) {
+                const int c = tid + i * kQuantThreads;
+                if (c < qchunks) {
+                    raw_chunk(c, qraw[i]);
+                    if constexpr (FRMS) load_gain(c, gcache[i]);
+                }
+            }
+        }
+    } else {
         // row = pos / WR and group = k / KG by multiply-high with a reciprocal
         // taken once: floor(x / d) = umulhi(x, floor((2^32 - 1) / d) + 1),
         // exact for x * d < 2^32 (here pos * WR < 2^30 and (k/256) * (KG/256)
@@ -222,7 +309,168 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 
     // 2. the first batch of weight loads stays in flight across the barrier
     //    that publishes the activations; 3. activation sums while it lands
+    __shared__ int s_qsum[kDecWaves];
+    // plain rows: absmax over the pieces, codes of each piece into the LDS
+    // row (4 or 8 bytes at its entries' offset), their sum
+    auto publish_plain = [&]() {
+        float amax = 0.0f;
+        auto pmax = [&](const v4u& t) {
+            const uint32_t d[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                if constexpr (FQ == 2) {
+                    amax = fmaxf(amax, fabsf(__uint_as_float(d[jj] << 16)));
+                    amax = fmaxf(amax, fabsf(__uint_as_float(d[jj] & 0xFFFF0000u)));
+                } else {
+                    amax = fmaxf(amax, fabsf(__uint_as_float(d[jj])));
+                }
+            }
+        };
+        constexpr int T = kDecWaves * kWave;
+#pragma unroll
+        for (int i = 0; i < kPlainVec; ++i)
+            if (tid + i * T < npiece) pmax(praw[i]);
+        for (int idx = tid + kPlainVec * T; idx < npiece; idx += T) pmax(__builtin_nontemporal_load(xrow + idx));
+        double ss = 0.0;
+        block_reduce<kDecWaves>(amax, ss, false);
+        int csum = 0;
+        auto put = [&](int idx, const v4u& t) {
+            const uint32_t d[4] = {t.x, t.y, t.z, t.w};
+            uint32_t c[2] = {0u, 0u};
+            if (amax != 0.0f) {
+                if constexpr (FQ == 2) {
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int q0 = quant_code(__uint_as_float(d[2 * h2] << 16), amax);
+                        const int q1 = quant_code(__uint_as_float(d[2 * h2] & 0xFFFF0000u), amax);
+                        const int q2 = quant_code(__uint_as_float(d[2 * h2 + 1] << 16), amax);
+                        const int q3 = quant_code(__uint_as_float(d[2 * h2 + 1] & 0xFFFF0000u), amax);
+                        csum += q0 + q1 + q2 + q3;
+                        c[h2] = pack4(q0, q1, q2, q3);
+                    }
+                } else {
+                    const int q0 = quant_code(__uint_as_float(d[0]), amax), q1 = quant_code(__uint_as_float(d[1]), amax);
+                    const int q2 = quant_code(__uint_as_float(d[2]), amax), q3 = quant_code(__uint_as_float(d[3]), amax);
+                    csum += q0 + q1 + q2 + q3;
+                    c[0] = pack4(q0, q1, q2, q3);
+                }
+            }
+            if constexpr (FQ == 2) {
+                *reinterpret_cast<v2u*>(As + 8 * idx) = v2u{c[0], c[1]};
+                if (blockIdx.x == 0) *reinterpret_cast<v2u*>(fr.q_out + 8 * (int64_t)idx) = v2u{c[0], c[1]};
+            } else {
+                *reinterpret_cast<uint32_t*>(As + 4 * idx) = c[0];
+                if (blockIdx.x == 0) *reinterpret_cast<uint32_t*>(fr.q_out + 4 * (int64_t)idx) = c[0];
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < kPlainVec; ++i)
+            if (tid + i * T < npiece) put(tid + i * T, praw[i]);
+        for (int idx = tid + kPlainVec * T; idx < npiece; idx += T) put(idx, __builtin_nontemporal_load(xrow + idx));
+        csum = wave_sum_i(csum);
+        if (lane == 0) s_qsum[wv] = csum;
+        if (blockIdx.x == 0 && tid == 0) fr.gamma_out[0] = amax;
+        __syncthreads();  // the codes and the partial sums are visible
+        if (tid < 16) {
+            int S = 0;
+#pragma unroll
+            for (int i = 0; i < kDecWaves; ++i) S += s_qsum[i];
+            Ssum[tid] = tid == 0 ? S : 0;
+            Ssc[tid] = tid == 0 ? out_scale(beta, amax) : 0.0f;
+        }
+    };
+    // fused quantisation: absmax (and the float64 sum of squares) over the
+    // row as the quantiser takes it, codes into the LDS row (slot = piece:
+    // row 0 is not swizzled), their sum, and the output scale
+    auto publish_fused = [&]() {
+        float amax = 0.0f;
+        double ss = 0.0;
+        auto process = [&](float v[16], const float g16[16]) {
+            if constexpr (FRMS) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float xv = v[e];
+                    ss += (double)xv * (double)xv;
+                    v[e] = g16[e] * xv;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 16; ++e) amax = fmaxf(amax, fabsf(v[e]));
+        };
+        float qcache[kQuantCache][16];
+        if (quantiser) {
+#pragma unroll
+            for (int i = 0; i < kQuantCache; ++i) {
+                const int c = tid + i * kQuantThreads;
+                if (c < qchunks) {
+                    widen(qraw[i], qcache[i]);
+                    process(qcache[i], gcache[FRMS ? i : 0]);
+                }
+            }
+            for (int c = tid + kQuantCache * kQuantThreads; c < qchunks; c += kQuantThreads) {
+                float v[16], g16[16];
+                load_chunk<kQS>(qsrc, 0, K, c, v);
+                if constexpr (FRMS) load_gain(c, g16);
+                process(v, g16);
+            }
+        }
+        block_reduce<kQuantThreads / kWave>(amax, ss, FRMS);
+        float gq = amax;
+        if constexpr (FRMS) gq = (float)((1.0 / sqrt(ss / (double)K + (double)fr.eps)) * (double)amax);
+        int csum = 0;
+        auto put_codes = [&](int c, const float v[16]) {
+            uint32_t d[4] = {0u, 0u, 0u, 0u};
+            if (amax != 0.0f) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int q0 = quant_code(v[4 * jj], amax), q1 = quant_code(v[4 * jj + 1], amax);
+                    const int q2 = quant_code(v[4 * jj + 2], amax), q3 = quant_code(v[4 * jj + 3], amax);
+                    csum += q0 + q1 + q2 + q3;
+                    d[jj] = pack4(q0, q1, q2, q3);
+                }
+            }
+            const v4u dv = v4u{d[0], d[1], d[2], d[3]};
+            *reinterpret_cast<v4u*>(As + 16 * c) = dv;
+            if (blockIdx.x == 0) *reinterpret_cast<v4u*>(fr.q_out + 16 * (int64_t)c) = dv;
+        };
+        if (quantiser) {
+#pragma unroll
+            for (int i = 0; i < kQuantCache; ++i) {
+                const int c = tid + i * kQuantThreads;
+                if (c < qchunks) put_codes(c, qcache[i]);
+            }
+            for (int c = tid + kQuantCache * kQuantThreads; c < qchunks; c += kQuantThreads) {
+                float v[16];
+                load_chunk<kQS>(qsrc, 0, K, c, v);
+                if constexpr (FRMS) {
+                    float g16[16];
+                    load_gain(c, g16);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) v[e] *= g16[e];
+                }
+                put_codes(c, v);
+            }
+            csum = wave_sum_i(csum);
+            if (lane == 0) s_qsum[wv] = csum;
+        }
+        if (blockIdx.x == 0 && tid == 0) fr.gamma_out[0] = gq;
+        __syncthreads();  // the codes and the partial sums are visible
+        if (tid < 16) {
+            int S = 0;
+#pragma unroll
+            for (int i = 0; i < kQuantThreads / kWave; ++i) S += s_qsum[i];
+            Ssum[tid] = tid == 0 ? S : 0;
+            Ssc[tid] = tid == 0 ? out_scale(beta, gq) : 0.0f;
+        }
+    };
     auto publish = [&]() {
+        if constexpr (FQ != 0 && !FRMS) {
+            publish_plain();
+            return;
+        } else if constexpr (FQ != 0) {
+            publish_fused();
+            return;
+        }
         fence_code();
         __builtin_amdgcn_s_waitcnt(vm_wait_imm(B * NTW));  // own copies (older) have landed
         __builtin_amdgcn_s_barrier();
@@ -356,39 +604,42 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
 }
 
 
-template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1, int TG = 1>
+template <int CT, int NTW, int B, bool ONEBIT, int G, int H = 1, int TG = 1, int FQ = 0, bool FRMS = false>
 hipError_t launch_ctb(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
-                      float beta, float* y, int32_t* acc, hipStream_t s, const float* beta_g) {
+                      float beta, float* y, int32_t* acc, hipStream_t s, const float* beta_g,
+                      FusedRow fr = {}) {
     static DynLdsOptIn opt_in;
     const hipError_t e = opt_in.ensure(
-        reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT, G, H, TG>), kDecLdsMax);
+        reinterpret_cast<const void*>(&decode_lds_kernel<CT, NTW, B, ONEBIT, G, H, TG, FQ, FRMS>),
+        kDecLdsMax);
     if (e != hipSuccess) return e;
     constexpr int rows = 16 / H * CT;  // weight rows of a workgroup
     constexpr int red_ntw = (H == 2 && kDecWaves * NTW / CT == 1) ? 0 : NTW;  // no LDS reduction
     const size_t lds = decode_lds_bytes(M, K, red_ntw, G);
     if (M > 16 / H * TG || lds > (size_t)kDecLdsMax) return hipErrorInvalidValue;
     const int blocks = (N + rows - 1) / rows;
-    decode_lds_kernel<CT, NTW, B, ONEBIT, G, H, TG><<<dim3(blocks), dim3(kDecWaves * kWave), lds, s>>>(
-        xq, gamma, M, K, wp, N, beta, y, acc, decode_a_bytes(M, K), beta_g);
+    decode_lds_kernel<CT, NTW, B, ONEBIT, G, H, TG, FQ, FRMS>
+        <<<dim3(blocks), dim3(kDecWaves * kWave), lds, s>>>(xq, gamma, M, K, wp, N, beta, y, acc,
+                                                            decode_a_bytes(M, K), beta_g, fr);
     return hipGetLastError();
 }
 
 // Batch: a wave's whole K range in one batch when it has at most 4 load units,
 // else a stream of 2-unit batches (measured at K = 2560 .. 8192: larger
 // batches stall load issue, a 2-chunk stream is 15 % faster at K = 8192).
-template <int CT, int NTW, bool ONEBIT, int G = 1, int H = 1, int TG = 1>
+template <int CT, int NTW, bool ONEBIT, int G = 1, int H = 1, int TG = 1, int FQ = 0, bool FRMS = false>
 hipError_t launch_ct(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp, int N,
                      float beta, float* y, int32_t* acc, hipStream_t s,
-                     const float* beta_g = nullptr) {
+                     const float* beta_g = nullptr, FusedRow fr = {}) {
     constexpr int KS = kDecWaves * NTW / CT;
     constexpr int unit_log = (ONEBIT ? 9 : 8) + (H == 16 ? 4 : H == 8 ? 3 : H == 4 ? 2 : H == 2 ? 1 : 0);
     const int cpw = ((K >> unit_log) + KS - 1) / KS;  // load units a wave
     // one batch no larger than the wave's units (a larger one re-reads the
     // last unit and multiplies zero codes for the rest)
-    if (cpw <= 1) return launch_ctb<CT, NTW, 1, ONEBIT, G, H, TG>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
-    if (cpw <= 2) return launch_ctb<CT, NTW, 2, ONEBIT, G, H, TG>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
-    if (cpw <= 4) return launch_ctb<CT, NTW, 4, ONEBIT, G, H, TG>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
-    return launch_ctb<CT, NTW, 2, ONEBIT, G, H, TG>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g);
+    if (cpw <= 1) return launch_ctb<CT, NTW, 1, ONEBIT, G, H, TG, FQ, FRMS>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g, fr);
+    if (cpw <= 2) return launch_ctb<CT, NTW, 2, ONEBIT, G, H, TG, FQ, FRMS>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g, fr);
+    if (cpw <= 4) return launch_ctb<CT, NTW, 4, ONEBIT, G, H, TG, FQ, FRMS>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g, fr);
+    return launch_ctb<CT, NTW, 2, ONEBIT, G, H, TG, FQ, FRMS>(xq, gamma, M, K, wp, N, beta, y, acc, s, beta_g, fr);
 }
 
 // Grouped launch of one width: G as a template argument (2, 4 or 8, at most
@@ -468,6 +719,31 @@ hipError_t launch_decode_lds(const int8_t* xq, const float* gamma, int M, int K,
                              const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
                              hipStream_t s) {
     return launch_route<false>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+}
+
+namespace {
+template <int FQ, bool FRMS>
+hipError_t launch_quant_decode_t(int K, const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
+                                 hipStream_t s, FusedRow fr) {
+    // the two-part one-token routes of launch_route (x_q and gamma come from
+    // the kernel itself: their pointers are the outputs)
+    if (N / 128 >= 200)
+        return launch_ct<16, 2, false, 1, 2, 1, FQ, FRMS>(fr.q_out, fr.gamma_out, 1, K, wp, N, beta, y, acc, s,
+                                                          nullptr, fr);
+    return launch_ct<8, 1, false, 1, 2, 1, FQ, FRMS>(fr.q_out, fr.gamma_out, 1, K, wp, N, beta, y, acc, s,
+                                                     nullptr, fr);
+}
+}  // namespace
+
+hipError_t launch_quant_decode1(const void* x, bool bf16, int K, const float* gain, float eps,
+                                const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
+                                int8_t* x_q, float* gamma, hipStream_t s) {
+    const FusedRow fr{x, gain, eps, x_q, gamma};
+    if (bf16)
+        return gain ? launch_quant_decode_t<2, true>(K, wp, N, beta, y, acc, s, fr)
+                    : launch_quant_decode_t<2, false>(K, wp, N, beta, y, acc, s, fr);
+    return gain ? launch_quant_decode_t<1, true>(K, wp, N, beta, y, acc, s, fr)
+                : launch_quant_decode_t<1, false>(K, wp, N, beta, y, acc, s, fr);
 }
 
 hipError_t launch_decode_lds1(const int8_t* xq, const float* gamma, int M, int K,

@@ -12,9 +12,11 @@ namespace bl {
 
 // Opt-in of one kernel to more than 64 KB of dynamic LDS, made once per
 // device (the attribute belongs to the calling thread's current device, the
-// device of the launch's stream in the usual setup).  One object per kernel
-// (a function-local static of its launcher); concurrent first calls may both
-// set the attribute, which is idempotent.
+// device of the launch's stream in the usual setup).  The dynamic maximum
+// set is `bytes`, at most the compute unit's 160 KB less the kernel's static
+// LDS (hipFuncGetAttributes): the two together may not exceed it.  One
+// object per kernel (a function-local static of its launcher); concurrent
+// first calls may both set the attribute, which is idempotent.
 class DynLdsOptIn {
   public:
     hipError_t ensure(const void* kernel, int bytes) {
@@ -22,7 +24,12 @@ class DynLdsOptIn {
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < kMaxDevices && done_[dev].load(std::memory_order_acquire)) return hipSuccess;
-        e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        hipFuncAttributes attr{};
+        e = hipFuncGetAttributes(&attr, kernel);
+        if (e != hipSuccess) return e;
+        const int cap = 160 * 1024 - (int)attr.sharedSizeBytes;
+        e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                bytes < cap ? bytes : cap);
         if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done_[dev].store(true, std::memory_order_release);
         return e;
     }
@@ -83,6 +90,12 @@ int decode_a_bytes(int M, int K);
 size_t decode_lds_bytes(int M, int K, int ntw, int G = 1);
 int grouped_width(int tiles, int G, int nchunks);
 bool decode_lds_supports(int M, int K, int N);
+// One token quantised inside the decode kernel (fp32 or bf16 row, optional
+// RMSNorm gain) and multiplied, when decode_one_token(K, N): x_q and gamma
+// are written, bit-identical to bitlinear_quant_act's.
+hipError_t launch_quant_decode1(const void* x, bool bf16, int K, const float* gain, float eps,
+                                const uint32_t* wp, int N, float beta, float* y, int32_t* acc,
+                                int8_t* x_q, float* gamma, hipStream_t s);
 // Whether one token runs on the decode kernel instead of the VALU GEMV
 // (2-bit or 1-bit weights).
 bool decode_one_token(int K, int N, bool onebit = false);

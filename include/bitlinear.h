@@ -131,9 +131,11 @@ bitlinear_status_t bitlinear_forward(const int8_t* x_q, const float* gamma, int6
  * absmax quantisation, ternary product; unite.ai article, 2.
  * Aktivierungsquantisierung and 3. BitLinear-Betrieb).  Arguments as in those
  * two calls; x_q and gamma are outputs here and are written in every case.
- * For one token with K % 64 == 0, K <= 16384 and N <= 16384 it runs as one
- * kernel (each workgroup quantises the token into LDS and multiplies its
- * weight rows); otherwise as the two calls in order on `stream`.  x_q, gamma, y and acc are
+ * One token runs as one kernel in which each workgroup quantises the token
+ * into LDS and multiplies its weight rows: on the MFMA decode kernel when
+ * K >= 4096, K % 512 == 0 and N / 64 >= 150 (long rows over many row tiles),
+ * else on the vector ALUs when K % 64 == 0, K <= 16384 and N <= 16384;
+ * otherwise the two calls run in order on `stream`.  x_q, gamma, y and acc are
  * bit-identical to those of the two calls; y may be NULL when acc is given.
  */
 bitlinear_status_t bitlinear_quant_forward(const void* x, bitlinear_dtype_t x_dtype, int64_t M,

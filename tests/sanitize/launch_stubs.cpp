@@ -28,6 +28,8 @@ hipError_t launch_decode_lds_grouped(const int8_t*, const float*, int, int, int,
                                      const float*, float*, int32_t*, hipStream_t) { return hipSuccess; }
 hipError_t launch_decode_lds1(const int8_t*, const float*, int, int, const uint32_t*, int, float, float*,
                               int32_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_quant_decode1(const void*, bool, int, const float*, float, const uint32_t*, int, float,
+                                float*, int32_t*, int8_t*, float*, hipStream_t) { return hipSuccess; }
 hipError_t launch_pairwise_mean(const float*, int64_t, int64_t, int64_t, bool, int, double*, double*,
                                 float*, hipStream_t) { return hipSuccess; }
 hipError_t launch_binarize(const float*, int64_t, int64_t, uint32_t*, int8_t*, double*, float*, double*,

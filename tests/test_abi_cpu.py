@@ -358,7 +358,10 @@ def test_quant_forward_one_launch_query():
     assert q(1, 4096, 11008) == 1
     assert q(1, 16384, 16384) == 1
     assert q(1, 64, 1) == 1
-    assert q(1, 8192, 28672) == 0         # past 16384 rows: the two calls
+    assert q(1, 8192, 28672) == 1         # long rows over many row tiles: the MFMA decode kernel
+    assert q(1, 20480, 28672) == 1        # longer than the VALU kernel's LDS copy: MFMA decode
+    assert q(1, 2048, 28672) == 0         # past 16384 rows with short rows: the two calls
+    assert q(1, 4352, 20000) == 0         # K % 512 != 0 past 16384 rows: the two calls
     assert q(1, 16448, 40) == 0           # the codes of a longer token do not fit the LDS copy
     assert q(1, 1040, 77) == 0            # K not a multiple of 64
     assert q(2, 4096, 1000) == 0          # several tokens

@@ -120,6 +120,11 @@ def test_kernel_labels_follow_the_dispatch():
     assert bench.forward_kernel(1, 2560, 6912) == "gemv_valu_kernel"
     assert bench.forward_kernel(1, 4096, 11008) == "decode_lds_kernel"
     assert bench.forward_kernel(1, 8192, 28672) == "decode_lds_kernel"
+    # one token quantised inside the kernel: MFMA decode on long rows, else VALU
+    assert bench.quant_forward_kernel(1, 8192, 28672) == "decode_lds_kernel"
+    assert bench.quant_forward_kernel(1, 4096, 11008) == "decode_lds_kernel"
+    assert bench.quant_forward_kernel(1, 2048, 2048) == "quant_gemv_kernel"
+    assert bench.quant_forward_kernel(1, 2560, 13824) == "quant_gemv_kernel"
     assert bench.forward_kernel(16, 4096, 11008) == "decode_lds_kernel"
 
 

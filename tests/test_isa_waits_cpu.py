@@ -13,6 +13,9 @@ GPU) and checks, for every instantiation:
   vector-memory wait, and its count equals the copies the loop issues per
   step (with three stages, the step just issued stays in flight while the
   wave waits for the one before it);
+- decode with the token quantised in the kernel: the first wait for the
+  row's chunks leaves the first batch of weight loads (issued after them)
+  in flight;
 - decode (``decode_lds_kernel``): every wait that publishes the activation
   block (a vmcnt wait followed by the barrier after the copies' barrier, with
   no multiply in between) counts exactly the weight loads issued between the
@@ -95,10 +98,30 @@ def test_ring_gemm_waits_match_its_copies(tmp_path):
         assert not others, f"{name}: other vector-memory instructions in the loop: {others[:3]}"
 
 
+def _fused(name):
+    """decode_lds_kernel<..., FQ, FRMS>: FQ != 0 quantises one token in the kernel"""
+    m = re.search(r"ELi(\d+)ELb[01]EEEv", name)
+    return m is not None and int(m.group(1)) != 0
+
+
 def test_decode_publish_waits_match_its_weight_loads(tmp_path):
     funcs = _functions(_asm("decode_lds.hip", tmp_path), "decode_lds_kernel")
     assert funcs, "no decode_lds_kernel instantiation found"
+    assert any(_fused(n) for n in funcs) and any(not _fused(n) for n in funcs)
     for name, lines in funcs.items():
+        if _fused(name):
+            # the row's chunk loads, a barrier, the first weight batch; the
+            # waits for the cached chunks must leave that batch in flight
+            b = next(i for i, l in enumerate(lines) if l.startswith("s_barrier"))
+            assert any(re.match(r"global_load_dword", l) for l in lines[:b]), f"{name}: no row loads"
+            k = b + 1
+            while k < len(lines) and not lines[k].startswith(("s_waitcnt", "s_cbranch", ".LBB")):
+                k += 1
+            weights = sum(bool(re.match(r"global_load_dword", l)) for l in lines[b + 1:k])
+            assert weights > 0, f"{name}: no weight loads after the row loads"
+            first = next(_vmcnt(l) for l in lines[k:] if _vmcnt(l) is not None)
+            assert first >= weights, f"{name}: vmcnt({first}) waits for the {weights} weight loads"
+            continue
         barriers = [i for i, l in enumerate(lines) if l.startswith("s_barrier")]
         checked = 0
         for b in barriers:

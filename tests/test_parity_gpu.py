@@ -1127,6 +1127,13 @@ QFWD_CASES = [(1, 64, 1, "f32", None), (1, 2048, 1000, "bf16", "unit"),
               (1, 512, 8193, "f32", "unit"), (1, 512, 16384, "f32", None),
               (1, 256, 16385, "f32", None), (1, 8192, 28672, "f32", None),
               (1, 4096, 16385, "bf16", "unit"),
+              # one token quantised inside the MFMA decode kernel (K >= 4096,
+              # K % 512 == 0, N / 64 >= 150): fp32 and bf16 rows, with and
+              # without RMSNorm, 128- and 64-row workgroups, rows past the
+              # quantiser's register cache (K > 8192), ragged row tails
+              (1, 8192, 25700, "bf16", "rand"), (1, 4608, 9631, "f32", "rand"),
+              (1, 12288, 9700, "f32", None), (1, 20480, 9650, "bf16", None),
+              (1, 5120, 26000, "f32", "unit"),
               (1, 16448, 40, "f32", None), (1, 1040, 77, "bf16", "rand"),
               (3, 4096, 500, "bf16", "rand"), (16, 2560, 700, "f32", None),
               # 2..4 tokens on the LDS decode route (K >= 4096) at every tile
@@ -1155,7 +1162,8 @@ def test_quant_forward_parity(dev, M, K, N, dt, gain_kind):
     wp = gpu_pack(w, dev)
     outs = dict(y=Guard((M, N), torch.float32, dev), q=Guard((M, K), torch.int8, dev),
                 g=Guard((M,), torch.float32, dev), acc=Guard((M, N), torch.int32, dev))
-    one = M == 1 and K % 64 == 0 and K <= 16384 and N <= 16384
+    decode_one = M == 1 and K >= 4096 and K % 512 == 0 and N // 64 >= 150
+    one = decode_one or (M == 1 and K % 64 == 0 and K <= 16384 and N <= 16384)
     assert bl.lib.bitlinear_quant_forward_one_launch(M, K, N) == int(one)
     st = bl.lib.bitlinear_quant_forward(
         xd.data_ptr(), bl.BF16 if dt == "bf16" else bl.F32, M, K, None if gd is None else gd.data_ptr(),
@@ -1184,8 +1192,10 @@ def test_quant_forward_parity(dev, M, K, N, dt, gain_kind):
     np.testing.assert_array_equal(y.view(np.uint32), host(y2).view(np.uint32))
 
 
-def test_quant_forward_zero_token_and_extremes(dev):
-    K, N = 4096, 333
+@pytest.mark.parametrize("N", [333, 9700])  # VALU fused kernel; MFMA decode kernel
+def test_quant_forward_zero_token_and_extremes(dev, N):
+    K = 4096
+    assert bl.lib.bitlinear_quant_forward_one_launch(1, K, N) == 1
     w = workloads.ternary(workloads.rng_for(1102), N, K, workloads.TERNARY_UNIFORM)
     w[0, :] = 1
     w[1, :] = -1
