@@ -310,6 +310,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
     // 2. the first batch of weight loads stays in flight across the barrier
     //    that publishes the activations; 3. activation sums while it lands
     __shared__ int s_qsum[kDecWaves];
+    __shared__ float s_qmax[kDecWaves];
     // plain rows: absmax over the pieces, codes of each piece into the LDS
     // row (4 or 8 bytes at its entries' offset), their sum
     auto publish_plain = [&]() {
@@ -331,8 +332,12 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
         for (int i = 0; i < kPlainVec; ++i)
             if (tid + i * T < npiece) pmax(praw[i]);
         for (int idx = tid + kPlainVec * T; idx < npiece; idx += T) pmax(__builtin_nontemporal_load(xrow + idx));
-        double ss = 0.0;
-        block_reduce<kDecWaves>(amax, ss, false);
+        // wave maxima with DPP, then across the waves (a max: any order)
+        amax = wave_max_dpp(amax);
+        if (lane == 0) s_qmax[wv] = amax;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kDecWaves; ++i) amax = fmaxf(amax, s_qmax[i]);
         int csum = 0;
         auto put = [&](int idx, const v4u& t) {
             const uint32_t d[4] = {t.x, t.y, t.z, t.w};
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_lds_kernel(
         for (int i = 0; i < kPlainVec; ++i)
             if (tid + i * T < npiece) put(tid + i * T, praw[i]);
         for (int idx = tid + kPlainVec * T; idx < npiece; idx += T) put(idx, __builtin_nontemporal_load(xrow + idx));
-        csum = wave_sum_i(csum);
+        csum = wave_sum_dpp(csum);
         if (lane == 0) s_qsum[wv] = csum;
         if (blockIdx.x == 0 && tid == 0) fr.gamma_out[0] = amax;
         __syncthreads();  // the codes and the partial sums are visible

@@ -92,6 +92,21 @@ __device__ __forceinline__ int wave_sum_dpp(int v) {
            __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
+// Maximum of a non-negative float over the 64 lanes of a wave, with the DPP
+// pattern of wave_sum_dpp (fmaxf: a NaN loses to a number, as in fmaxf
+// chains); the result is wave-uniform.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false)));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // Copy 16 bytes per lane from global memory straight into LDS at
 // lds_wave_base + 16 * lane (global_load_lds_dwordx4; the base is
 // wave-uniform and goes to M0).  The builtin exists only in the device pass;
