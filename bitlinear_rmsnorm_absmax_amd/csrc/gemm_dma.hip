@@ -41,10 +41,11 @@ constexpr int kXcds = 8;
 // L2.  Measured against columns fastest (the tiles of one row range per XCD,
 // each weight column then fetched by several XCDs), bit-identical output:
 // M = 512, K = 8192, N = 28672 142.8 -> 140.1 us; M = 2048, K = 4096,
-// N = 11008 125.6 -> 123.1 us; M = 64 31.6 -> 31.4 us.  Returns m0, sets n0.
+// N = 11008 125.6 -> 123.1 us; M = 64 31.6 -> 31.4 us.  Returns m0, sets n0
+// and the tile's position b in that order.
 __device__ __forceinline__ int tile_origin(int blk, int tiles_n, int tiles_total, int BM, int BN,
-                                           int& n0) {
-    int b = blk;
+                                           int& n0, int& b) {
+    b = blk;
     const int full = (tiles_total / kXcds) * kXcds;
     if (b < full) b = (b % kXcds) * (full / kXcds) + b / kXcds;
     const int tiles_m = tiles_total / tiles_n;
@@ -88,7 +89,7 @@ __attribute__((amdgpu_waves_per_eu(KSP * WM * WN > 8 ? 3 : 2, KSP * WM * WN > 8 
 void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M,
                      int K, const uint32_t* __restrict__ wp, int N, float beta,
                      float* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
-                     int tiles_total) {
+                     int tiles_total, int stagger) {
     using C = DCfg<WM, WN, TM, TN, STAGES>;
     __shared__ __attribute__((aligned(16))) char lds[KSP * STAGES * C::kStageBytes];
 
@@ -101,10 +102,15 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     char* ring = lds + kgrp * STAGES * C::kStageBytes;
     const int l32 = lane & 31, h = lane >> 5;
 
-    int n0;
-    const int m0 = tile_origin(blockIdx.x, tiles_n, tiles_total, C::BM, C::BN, n0);
+    int n0, b;
+    const int m0 = tile_origin(blockIdx.x, tiles_n, tiles_total, C::BM, C::BN, n0, b);
     const int WR = K >> 4;
     const int KT = K / BK / KSP;  // K steps of each group (K % (BK * KSP) == 0)
+    // stagger > 1: the tile starts its K loop at step koff and wraps around,
+    // koff cycling through `stagger` evenly spaced steps over consecutive
+    // tiles, so the workgroups of an XCD do not all copy the same activation
+    // lines at once.  The integer sums do not depend on the order.
+    const int koff = stagger > 1 ? (b % stagger) * KT / stagger : 0;
 
     // per-lane source offsets of this wave's copies at step 0 (32-bit, from
     // the block's first row / column); rows and columns past the matrix are
@@ -129,6 +135,8 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     }
 
     auto issue = [&](int kt, int buf) {
+        kt += koff;
+        if (kt >= KT) kt -= KT;
         char* stage = ring + buf * C::kStageBytes;
         const int8_t* a_step = abase + (int64_t)kt * BK;
         const uint32_t* b_step = bbase + (int64_t)kt * (BK / 16);
@@ -238,7 +246,8 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
 
 template <int WM, int WN, int TM, int TN, int STAGES, int KSP = 1>
 hipError_t launch_dcfg(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
-                       int N, float beta, float* y, int32_t* acc, hipStream_t s) {
+                       int N, float beta, float* y, int32_t* acc, hipStream_t s,
+                       int stagger = 1) {
     using C = DCfg<WM, WN, TM, TN, STAGES>;
     if (K % (BK * KSP) != 0) return hipErrorInvalidValue;
     const int tm = (M + C::BM - 1) / C::BM;
@@ -247,7 +256,7 @@ hipError_t launch_dcfg(const int8_t* xq, const float* gamma, int M, int K, const
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
     gemm_dma_kernel<WM, WN, TM, TN, STAGES, KSP>
         <<<dim3((unsigned)total), dim3(KSP * C::kThreads), 0, s>>>(xq, gamma, M, K, wp, N, beta, y,
-                                                                   acc, tn, (int)total);
+                                                                   acc, tn, (int)total, stagger);
     return hipGetLastError();
 }
 
@@ -291,6 +300,14 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
     // N = 2560: 22.8 -> 22.2 us; with the side-by-side waves 21.9 -> 19.5 us)
     if (tiles64 <= 256 && K >= 36 * BK && K % (3 * BK) == 0)
         return launch_dcfg<1, 4, 2, 1, 3, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+    // K of 32 or more steps a group: four stages, each tile starting at its
+    // own K step (every workgroup otherwise copies the same activation lines
+    // as the others of its XCD at the same time); bit-identical, interleaved
+    // A/B: M = 64, K = 8192, N = 28672 23.7 -> 21.6 us; M = 32 24.2 -> 22.4 us.
+    // At K = 4096 (16 steps a group) neither change gains (M = 64, N = 11008
+    // 11.2 us either way; M = 96 12.8 -> 13.0 us).
+    if (tiles64 <= 256 && K % (2 * BK) == 0 && K >= 64 * BK)
+        return launch_dcfg<1, 4, 2, 1, 4, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s, K / (2 * BK));
     if (tiles64 <= 256 && K % (2 * BK) == 0)
         return launch_dcfg<1, 4, 2, 1, 3, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     // else 128 x 128 tiles (2 x 2 waves of 64 x 64)

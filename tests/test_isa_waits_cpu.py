@@ -11,8 +11,8 @@ GPU) and checks, for every instantiation:
 - ring GEMM (``gemm_dma_kernel``): the steady-state loop -- the one that
   copies, waits, meets at a barrier and multiplies -- holds exactly one
   vector-memory wait, and its count equals the copies the loop issues per
-  step (with three stages, the step just issued stays in flight while the
-  wave waits for the one before it);
+  step times STAGES - 2 (the steps issued after the one the wave multiplies
+  next stay in flight while it waits: one with three stages, two with four);
 - decode with the token quantised in the kernel: the first wait for the
   row's chunks leaves the first batch of weight loads (issued after them)
   in flight;
@@ -94,7 +94,11 @@ def test_ring_gemm_waits_match_its_copies(tmp_path):
         copies = sum(l.startswith("global_load_lds") for l in body)
         others = [l for l in body if re.match(r"(global|buffer|flat)_(load|store|atomic)", l)
                   and not l.startswith("global_load_lds")]
-        assert waits == [copies], f"{name}: waits {waits} in the loop, {copies} copies a step"
+        # gemm_dma_kernel<WM, WN, TM, TN, STAGES, KSP>: STAGES - 2 later steps
+        # stay in flight while the wave waits for the step it multiplies next
+        stages = int(re.search(r"gemm_dma_kernelILi\d+ELi\d+ELi\d+ELi\d+ELi(\d+)ELi", name).group(1))
+        assert waits == [(stages - 2) * copies], (
+            f"{name}: waits {waits} in the loop, {copies} copies a step, {stages} stages")
         assert not others, f"{name}: other vector-memory instructions in the loop: {others[:3]}"
 
 
