@@ -14,13 +14,19 @@ Inputs are seeded synthetic draws (workloads.py), resident in HBM before the
 timed region.  The packed weights rotate through at least 512 MB of copies so
 that consecutive steps cannot be served from the 256 MB Infinity Cache.
 The K timed steps are one replay of a HIP graph holding all K of them, so
-host launch overhead does not pace the GPU.  Per-call durations come from two
-further passes: the back-to-back time (a HIP graph of that call alone, once
-per weight copy, replayed between two events), and per-launch durations (each
-launch between two events on the stream it runs on, all queued behind a spin
-kernel so that they run back to back): mean, median, p10 and p90.  The
-dominant forward call's mean per-launch duration gives the roofline; the
-floors are an empty launch and a read-only pass over the same weight bytes.
+host launch overhead does not pace the GPU.  Per-call durations come from
+three further passes: the in-step durations (the same K steps once more,
+eager, queued behind a spin kernel so that they run back to back, with a
+timing event between consecutive calls on their stream; HIP graphs here do
+not time events recorded inside them), the back-to-back time (a HIP graph of
+that call alone, once per weight copy, replayed between two events), and
+per-launch durations (each launch of the call alone between two events):
+mean, median, p10 and p90.  The dominant forward call's back-to-back time
+gives the roofline (the fraction from its in-step durations rides along: a
+long MFMA kernel runs cooler between the memory-bound calls of a step, while
+every in-step duration also carries an event's cost of a few microseconds);
+the floors are an empty launch and a read-only pass over the same weight
+bytes.
 The headline workload is the large-shape sweep (K=8192, N=28672, M in
 {1, 8, 64, 512}); the other four workloads are measured the same way into the
 line's "configs" record.
@@ -522,10 +528,12 @@ def traffic_write(args):
 
 def _phase_counts(wid, steps, warmup, per_launch, ncopy):
     """Launches of one call in a bench run, in order: the first step, the
-    warmup graph, the timed graph, the back-to-back graph (its first replay,
-    then the timed replays) and the per-launch event pairs."""
+    warmup graph, the timed graph, the in-step event pass (the timed steps
+    again, eager, an event between consecutive calls), the back-to-back graph
+    (its first replay, then the timed replays) and the per-launch event
+    pairs."""
     reps = max(1, math.ceil(steps / ncopy))
-    return [("first", 1), ("warmup", warmup), ("timed steps", steps),
+    return [("first", 1), ("warmup", warmup), ("timed steps", steps), ("in-step events", steps),
             ("back-to-back first", ncopy), ("back-to-back", reps * ncopy),
             ("per-launch events", per_launch)]
 
@@ -569,9 +577,9 @@ def trace_summary(args):
         """the launch pattern of the k calls of workload wid that share one
         kernel and grid, with `count` dispatches in all: (label, dispatches)
         in trace order.  The steps launch the k calls in turn (first step,
-        warmup and timed graphs hold k dispatches a step); then each call
-        has its own back-to-back graph and per-launch pairs, one call after
-        the other."""
+        warmup and timed graphs and the in-step pass hold k dispatches a
+        step); then each call has its own back-to-back graph and per-launch
+        pairs, one call after the other."""
         head = wid == args.workload
         steps = args.steps if head else args.sub_steps
         warm = args.warmup if head else max(2, args.warmup // 4)
@@ -590,9 +598,9 @@ def trace_summary(args):
                 continue
             if k == 1:
                 return pat
-            shared = [(lab if lab != "timed steps" else f"timed steps ({k} calls)", k * c)
-                      for lab, c in pat[:3]]
-            own = [(f"{lab} (call {j + 1} of {k})", c) for j in range(k) for lab, c in pat[3:]]
+            shared = [(lab if lab not in ("timed steps", "in-step events") else f"{lab} ({k} calls)",
+                       k * c) for lab, c in pat[:4]]
+            own = [(f"{lab} (call {j + 1} of {k})", c) for j in range(k) for lab, c in pat[4:]]
             return shared + own
         return None
 
@@ -613,8 +621,9 @@ def trace_summary(args):
             continue
         lines.append(f"| {wname} | `{name}` | {grid} | {wg} | {stats(v)} |")
     lines += ["", "By bench phase (library calls of the measured steps: the timed steps graph, "
-              "the back-to-back graph that bench.py's avg_launch_us comes from, and the "
-              "per-launch event pairs):", "",
+              "the in-step event pass (the same steps, eager, an event between consecutive "
+              "calls), the back-to-back graph of each call alone that bench.py's avg_launch_us "
+              "comes from, and the per-launch event pairs):", "",
               "| workload | kernel | grid | phase | dispatches | mean | median | p10 | p90 |",
               "|---|---|---:|---|---:|---:|---:|---:|---:|"]
     for (wname, name, grid, wg), v in order:
@@ -626,7 +635,7 @@ def trace_summary(args):
             continue
         i = 0
         for lab, c in pat:
-            if lab.startswith(("timed steps", "back-to-back", "per-launch events")) \
+            if lab.startswith(("timed steps", "in-step events", "back-to-back", "per-launch events")) \
                     and not lab.startswith("back-to-back first") and c > 0:
                 lines.append(f"| {wname} | `{name}` | {grid} | {lab} | {stats(v[i:i + c])} |")
             i += c
@@ -1161,6 +1170,43 @@ def launch_stats(torch, s, launch, n):
                 launches=n)
 
 
+def in_step_stats(torch, s, ops, first, count, chunk=20):
+    """Per-call durations inside whole steps: steps first .. first+count-1
+    launched again in step order on stream ``s`` (the timed steps' weight
+    copies and call sequence), with one timing event between consecutive
+    calls, so each call's duration is the time between the events around it.
+    The steps go in chunks of ``chunk``, each queued behind a spin kernel so
+    that the GPU runs its calls back to back, as in the timed graph.  Returns
+    {call: [durations in us]} and the per-step sums of the durations."""
+    durs, sums = {}, []
+    torch.cuda.synchronize()
+    for c0 in range(first, first + count, chunk):
+        marks = []
+
+        def mark(name, *a, **kw):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(s)
+            marks.append((name, ev))
+            return True
+
+        with torch.cuda.stream(s):
+            torch.cuda._sleep(SPIN_CYCLES)
+            for i in range(c0, min(c0 + chunk, first + count)):
+                ops(i, mark)
+                mark(None)  # closes the step's last call; the next step's first mark is not used
+        torch.cuda.synchronize()
+        step = 0.0
+        for (name, e0), (_, e1) in zip(marks, marks[1:]):
+            if name is None:
+                sums.append(step)
+                step = 0.0
+                continue
+            us = e0.elapsed_time(e1) * 1e3
+            durs.setdefault(name, []).append(us)
+            step += us
+    return durs, sums
+
+
 def floors(torch, bl, dev, s, nbytes, n=50):
     """The empty-launch floor and a read-only pass over ``nbytes`` (weight
     copies rotated as the layer's own calls rotate them)."""
@@ -1254,6 +1300,9 @@ def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headl
     del timed
     ms_step = e0.elapsed_time(e1) / steps
     print(f"# timed {steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    # the durations of the calls inside the steps: the timed steps once more,
+    # eager, with an event between consecutive calls
+    ins, ins_sums = in_step_stats(torch, s, ops, warmup, steps)
 
     kern = {}
     for name, per_step in rec.calls.items():
@@ -1274,9 +1323,14 @@ def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headl
         st = launch_stats(torch, s, lambda i, name=name: ops(i, lambda n, *a, **kw: n == name),
                           per_launch)
         st = {k: v / per_step if k.endswith("_us") else v for k, v in st.items()}
-        kern[name] = dict(b2b_us=b2b, per_step=per_step, **st, **rec.info.get(name, {}))
-    print("# per-call GPU time (us, per-launch mean | back-to-back): " +
-          ", ".join(f"{k} {v['avg_us']:.2f} | {v['b2b_us']:.2f}" for k, v in kern.items()),
+        d_in = np.array(ins[name])
+        kern[name] = dict(b2b_us=b2b, per_step=per_step, **st, **rec.info.get(name, {}),
+                          in_step=dict(mean_us=float(d_in.mean()), median_us=float(np.median(d_in)),
+                                       p10_us=float(np.percentile(d_in, 10)),
+                                       p90_us=float(np.percentile(d_in, 90)), launches=len(d_in)))
+    print("# per-call GPU time (us, in-step mean | per-launch mean | back-to-back): " +
+          ", ".join(f"{k} {v['in_step']['mean_us']:.2f} | {v['avg_us']:.2f} | {v['b2b_us']:.2f}"
+                    for k, v in kern.items()),
           file=sys.stderr, flush=True)
 
     fwd = {k: v for k, v in kern.items() if "alg_bytes" in v}
@@ -1290,6 +1344,8 @@ def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headl
     per_call = {}
     for k, v in kern.items():
         e = dict(avg_us=round(v["b2b_us"], 3), per_step=v["per_step"],
+                 in_step_events={a: (round(b, 3) if a.endswith("_us") else b)
+                                 for a, b in v["in_step"].items()},
                  per_launch_events=dict(mean_us=round(v["avg_us"], 3),
                                         median_us=round(v["median_us"], 3),
                                         p10_us=round(v["p10_us"], 3), p90_us=round(v["p90_us"], 3)))
@@ -1309,6 +1365,7 @@ def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headl
         value=round(value, 2), ms_per_step=round(ms_step, 5), steps=steps, warmup=warmup,
         config={"workload": meta["workload"], "M": meta["M"], "K": meta["K"], "N": meta["N"],
                 "weight_copies": meta["weight_copies"],
+                "in_step_sum_us": round(float(np.mean(ins_sums)), 3),
                 "timing": "eager" if args.eager else "hip_graph_of_all_timed_steps",
                 "fusion": "separate calls" if args.unfused else
                 "one-token quant_forward; GLU gate+up stacked",
@@ -1318,25 +1375,31 @@ def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headl
 
 
 def roofline_of(d, traffic, floor):
-    """Roofline of one forward call from its average launch duration (the
-    back-to-back time: HIP events around a graph of that call's launches on
+    """Roofline of one forward call from its average launch duration, the
+    back-to-back time (HIP events around a graph of that call's launches on
     its stream, divided by the launch count): int8 MFMA for 512 tokens and
     more (2*M*N*K ops), HBM bytes otherwise (packed W + x_q + gamma + y, + the
-    fp32/bf16 rows a fused call reads).  The per-launch event statistics ride
-    along; each of those launches also carries the event pair's own cost
-    (about 2 us, see the floor's empty launch)."""
-    us = d["b2b_us"]
+    fp32/bf16 rows a fused call reads).  The same fraction from the in-step
+    event pass (the call between the other calls of the timed steps, where a
+    long MFMA kernel runs cooler and so faster than back to back, but each
+    duration also carries an event's own cost of about 3-4 us) and the
+    per-launch event statistics ride along."""
+    us, ins = d["b2b_us"], d["in_step"]["mean_us"]
     if d["M"] >= 512:
         tops = d["ops"] / (us * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(tops, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
-                    frac=round(tops / INT8_PEAK_TOPS, 4), traffic=traffic)
+                    frac=round(tops / INT8_PEAK_TOPS, 4), traffic=traffic,
+                    frac_in_step=round(d["ops"] / (ins * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4))
     else:
         gbs = d["alg_bytes"] / (us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic)
+                    frac=round(gbs / HBM_PEAK_GBS, 4), traffic=traffic,
+                    frac_in_step=round(d["alg_bytes"] / (ins * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
         if floor:
             roof["frac_of_stream_read"] = round(floor["stream_read_b2b_us"] / us, 4)
     roof.update(call=None, kernel=d["kernel"], avg_launch_us=round(us, 3),
+                in_step_events={a: (round(b, 3) if a.endswith("_us") else b)
+                                for a, b in d["in_step"].items()},
                 per_launch_events=dict(mean_us=round(d["avg_us"], 3),
                                        median_us=round(d["median_us"], 3),
                                        p10_us=round(d["p10_us"], 3), p90_us=round(d["p90_us"], 3),

@@ -187,9 +187,9 @@ def test_mfma_counters_give_utilisation(tmp_path, monkeypatch):
 
 def test_trace_phases_split_calls_that_share_a_kernel(tmp_path, monkeypatch):
     """Two calls of one step run the same kernel at the same grid (one and
-    eight tokens on the decode kernel): their timed-steps dispatches are
-    reported together, and each call's back-to-back graph and per-launch
-    pairs on their own, in bench order."""
+    eight tokens on the decode kernel): their timed-steps and in-step
+    dispatches are reported together, and each call's back-to-back graph and
+    per-launch pairs on their own, in bench order."""
     import argparse
     import math
     bench = load_bench()
@@ -200,7 +200,8 @@ def test_trace_phases_split_calls_that_share_a_kernel(tmp_path, monkeypatch):
     ncopy = max(1, math.ceil(bench.ROTATE_BYTES / (wl.N * wl.K // 4)))
     reps = max(1, math.ceil(steps / ncopy))
     kern = "void bl::decode_lds_kernel<16, 2, 2, false, 1, 2, 1>(int)"
-    seq = [(kern, 5.0)] * 2 + [(kern, 6.0)] * (2 * warmup) + [(kern, 10.0)] * (2 * steps)
+    seq = [(kern, 5.0)] * 2 + [(kern, 6.0)] * (2 * warmup) + [(kern, 10.0)] * (2 * steps) + \
+        [(kern, 12.0)] * (2 * steps)
     for own in (20.0, 30.0):
         seq += [(kern, 99.0)] * ncopy + [(kern, own)] * (reps * ncopy) + \
             [(kern, own + 1.0)] * per_launch
@@ -225,6 +226,8 @@ def test_trace_phases_split_calls_that_share_a_kernel(tmp_path, monkeypatch):
             rows[cols[4].strip()] = cols[5:7]
     assert rows["timed steps (2 calls)"][0].strip() == str(2 * steps)
     assert float(rows["timed steps (2 calls)"][1]) == 10.0
+    assert rows["in-step events (2 calls)"][0].strip() == str(2 * steps)
+    assert float(rows["in-step events (2 calls)"][1]) == 12.0
     assert float(rows["back-to-back (call 1 of 2)"][1]) == 20.0
     assert float(rows["per-launch events (call 1 of 2)"][1]) == 21.0
     assert float(rows["back-to-back (call 2 of 2)"][1]) == 30.0
