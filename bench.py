@@ -278,8 +278,17 @@ def build_plan(args, torch, bl, dev, wid):
                                                 L.copies[c].data_ptr(), D, L.beta, b["y"].data_ptr(),
                                                 None, stream()))
 
+        operands = {}
+        for b in bufs:
+            M = b["M"]
+            if stacked:
+                operands[f"forward_gateup_M{M}"] = (b["q"], layers[0].copies[0], M, D, 2 * Fh)
+            else:
+                operands[f"forward_gate_M{M}"] = (b["q"], layers[0].copies[0], M, D, Fh)
+                operands[f"forward_up_M{M}"] = (b["q"], layers[1].copies[0], M, D, Fh)
+            operands[f"forward_down_M{M}"] = (b["hq"], layers[-1].copies[0], M, Fh, D)
         meta.update(weight_bytes_per_step=sum(L.wbytes for L in layers) * len(wl.ms),
-                    weight_copies=ncopy,
+                    weight_copies=ncopy, operands=operands,
                     ops_per_step=sum(2 * M * (2 * D * Fh + Fh * D) for M in wl.ms))
         return ops, meta, (layers, bufs, gain)
 
@@ -316,7 +325,8 @@ def build_plan(args, torch, bl, dev, wid):
                                             L.beta, b["y"].data_ptr(), None, stream()))
 
     meta.update(weight_bytes_per_step=L.wbytes * len(wl.ms), weight_copies=len(L.copies),
-                ops_per_step=sum(2 * M * N * K for M in wl.ms))
+                ops_per_step=sum(2 * M * N * K for M in wl.ms),
+                operands={f"forward_M{b['M']}": (b["q"], L.copies[0], b["M"], K, N) for b in bufs})
     return ops, meta, (L, bufs)
 
 
@@ -1207,9 +1217,11 @@ def in_step_stats(torch, s, ops, first, count, chunk=20):
     return durs, sums
 
 
-def floors(torch, bl, dev, s, nbytes, n=50):
+def floors(torch, bl, dev, s, nbytes, n=50, mfma=None):
     """The empty-launch floor and a read-only pass over ``nbytes`` (weight
-    copies rotated as the layer's own calls rotate them)."""
+    copies rotated as the layer's own calls rotate them); with ``mfma`` =
+    (x_q, w_packed, M, K, N) of a product, also the register-only MFMA floor
+    of that product (bitlinear_floor_mfma on its own operands)."""
     lib = bl.lib
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     nb = nbytes // 16 * 16
@@ -1248,12 +1260,27 @@ def floors(torch, bl, dev, s, nbytes, n=50):
     r = launch_stats(torch, s, read, n)
     eb, rb = b2b(empty), b2b(read)
     del buf
-    return dict(empty_launch_b2b_us=round(eb, 3), stream_read_b2b_us=round(rb, 3),
-                empty_launch_event_us=round(e["median_us"], 3),
-                stream_read_event_us=round(r["median_us"], 3),
-                stream_read_bytes=nb,
-                stream_read_GBs=round(nb / (rb * 1e-6) / 1e9, 1),
-                stream_read_frac_of_peak=round(nb / (rb * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+    out = dict(empty_launch_b2b_us=round(eb, 3), stream_read_b2b_us=round(rb, 3),
+               empty_launch_event_us=round(e["median_us"], 3),
+               stream_read_event_us=round(r["median_us"], 3),
+               stream_read_bytes=nb,
+               stream_read_GBs=round(nb / (rb * 1e-6) / 1e9, 1),
+               stream_read_frac_of_peak=round(nb / (rb * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+    if mfma is not None and mfma[3] % 128 == 0:
+        q, w, M, K, N = mfma
+
+        def mf(i):
+            if lib.bitlinear_floor_mfma(q.data_ptr(), M, K, w.data_ptr(), N, sink.data_ptr(),
+                                        torch.cuda.current_stream(dev).cuda_stream) != 0:
+                raise RuntimeError(bl.last_error())
+
+        mf(0)
+        mb = b2b(mf)
+        tops = 2 * M * N * K / (mb * 1e-6) / 1e12
+        out.update(mfma_floor_b2b_us=round(mb, 3), mfma_floor_TOPS=round(tops, 1),
+                   mfma_floor_frac_of_peak=round(tops / INT8_PEAK_TOPS, 4),
+                   mfma_floor_shape=[M, K, N])
+    return out
 
 
 def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headline):
@@ -1336,7 +1363,8 @@ def measure_workload(args, torch, bl, dev, wid, steps, warmup, per_launch, headl
     fwd = {k: v for k, v in kern.items() if "alg_bytes" in v}
     dom = max(fwd, key=lambda k: fwd[k]["b2b_us"] * fwd[k]["per_step"])
     d = fwd[dom]
-    floor = floors(torch, bl, dev, s, d["wbytes"], per_launch)
+    floor = floors(torch, bl, dev, s, d["wbytes"], per_launch,
+                   mfma=meta["operands"].get(dom) if d["M"] >= 512 else None)
     traffic = read_traffic(meta["workload"], dom)
     roof = roofline_of(d, traffic, floor)
     if roof["bound"] == "mfma":
@@ -1390,6 +1418,8 @@ def roofline_of(d, traffic, floor):
         roof = dict(bound="mfma", achieved=round(tops, 2), peak=INT8_PEAK_TOPS, unit="TOP/s",
                     frac=round(tops / INT8_PEAK_TOPS, 4), traffic=traffic,
                     frac_in_step=round(d["ops"] / (ins * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4))
+        if floor and "mfma_floor_b2b_us" in floor:
+            roof["frac_of_mfma_floor"] = round(floor["mfma_floor_b2b_us"] / us, 4)
     else:
         gbs = d["alg_bytes"] / (us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(gbs, 2), peak=HBM_PEAK_GBS, unit="GB/s",

@@ -49,6 +49,7 @@ _SIGNATURES = {
     "bitlinear_forward3": [_vp, _vp, _i64, _i64, _vp, _i64, _f32, _vp, _vp, _vp],
     "bitlinear_floor_empty": [_vp],
     "bitlinear_floor_stream_read": [_vp, _i64, _vp, _vp],
+    "bitlinear_floor_mfma": [_vp, _i64, _i64, _vp, _i64, _vp, _vp],
     "bitlinear_last_error": [],
     "bitlinear_abi_version": [],
 }

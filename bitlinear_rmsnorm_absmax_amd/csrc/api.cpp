@@ -527,6 +527,23 @@ bitlinear_status_t bitlinear_floor_stream_read(const void* p, int64_t bytes, uin
     return from_hip(bl::launch_floor_stream_read(p, bytes, sink, stream), fn);
 }
 
+bitlinear_status_t bitlinear_floor_mfma(const int8_t* x_q, int64_t M, int64_t K,
+                                        const uint32_t* w_packed, int64_t N, uint32_t* sink,
+                                        hipStream_t stream) {
+    const char* fn = "bitlinear_floor_mfma";
+    BL_TRY(check_rows(fn, "M", M, kMaxM));
+    BL_TRY(check_k(fn, "K", K));
+    BL_TRY(check_rows(fn, "N", N, kMaxN));
+    if (K % 128 != 0)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld must be a multiple of 128", fn, (long long)K);
+    const bool any = M > 0 && N > 0 && K > 0;
+    BL_TRY(need(fn, "x_q", x_q, any, 16));
+    BL_TRY(need(fn, "w_packed", w_packed, any, 16));
+    BL_TRY(need(fn, "sink", sink, any, 4));
+    if (!any) return ok();
+    return from_hip(bl::launch_floor_mfma(x_q, (int)M, (int)K, w_packed, (int)N, sink, stream), fn);
+}
+
 const char* bitlinear_last_error(void) { return g_err; }
 
 int bitlinear_abi_version(void) { return BITLINEAR_ABI_VERSION; }

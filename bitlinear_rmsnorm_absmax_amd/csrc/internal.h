@@ -165,5 +165,7 @@ hipError_t launch_gemm_mfma(const int8_t* xq, const float* gamma, int M, int K,
 // `bytes` (a multiple of 16) at p (16-byte aligned).
 hipError_t launch_floor_empty(hipStream_t s);
 hipError_t launch_floor_stream_read(const void* p, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_floor_mfma(const int8_t* xq, int M, int K, const uint32_t* wp, int N,
+                             uint32_t* sink, hipStream_t s);
 
 }  // namespace bl

@@ -369,11 +369,12 @@ bitlinear_status_t bitlinear_forward3(const int8_t* x_q, const float* gamma, int
                                       int32_t* acc, hipStream_t stream);
 
 /*
- * Measurement floors.  Not steps of the layer: the two references a roofline
+ * Measurement floors.  Not steps of the layer: the references a roofline
  * report needs next to the layer's kernels on the same device -- the duration
- * of a launch that does nothing, and of a read-only pass over the same number
- * of bytes a product streams (the weight matrix), with the coalesced 16-byte
- * loads the decode kernels issue.
+ * of a launch that does nothing, of a read-only pass over the same number of
+ * bytes a product streams (the weight matrix), with the coalesced 16-byte
+ * loads the decode kernels issue, and of the int8 multiplies of a product
+ * with no memory work around them.
  *
  * bitlinear_floor_empty: launches one empty workgroup on `stream`.
  * bitlinear_floor_stream_read: reads `bytes` (>= 0, a multiple of 16) at p
@@ -384,6 +385,24 @@ bitlinear_status_t bitlinear_forward3(const int8_t* x_q, const float* gamma, int
 bitlinear_status_t bitlinear_floor_empty(hipStream_t stream);
 bitlinear_status_t bitlinear_floor_stream_read(const void* p, int64_t bytes, uint32_t* sink,
                                                hipStream_t stream);
+
+/*
+ * bitlinear_floor_mfma: the v_mfma_i32_32x32x32_i8 work of a product at
+ *   (M, K, N) on the GEMM's 128 x 256 tiles -- one workgroup of four waves per
+ *   tile, two workgroups per CU, 32 MFMAs per wave for each 128 inputs of K --
+ *   with operands loaded once from the product's own inputs (x_q [M][K] int8
+ *   and w_packed [N][K/16] in the layout of bitlinear_pack_weights, both
+ *   device, 16-byte aligned: each wave's activation rows and signed weights of
+ *   the first 128 inputs) and then multiplied from registers only.  Its
+ *   duration is what those multiplies take on this device with that data and
+ *   nothing else to wait for.  M in [0, 65535 * 128], N in [0, 2^30],
+ *   K in [0, 131072] a multiple of 128; M, N or K = 0 launches nothing.
+ *   sink: device uint32 [1], stored only if the xor of all accumulators equals
+ *   0x9E3779B9, so its content carries no meaning.
+ */
+bitlinear_status_t bitlinear_floor_mfma(const int8_t* x_q, int64_t M, int64_t K,
+                                        const uint32_t* w_packed, int64_t N, uint32_t* sink,
+                                        hipStream_t stream);
 
 /* Text of the last non-OK status on this thread ("" if none). */
 const char* bitlinear_last_error(void);

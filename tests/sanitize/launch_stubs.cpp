@@ -53,5 +53,6 @@ hipError_t launch_gemm_mfma(const int8_t*, const float*, int, int, const uint32_
 bool gemm_dma_supports(int, int, int) { return true; }
 hipError_t launch_floor_empty(hipStream_t) { return hipSuccess; }
 hipError_t launch_floor_stream_read(const void*, int64_t, uint32_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_floor_mfma(const int8_t*, int, int, const uint32_t*, int, uint32_t*, hipStream_t) { return hipSuccess; }
 
 }  // namespace bl

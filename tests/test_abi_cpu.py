@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
         "bitlinear_binarize", "bitlinear_pack_weights1", "bitlinear_forward1",
         "bitlinear_quant_act_grouped", "bitlinear_forward_grouped", "bitlinear_ternarize_grouped",
         "bitlinear_forward_grouped_one_launch", "bitlinear_quant_forward_one_launch", "bitlinear_pack_weights3", "bitlinear_forward3",
-        "bitlinear_floor_empty", "bitlinear_floor_stream_read",
+        "bitlinear_floor_empty", "bitlinear_floor_stream_read", "bitlinear_floor_mfma",
         "bitlinear_last_error", "bitlinear_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -497,3 +497,19 @@ def test_floor_stream_read_rejects():
     assert bl.lib.bitlinear_floor_stream_read(FAKE + 8, 32, FAKE, None) == bl.ERR_ALIGN
     assert bl.lib.bitlinear_floor_stream_read(FAKE, 32, None, None) == bl.ERR_NULL
     assert bl.lib.bitlinear_floor_stream_read(None, 0, None, None) == bl.OK
+
+
+def test_floor_mfma_rejects():
+    f = bl.lib.bitlinear_floor_mfma
+    assert f(FAKE, 512, 200, FAKE, 256, FAKE, None) == bl.ERR_SHAPE      # K not a multiple of 128
+    assert f(FAKE, 512, 8192 + 16, FAKE, 256, FAKE, None) == bl.ERR_SHAPE
+    assert f(FAKE, -1, 128, FAKE, 256, FAKE, None) == bl.ERR_SHAPE
+    assert f(FAKE, 512, 128, FAKE, (1 << 30) + 1, FAKE, None) == bl.ERR_SHAPE
+    assert f(FAKE, 512, 262144, FAKE, 256, FAKE, None) == bl.ERR_SHAPE
+    assert f(None, 512, 128, FAKE, 256, FAKE, None) == bl.ERR_NULL
+    assert f(FAKE, 512, 128, None, 256, FAKE, None) == bl.ERR_NULL
+    assert f(FAKE, 512, 128, FAKE, 256, None, None) == bl.ERR_NULL
+    assert f(FAKE + 8, 512, 128, FAKE, 256, FAKE, None) == bl.ERR_ALIGN
+    assert f(FAKE, 512, 128, FAKE + 4, 256, FAKE, None) == bl.ERR_ALIGN
+    assert f(None, 0, 128, None, 256, None, None) == bl.OK                # nothing to launch
+    assert f(None, 512, 0, None, 256, None, None) == bl.OK

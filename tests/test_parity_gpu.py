@@ -1328,3 +1328,19 @@ def test_graph_replays_widened_paths(dev):
         for outs, r in zip(got, ref):
             for t, rt in zip(outs, r):
                 np.testing.assert_array_equal(host(t).view(np.uint8), rt.view(np.uint8))
+
+
+# The register-only MFMA floor (a measurement aid, not a step of the layer)
+# runs on ragged shapes and the sweep's GEMM shape without a fault; its sink
+# holds either the caller's value or the one constant it may store.
+@pytest.mark.parametrize("M,K,N", [(1, 128, 1), (300, 256, 700), (512, 8192, 28672)])
+def test_floor_mfma_runs(dev, M, K, N):
+    rng = np.random.default_rng(M + K + N)
+    q = to_dev(rng.integers(-127, 128, (M, K)).astype(np.int8), dev)
+    w = gpu_pack(workloads.ternary(rng, N, K, workloads.TERNARY_HALF_ZERO), dev)
+    sink = torch.full((1,), 0x1234567, dtype=torch.int32, device=dev)
+    st = bl.lib.bitlinear_floor_mfma(q.data_ptr(), M, K, w.data_ptr(), N, sink.data_ptr(),
+                                     torch.cuda.current_stream(dev).cuda_stream)
+    assert st == bl.OK, bl.last_error()
+    torch.cuda.synchronize()
+    assert int(sink.item()) & 0xFFFFFFFF in (0x1234567, 0x9E3779B9)
