@@ -41,11 +41,10 @@ constexpr int kXcds = 8;
 // L2.  Measured against columns fastest (the tiles of one row range per XCD,
 // each weight column then fetched by several XCDs), bit-identical output:
 // M = 512, K = 8192, N = 28672 142.8 -> 140.1 us; M = 2048, K = 4096,
-// N = 11008 125.6 -> 123.1 us; M = 64 31.6 -> 31.4 us.  Returns m0, sets n0
-// and the tile's position b in that order.
+// N = 11008 125.6 -> 123.1 us; M = 64 31.6 -> 31.4 us.  Returns m0, sets n0.
 __device__ __forceinline__ int tile_origin(int blk, int tiles_n, int tiles_total, int BM, int BN,
-                                           int& n0, int& b) {
-    b = blk;
+                                           int& n0) {
+    int b = blk;
     const int full = (tiles_total / kXcds) * kXcds;
     if (b < full) b = (b % kXcds) * (full / kXcds) + b / kXcds;
     const int tiles_m = tiles_total / tiles_n;
@@ -89,7 +88,7 @@ __attribute__((amdgpu_waves_per_eu(KSP * WM * WN > 8 ? 3 : 2, KSP * WM * WN > 8 
 void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M,
                      int K, const uint32_t* __restrict__ wp, int N, float beta,
                      float* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
-                     int tiles_total, int stagger) {
+                     int tiles_total) {
     using C = DCfg<WM, WN, TM, TN, STAGES>;
     __shared__ __attribute__((aligned(16))) char lds[KSP * STAGES * C::kStageBytes];
 
@@ -102,15 +101,10 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     char* ring = lds + kgrp * STAGES * C::kStageBytes;
     const int l32 = lane & 31, h = lane >> 5;
 
-    int n0, b;
-    const int m0 = tile_origin(blockIdx.x, tiles_n, tiles_total, C::BM, C::BN, n0, b);
+    int n0;
+    const int m0 = tile_origin(blockIdx.x, tiles_n, tiles_total, C::BM, C::BN, n0);
     const int WR = K >> 4;
     const int KT = K / BK / KSP;  // K steps of each group (K % (BK * KSP) == 0)
-    // stagger > 1: the tile starts its K loop at step koff and wraps around,
-    // koff cycling through `stagger` evenly spaced steps over consecutive
-    // tiles, so the workgroups of an XCD do not all copy the same activation
-    // lines at once.  The integer sums do not depend on the order.
-    const int koff = stagger > 1 ? (b % stagger) * KT / stagger : 0;
 
     // per-lane source offsets of this wave's copies at step 0 (32-bit, from
     // the block's first row / column); rows and columns past the matrix are
@@ -135,8 +129,6 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     }
 
     auto issue = [&](int kt, int buf) {
-        kt += koff;
-        if (kt >= KT) kt -= KT;
         char* stage = ring + buf * C::kStageBytes;
         const int8_t* a_step = abase + (int64_t)kt * BK;
         const uint32_t* b_step = bbase + (int64_t)kt * (BK / 16);
@@ -244,10 +236,156 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
 }
 
 
+// 64-row tiles with two K groups whose steps interleave (group g takes the
+// 128-input steps 2p + g) and share one weight copy.  A stage holds both
+// groups' activation steps (64 rows x 128 bytes each, laid out as above) and
+// both steps of the tile's 128 weight columns as 64 contiguous bytes a column,
+// so one weight copy instruction reads 16 columns x 64 bytes where the ring
+// above reads 32 columns x 32 bytes.  The 64 bytes of column c hold four
+// 16-byte pieces j = 2g + h (group g's packed words 4h .. 4h+3), piece j at
+// position j ^ ((c >> 2) & 3), so the 16 columns a ds_read_b128 phase serves
+// fall on different banks.  Eight waves (two groups of four side by side, 64
+// rows x 32 columns each) issue three copies a stage each: two activation
+// copies and one weight copy.  Measured against the two-group ring with weights
+// streamed from HBM (copies rotated over 512 MB), bit-identical: M = 64,
+// K = 8192, N = 28672 26.8 -> 24.5 us; M = 32 26.8 -> 24.5 us; M = 64,
+// K = 4096, N = 11008 12.9 -> 11.8 us; M = 96 14.4 -> 13.4 us.
+template <int STAGES>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_pair_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
+                      const uint32_t* __restrict__ wp, int N, float beta, float* __restrict__ y,
+                      int32_t* __restrict__ acc_out, int tiles_n, int tiles_total) {
+    constexpr int BM = 64, BN = 128, TM = 2, TN = 1;
+    constexpr int kABytes = BM * BK;           // one group's activation step
+    constexpr int kBBytes = BN * 64;           // both groups' weight steps
+    constexpr int kStageBytes = 2 * kABytes + kBBytes;
+    constexpr int kPerStep = 3;                // copies of a wave per stage
+    __shared__ __attribute__((aligned(16))) char lds[STAGES * kStageBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);  // 0..7
+    const int kgrp = wv / 4, wn = wv % 4;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    int n0;
+    const int m0 = tile_origin(blockIdx.x, tiles_n, tiles_total, BM, BN, n0);
+    const int WR = K >> 4;
+    const int KP = K / (2 * BK);  // step pairs (K % 256 == 0)
+
+    // activation copies q = 2 wv, 2 wv + 1 of 16: group q / 8, rows 8 (q % 8)
+    // .. +7 of that group's step; weight copy wv: columns 16 wv .. +15.  Rows
+    // and columns past the matrix are clamped (their products are never stored).
+    uint32_t aoff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = 2 * wv + i;
+        const int row = 8 * (q % 8) + lane / 8;
+        const int lchunk = (lane % 8) ^ swz(row);
+        aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + (uint32_t)((q / 8) * BK) +
+                  16u * lchunk;
+    }
+    uint32_t boff;
+    {
+        const int c = 16 * wv + lane / 4;
+        const int j = (lane % 4) ^ ((c >> 2) & 3);
+        boff = (uint32_t)(min(n0 + c, N - 1) - n0) * (uint32_t)WR + 4u * j;
+    }
+    const int8_t* abase = xq + (int64_t)m0 * K;
+    const uint32_t* bbase = wp + (int64_t)n0 * WR;
+
+    auto issue = [&](int kp, int buf) {
+        char* stage = lds + buf * kStageBytes;
+        const int8_t* a_step = abase + (int64_t)kp * (2 * BK);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = 2 * wv + i;
+            copy16_to_lds(a_step + aoff[i], stage + (q / 8) * kABytes + 1024 * (q % 8));
+        }
+        copy16_to_lds(bbase + (int64_t)kp * 16 + boff, stage + 2 * kABytes + 1024 * wv);
+    };
+
+    v16i acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) acc[i][0] = v16i{};
+
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p) issue(min(p, KP - 1), p);
+
+    for (int kp = 0; kp < KP; ++kp) {
+        // this wave's copies of pair kp are done (later pairs may be in flight)
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((STAGES - 2) * kPerStep, 0));
+        __builtin_amdgcn_s_barrier();
+        issue(min(kp + STAGES - 1, KP - 1), (kp + STAGES - 1) % STAGES);
+
+        const char* stage = lds + (kp % STAGES) * kStageBytes;
+        const v4i* As = reinterpret_cast<const v4i*>(stage + kgrp * kABytes);
+        const v4u* Bs = reinterpret_cast<const v4u*>(stage + 2 * kABytes);
+        const int col = wn * 32 + l32;
+        const v4u wq = Bs[col * 4 + ((2 * kgrp + h) ^ ((col >> 2) & 3))];
+        v4i af[4][TM];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int r = 32 * i + l32;
+                af[kk][i] = As[r * 8 + ((4 * h + kk) ^ swz(r))];
+            }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const v4i bf = unpack_signed(wq[kk]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                acc[i][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kk][i], bf, acc[i][0], 0, 0, 0);
+        }
+    }
+    // every copy (including the re-reads past the end) has landed before the
+    // LDS is reused below or released
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    __syncthreads();
+
+    // group 1's accumulators go through LDS (lane-major) to group 0, whose
+    // waves own the epilogue
+    constexpr int kAccInts = 4 * TM * TN * 16 * kWave;
+    int* red = reinterpret_cast<int*>(lds);
+    int* S = red + kAccInts;  // [BM], all 0 (no offset)
+    float* Ssc = reinterpret_cast<float*>(S + BM);
+    static_assert((kAccInts + 2 * BM) * 4 <= STAGES * kStageBytes, "the exchange fits the ring");
+    if (kgrp == 1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) red[((wn * TM + i) * 16 + v) * kWave + lane] = acc[i][0][v];
+    }
+    __syncthreads();
+    if (kgrp == 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][0][v] += red[((wn * TM + i) * 16 + v) * kWave + lane];
+    }
+    __syncthreads();
+    epilogue_tables(nullptr, 0, BM, m0, M, gamma, beta, S, Ssc, tid, 512);
+    __syncthreads();
+    if (kgrp == 0) store_tiles<TM, TN>(acc, S, Ssc, 0, wn * 32, m0, n0, M, N, y, acc_out, lane);
+}
+
+template <int STAGES>
+hipError_t launch_pair(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
+                       int N, float beta, float* y, int32_t* acc, hipStream_t s) {
+    if (K % (2 * BK) != 0) return hipErrorInvalidValue;
+    const int64_t total = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
+    if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int tn = (N + 127) / 128;
+    gemm_pair_kernel<STAGES><<<dim3((unsigned)total), dim3(512), 0, s>>>(xq, gamma, M, K, wp, N, beta, y,
+                                                                         acc, tn, (int)total);
+    return hipGetLastError();
+}
+
+
 template <int WM, int WN, int TM, int TN, int STAGES, int KSP = 1>
 hipError_t launch_dcfg(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
-                       int N, float beta, float* y, int32_t* acc, hipStream_t s,
-                       int stagger = 1) {
+                       int N, float beta, float* y, int32_t* acc, hipStream_t s) {
     using C = DCfg<WM, WN, TM, TN, STAGES>;
     if (K % (BK * KSP) != 0) return hipErrorInvalidValue;
     const int tm = (M + C::BM - 1) / C::BM;
@@ -256,7 +394,7 @@ hipError_t launch_dcfg(const int8_t* xq, const float* gamma, int M, int K, const
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
     gemm_dma_kernel<WM, WN, TM, TN, STAGES, KSP>
         <<<dim3((unsigned)total), dim3(KSP * C::kThreads), 0, s>>>(xq, gamma, M, K, wp, N, beta, y,
-                                                                   acc, tn, (int)total, stagger);
+                                                                   acc, tn, (int)total);
     return hipGetLastError();
 }
 
@@ -300,16 +438,12 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
     // N = 2560: 22.8 -> 22.2 us; with the side-by-side waves 21.9 -> 19.5 us)
     if (tiles64 <= 256 && K >= 36 * BK && K % (3 * BK) == 0)
         return launch_dcfg<1, 4, 2, 1, 3, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    // K of 32 or more steps a group: four stages, each tile starting at its
-    // own K step (every workgroup otherwise copies the same activation lines
-    // as the others of its XCD at the same time); bit-identical, interleaved
-    // A/B: M = 64, K = 8192, N = 28672 23.7 -> 21.6 us; M = 32 24.2 -> 22.4 us.
-    // At K = 4096 (16 steps a group) neither change gains (M = 64, N = 11008
-    // 11.2 us either way; M = 96 12.8 -> 13.0 us).
-    if (tiles64 <= 256 && K % (2 * BK) == 0 && K >= 64 * BK)
-        return launch_dcfg<1, 4, 2, 1, 4, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s, K / (2 * BK));
+    // otherwise the two groups on interleaved steps sharing each weight copy
+    // (gemm_pair_kernel); four stages from 32 step pairs on (M = 64, K = 8192,
+    // N = 28672 24.9 -> 24.5 us; at K = 4096 three: 11.8 against 12.0 us)
     if (tiles64 <= 256 && K % (2 * BK) == 0)
-        return launch_dcfg<1, 4, 2, 1, 3, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return K >= 64 * BK ? launch_pair<4>(xq, gamma, M, K, wp, N, beta, y, acc, s)
+                            : launch_pair<3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     // else 128 x 128 tiles (2 x 2 waves of 64 x 64)
     return launch_dcfg<2, 2, 2, 2, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }

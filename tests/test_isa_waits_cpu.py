@@ -8,7 +8,8 @@ the compiler emits exactly the expected loads, in program order, and adds no
 wait of its own.  This test compiles the two sources (hipcc, host only, no
 GPU) and checks, for every instantiation:
 
-- ring GEMM (``gemm_dma_kernel``): the steady-state loop -- the one that
+- ring GEMM (``gemm_dma_kernel`` and its two-group form ``gemm_pair_kernel``):
+  the steady-state loop -- the one that
   copies, waits, meets at a barrier and multiplies -- holds exactly one
   vector-memory wait, and its count equals the copies the loop issues per
   step times STAGES - 2 (the steps issued after the one the wave multiplies
@@ -81,8 +82,12 @@ def _loops(lines):
 
 
 def test_ring_gemm_waits_match_its_copies(tmp_path):
-    funcs = _functions(_asm("gemm_dma.hip", tmp_path), "gemm_dma_kernel")
+    asm = _asm("gemm_dma.hip", tmp_path)
+    funcs = _functions(asm, "gemm_dma_kernel")
     assert funcs, "no gemm_dma_kernel instantiation found"
+    pair = _functions(asm, "gemm_pair_kernel")
+    assert pair, "no gemm_pair_kernel instantiation found"
+    funcs.update(pair)
     for name, lines in funcs.items():
         steady = [(lab, body) for lab, body in _loops(lines)
                   if any(l.startswith("global_load_lds") for l in body)
@@ -94,9 +99,12 @@ def test_ring_gemm_waits_match_its_copies(tmp_path):
         copies = sum(l.startswith("global_load_lds") for l in body)
         others = [l for l in body if re.match(r"(global|buffer|flat)_(load|store|atomic)", l)
                   and not l.startswith("global_load_lds")]
-        # gemm_dma_kernel<WM, WN, TM, TN, STAGES, KSP>: STAGES - 2 later steps
-        # stay in flight while the wave waits for the step it multiplies next
-        stages = int(re.search(r"gemm_dma_kernelILi\d+ELi\d+ELi\d+ELi\d+ELi(\d+)ELi", name).group(1))
+        # gemm_dma_kernel<WM, WN, TM, TN, STAGES, KSP> / gemm_pair_kernel<STAGES>:
+        # STAGES - 2 later steps stay in flight while the wave waits for the
+        # step it multiplies next
+        m = re.search(r"gemm_dma_kernelILi\d+ELi\d+ELi\d+ELi\d+ELi(\d+)ELi", name) or \
+            re.search(r"gemm_pair_kernelILi(\d+)E", name)
+        stages = int(m.group(1))
         assert waits == [(stages - 2) * copies], (
             f"{name}: waits {waits} in the loop, {copies} copies a step, {stages} stages")
         assert not others, f"{name}: other vector-memory instructions in the loop: {others[:3]}"

@@ -304,11 +304,11 @@ WIDE_GEMM_CASES = [(257, 22053, 128), (256, 32769, 256), (300, 22016, 384), (384
 
 
 # At most 256 tiles of 64 x 128 and K % 256 == 0: 64-row tiles with two K
-# groups per workgroup (ragged M, a last row tile with one row, ragged N);
-# K >= 4608 in a multiple of 3 steps of 128: three K groups; otherwise
-# K >= 8192: four ring stages and every tile starting at its own K step
-# (32, 34 and 40 steps a group; tile counts of 24, 32 and 18, the last not a
-# multiple of the eight XCDs).
+# groups per workgroup on interleaved steps (ragged M, a last row tile with
+# one row, ragged N; one step pair at K = 256; three ring stages, and four from
+# K = 8192: 32, 34 and 40 step pairs over 24, 32 and 18 tiles, the last not a
+# multiple of the eight XCDs); K >= 4608 in a multiple of 3 steps of 128:
+# three K groups.
 SMALL_TILE_GEMM_CASES = [(64, 3000, 2560), (65, 1000, 768), (96, 2000, 1536), (300, 700, 1536),
                          (512, 257, 256), (65, 300, 9216), (100, 1000, 4608), (300, 1536, 6912),
                          (37, 3000, 8192), (100, 2000, 8704), (70, 1100, 10240)]
