@@ -236,30 +236,35 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
 }
 
 
-// 64-row tiles with two K groups whose steps interleave (group g takes the
-// 128-input steps 2p + g) and share one weight copy.  A stage holds both
-// groups' activation steps (64 rows x 128 bytes each, laid out as above) and
-// both steps of the tile's 128 weight columns as 64 contiguous bytes a column,
-// so one weight copy instruction reads 16 columns x 64 bytes where the ring
-// above reads 32 columns x 32 bytes.  The 64 bytes of column c hold four
-// 16-byte pieces j = 2g + h (group g's packed words 4h .. 4h+3), piece j at
-// position j ^ ((c >> 2) & 3), so the 16 columns a ds_read_b128 phase serves
-// fall on different banks.  Eight waves (two groups of four side by side, 64
-// rows x 32 columns each) issue three copies a stage each: two activation
-// copies and one weight copy.  Measured against the two-group ring with weights
-// streamed from HBM (copies rotated over 512 MB), bit-identical: M = 64,
-// K = 8192, N = 28672 26.8 -> 24.5 us; M = 32 26.8 -> 24.5 us; M = 64,
-// K = 4096, N = 11008 12.9 -> 11.8 us; M = 96 14.4 -> 13.4 us.
-template <int STAGES>
+// 64-row tiles with two K groups that share each weight copy.  A stage holds
+// 2P consecutive 128-input steps: group g multiplies steps P g .. P g + P-1 of
+// it.  The stage holds both groups' activation steps (64 rows x 128 bytes
+// each, laid out as above) and all 2P steps of the tile's 128 weight columns
+// as 64 P contiguous bytes a column, so one weight copy instruction reads
+// 16 / P columns x 64 P bytes where the ring above reads 32 columns x 32 bytes.
+// The 4P 16-byte pieces of column c (piece j = 2 s + h: step s of the stage,
+// packed words 4h .. 4h+3) sit at positions j ^ ((c >> (3 - P)) & (4P - 1)),
+// so the 16 neighbouring columns of a ds_read_b128 phase fall on different
+// banks.  Eight waves (two groups of four side by side, 64 rows x 32 columns
+// each) issue 3P copies a stage each: 2P activation copies and P weight
+// copies.  P = 1, measured against the two-group ring (one step a stage,
+// 32 columns x 32 bytes a weight copy) with weights streamed from HBM (copies
+// rotated over 512 MB), bit-identical: M = 64, K = 8192, N = 28672 26.8 ->
+// 24.5 us; M = 32 26.8 -> 24.5 us; M = 64, K = 4096, N = 11008 12.9 ->
+// 11.8 us; M = 96 14.4 -> 13.4 us.
+template <int STAGES, int P>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_pair_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M, int K,
                       const uint32_t* __restrict__ wp, int N, float beta, float* __restrict__ y,
                       int32_t* __restrict__ acc_out, int tiles_n, int tiles_total) {
+    static_assert(P == 1 || P == 2, "one or two steps a group per stage");
     constexpr int BM = 64, BN = 128, TM = 2, TN = 1;
-    constexpr int kABytes = BM * BK;           // one group's activation step
-    constexpr int kBBytes = BN * 64;           // both groups' weight steps
-    constexpr int kStageBytes = 2 * kABytes + kBBytes;
-    constexpr int kPerStep = 3;                // copies of a wave per stage
+    constexpr int kABytes = BM * BK;             // one activation step
+    constexpr int kColBytes = 64 * P;            // weight bytes of a column per stage
+    constexpr int kStageBytes = 2 * P * kABytes + BN * kColBytes;
+    constexpr int kPerStep = 3 * P;              // copies of a wave per stage
+    constexpr int kColsPerCopy = 16 / P;
+    constexpr int kSwzShift = 3 - P, kSwzMask = 4 * P - 1;
     __shared__ __attribute__((aligned(16))) char lds[STAGES * kStageBytes];
 
     const int tid = threadIdx.x;
@@ -271,38 +276,43 @@ void gemm_pair_kernel(const int8_t* __restrict__ xq, const float* __restrict__ g
     int n0;
     const int m0 = tile_origin(blockIdx.x, tiles_n, tiles_total, BM, BN, n0);
     const int WR = K >> 4;
-    const int KP = K / (2 * BK);  // step pairs (K % 256 == 0)
+    const int KP = K / (2 * P * BK);  // stages of K (K % (256 P) == 0)
 
-    // activation copies q = 2 wv, 2 wv + 1 of 16: group q / 8, rows 8 (q % 8)
-    // .. +7 of that group's step; weight copy wv: columns 16 wv .. +15.  Rows
-    // and columns past the matrix are clamped (their products are never stored).
-    uint32_t aoff[2];
+    // activation copies q = 2P wv .. 2P wv + 2P-1 of 16P: step q / 8 of the
+    // stage, rows 8 (q % 8) .. +7; weight copies P wv .. P wv + P-1 of 8P:
+    // columns (16 / P) q .. +(16 / P - 1).  Rows and columns past the matrix
+    // are clamped (their products are never stored).
+    uint32_t aoff[2 * P];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = 2 * wv + i;
+    for (int i = 0; i < 2 * P; ++i) {
+        const int q = 2 * P * wv + i;
         const int row = 8 * (q % 8) + lane / 8;
         const int lchunk = (lane % 8) ^ swz(row);
         aoff[i] = (uint32_t)(min(m0 + row, M - 1) - m0) * (uint32_t)K + (uint32_t)((q / 8) * BK) +
                   16u * lchunk;
     }
-    uint32_t boff;
-    {
-        const int c = 16 * wv + lane / 4;
-        const int j = (lane % 4) ^ ((c >> 2) & 3);
-        boff = (uint32_t)(min(n0 + c, N - 1) - n0) * (uint32_t)WR + 4u * j;
+    uint32_t boff[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+        const int c = kColsPerCopy * (P * wv + i) + lane / (4 * P);
+        const int j = (lane % (4 * P)) ^ ((c >> kSwzShift) & kSwzMask);
+        boff[i] = (uint32_t)(min(n0 + c, N - 1) - n0) * (uint32_t)WR + 4u * j;
     }
     const int8_t* abase = xq + (int64_t)m0 * K;
     const uint32_t* bbase = wp + (int64_t)n0 * WR;
 
     auto issue = [&](int kp, int buf) {
         char* stage = lds + buf * kStageBytes;
-        const int8_t* a_step = abase + (int64_t)kp * (2 * BK);
+        const int8_t* a_step = abase + (int64_t)kp * (2 * P * BK);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = 2 * wv + i;
+        for (int i = 0; i < 2 * P; ++i) {
+            const int q = 2 * P * wv + i;
             copy16_to_lds(a_step + aoff[i], stage + (q / 8) * kABytes + 1024 * (q % 8));
         }
-        copy16_to_lds(bbase + (int64_t)kp * 16 + boff, stage + 2 * kABytes + 1024 * wv);
+        const uint32_t* b_step = bbase + (int64_t)kp * (16 * P);
+#pragma unroll
+        for (int i = 0; i < P; ++i)
+            copy16_to_lds(b_step + boff[i], stage + 2 * P * kABytes + 1024 * (P * wv + i));
     };
 
     v16i acc[TM][TN];
@@ -313,30 +323,34 @@ void gemm_pair_kernel(const int8_t* __restrict__ xq, const float* __restrict__ g
     for (int p = 0; p < STAGES - 1; ++p) issue(min(p, KP - 1), p);
 
     for (int kp = 0; kp < KP; ++kp) {
-        // this wave's copies of pair kp are done (later pairs may be in flight)
+        // this wave's copies of stage kp are done (later stages may be in flight)
         __builtin_amdgcn_s_waitcnt(waitcnt_imm((STAGES - 2) * kPerStep, 0));
         __builtin_amdgcn_s_barrier();
         issue(min(kp + STAGES - 1, KP - 1), (kp + STAGES - 1) % STAGES);
 
         const char* stage = lds + (kp % STAGES) * kStageBytes;
-        const v4i* As = reinterpret_cast<const v4i*>(stage + kgrp * kABytes);
-        const v4u* Bs = reinterpret_cast<const v4u*>(stage + 2 * kABytes);
+        const v4u* Bs = reinterpret_cast<const v4u*>(stage + 2 * P * kABytes);
         const int col = wn * 32 + l32;
-        const v4u wq = Bs[col * 4 + ((2 * kgrp + h) ^ ((col >> 2) & 3))];
-        v4i af[4][TM];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int u = 0; u < P; ++u) {
+            const int st = P * kgrp + u;  // step of the stage
+            const v4i* As = reinterpret_cast<const v4i*>(stage + st * kABytes);
+            const v4u wq = Bs[col * (4 * P) + ((2 * st + h) ^ ((col >> kSwzShift) & kSwzMask))];
+            v4i af[4][TM];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = 32 * i + l32;
-                af[kk][i] = As[r * 8 + ((4 * h + kk) ^ swz(r))];
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int r = 32 * i + l32;
+                    af[kk][i] = As[r * 8 + ((4 * h + kk) ^ swz(r))];
+                }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const v4i bf = unpack_signed(wq[kk]);
+#pragma unroll
+                for (int i = 0; i < TM; ++i)
+                    acc[i][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kk][i], bf, acc[i][0], 0, 0, 0);
             }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const v4i bf = unpack_signed(wq[kk]);
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-                acc[i][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[kk][i], bf, acc[i][0], 0, 0, 0);
         }
     }
     // every copy (including the re-reads past the end) has landed before the
@@ -370,15 +384,15 @@ void gemm_pair_kernel(const int8_t* __restrict__ xq, const float* __restrict__ g
     if (kgrp == 0) store_tiles<TM, TN>(acc, S, Ssc, 0, wn * 32, m0, n0, M, N, y, acc_out, lane);
 }
 
-template <int STAGES>
+template <int STAGES, int P>
 hipError_t launch_pair(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
                        int N, float beta, float* y, int32_t* acc, hipStream_t s) {
-    if (K % (2 * BK) != 0) return hipErrorInvalidValue;
+    if (K % (2 * P * BK) != 0) return hipErrorInvalidValue;
     const int64_t total = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
     const int tn = (N + 127) / 128;
-    gemm_pair_kernel<STAGES><<<dim3((unsigned)total), dim3(512), 0, s>>>(xq, gamma, M, K, wp, N, beta, y,
-                                                                         acc, tn, (int)total);
+    gemm_pair_kernel<STAGES, P><<<dim3((unsigned)total), dim3(512), 0, s>>>(xq, gamma, M, K, wp, N, beta,
+                                                                            y, acc, tn, (int)total);
     return hipGetLastError();
 }
 
@@ -438,12 +452,21 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
     // N = 2560: 22.8 -> 22.2 us; with the side-by-side waves 21.9 -> 19.5 us)
     if (tiles64 <= 256 && K >= 36 * BK && K % (3 * BK) == 0)
         return launch_dcfg<1, 4, 2, 1, 3, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    // otherwise the two groups on interleaved steps sharing each weight copy
-    // (gemm_pair_kernel); four stages from 32 step pairs on (M = 64, K = 8192,
-    // N = 28672 24.9 -> 24.5 us; at K = 4096 three: 11.8 against 12.0 us)
+    // otherwise the two groups sharing each weight copy (gemm_pair_kernel):
+    // with K % 512 == 0 two steps a group per stage (8 columns x 128 bytes a
+    // copy) in two 48 KB stages, against one step in three or four stages,
+    // weights streamed from HBM, bit-identical: M = 64, K = 8192, N = 28672
+    // 22.9-24.4 -> 22.6-22.8 us; M = 32 23.0-24.6 -> 22.5-22.7 us; M = 96,
+    // K = 4096, N = 11008 13.4-13.9 -> 12.9-13.1 us; M = 512, K = 2560,
+    // N = 2560 9.0-9.3 -> 8.8 us; M = 200, K = 8192, N = 4096 19.2-19.7 ->
+    // 18.9-19.1 us (M = 64, K = 4096 11.8-12.0 -> 12.1-12.2 us).  One step a
+    // group: four stages from 32 step pairs on (M = 64, K = 8192 24.9 ->
+    // 24.5 us), three below.
+    if (tiles64 <= 256 && K % (4 * BK) == 0)
+        return launch_pair<2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     if (tiles64 <= 256 && K % (2 * BK) == 0)
-        return K >= 64 * BK ? launch_pair<4>(xq, gamma, M, K, wp, N, beta, y, acc, s)
-                            : launch_pair<3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return K >= 64 * BK ? launch_pair<4, 1>(xq, gamma, M, K, wp, N, beta, y, acc, s)
+                            : launch_pair<3, 1>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     // else 128 x 128 tiles (2 x 2 waves of 64 x 64)
     return launch_dcfg<2, 2, 2, 2, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }
