@@ -1290,7 +1290,8 @@ def test_graph_replays_match_eager(dev):
 def test_graph_replays_widened_paths(dev):
     """The widened products captured in one HIP graph -- base-3 on MFMA (16
     tokens), 1-bit on the LDS decode kernel, the grouped decode (G = 4), the
-    vector GEMV with K split over two waves, the GEMM with three K groups:
+    vector GEMV with K split over two waves, the GEMM with three K groups and
+    with two groups of one step a stage sharing each weight copy:
     each of three replays (outputs cleared and synchronised in between)
     reproduces the eager outputs bit for bit."""
     rng = workloads.rng_for(1310)
@@ -1306,13 +1307,16 @@ def test_graph_replays_widened_paths(dev):
     q1, g1 = bl.quant_act(to_dev(rng.standard_normal((1, 6912)).astype(np.float32), dev))
     w_k3 = gpu_pack(workloads.ternary(rng, 1000, 4608, workloads.TERNARY_UNIFORM), dev)
     qm, gm = bl.quant_act(to_dev(rng.standard_normal((100, 4608)).astype(np.float32), dev))
+    w_p1 = gpu_pack(workloads.ternary(rng, 700, 768, workloads.TERNARY_UNIFORM), dev)
+    qp, gp = bl.quant_act(to_dev(rng.standard_normal((64, 768)).astype(np.float32), dev))
 
     def run():
         return [bl.forward3(q16, g16, p3, 0.02, want_acc=True),
                 bl.forward1(q16, g16, p1, 0.02, want_acc=True),
                 bl.forward_grouped(qg, gg, pg, beta_g),
                 bl.forward(q1, g1, w_long, 0.02, want_acc=True),
-                bl.forward(qm, gm, w_k3, 0.02, path=bl.PATH_GEMM, want_acc=True)]
+                bl.forward(qm, gm, w_k3, 0.02, path=bl.PATH_GEMM, want_acc=True),
+                bl.forward(qp, gp, w_p1, 0.02, path=bl.PATH_GEMM, want_acc=True)]
 
     ref = [[host(t) for t in outs] for outs in run()]
     s = torch.cuda.Stream(device=dev)
