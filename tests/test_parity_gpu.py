@@ -307,13 +307,14 @@ WIDE_GEMM_CASES = [(257, 22053, 128), (256, 32769, 256), (300, 22016, 384), (384
 # groups per workgroup sharing each weight copy (ragged M, a last row tile
 # with one row, ragged N); K % 512 == 0: two steps a group per stage (one
 # stage at K = 512; 16, 17 and 20 stages over 24, 32 and 18 tiles, the last
-# not a multiple of the eight XCDs); else one step a group (one stage at
+# not a multiple of the eight XCDs; 17 tokens over 129 column tiles; two full
+# row tiles over 7 stages); else one step a group (one stage at
 # K = 256, three ring stages at K = 768, four from K = 8192: 35 stages at
 # K = 8960); K >= 4608 in a multiple of 3 steps of 128: three K groups.
 SMALL_TILE_GEMM_CASES = [(64, 3000, 2560), (65, 1000, 768), (96, 2000, 1536), (300, 700, 1536),
                          (512, 257, 256), (65, 300, 9216), (100, 1000, 4608), (300, 1536, 6912),
                          (37, 3000, 8192), (100, 2000, 8704), (70, 1100, 10240), (40, 700, 512),
-                         (50, 1500, 8960)]
+                         (50, 1500, 8960), (17, 16400, 1024), (128, 1000, 3584)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL_TILE_GEMM_CASES)
