@@ -144,13 +144,11 @@ def forward_kernel(M: int, K: int, N: int) -> str:
     if K % 128 != 0:
         return "gemm_mfma_kernel"
     # the LDS-ring kernel: 128 x 256 tiles (M >= 256 and at least 256 such
-    # tiles); at most 256 tiles of 64 x 128: three K groups (K >= 4608 in a
-    # multiple of 384) or the two groups on interleaved steps (K % 256 == 0,
-    # gemm_pair_kernel); else 128 x 128
+    # tiles); at most 256 tiles of 64 x 128 with K % 256 == 0: the two K
+    # groups sharing each weight copy (gemm_pair_kernel); else 128 x 128
     wide = -(-M // 128) * -(-N // 256)
     tiles64 = -(-M // 64) * -(-N // 128)
-    if not (M >= 256 and wide >= 256) and tiles64 <= 256 and K % 256 == 0 and \
-            not (K >= 36 * 128 and K % 384 == 0):
+    if not (M >= 256 and wide >= 256) and tiles64 <= 256 and K % 256 == 0:
         return "gemm_pair_kernel"
     return "gemm_dma_kernel"
 

@@ -77,40 +77,32 @@ struct DCfg {
     static_assert(kBBytes % (1024 * kWaves) == 0, "weight copies divide the waves");
 };
 
-// KSP > 1 splits K inside the workgroup: KSP groups of WM x WN waves, each
-// with its own LDS ring, run the same loop (so every wave meets the same
-// barriers) over their own K / KSP inputs; the groups' accumulators are added
-// through LDS before the epilogue.  For few tiles on a long K: the sequential
-// K steps of a tile drop by KSP and the compute unit holds KSP times the waves.
-template <int WM, int WN, int TM, int TN, int STAGES, int KSP>
-__global__ __launch_bounds__(KSP * WM * WN * 64)
-__attribute__((amdgpu_waves_per_eu(KSP * WM * WN > 8 ? 3 : 2, KSP * WM * WN > 8 ? 3 : 2)))
+template <int WM, int WN, int TM, int TN, int STAGES>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ gamma, int M,
                      int K, const uint32_t* __restrict__ wp, int N, float beta,
                      float* __restrict__ y, int32_t* __restrict__ acc_out, int tiles_n,
                      int tiles_total) {
     using C = DCfg<WM, WN, TM, TN, STAGES>;
-    __shared__ __attribute__((aligned(16))) char lds[KSP * STAGES * C::kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds[STAGES * C::kStageBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int wv_all = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int kgrp = wv_all / C::kWaves;   // K group
-    const int wv = wv_all % C::kWaves;     // wave within its group
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wv / WN, wn = wv % WN;
-    char* ring = lds + kgrp * STAGES * C::kStageBytes;
+    char* ring = lds;
     const int l32 = lane & 31, h = lane >> 5;
 
     int n0;
     const int m0 = tile_origin(blockIdx.x, tiles_n, tiles_total, C::BM, C::BN, n0);
     const int WR = K >> 4;
-    const int KT = K / BK / KSP;  // K steps of each group (K % (BK * KSP) == 0)
+    const int KT = K / BK;  // K steps (K % BK == 0)
 
     // per-lane source offsets of this wave's copies at step 0 (32-bit, from
     // the block's first row / column); rows and columns past the matrix are
     // clamped onto its last row / column (their products are never stored)
-    const int8_t* abase = xq + (int64_t)m0 * K + (int64_t)kgrp * KT * BK;
-    const uint32_t* bbase = wp + (int64_t)n0 * WR + (int64_t)kgrp * KT * (BK / 16);
+    const int8_t* abase = xq + (int64_t)m0 * K;
+    const uint32_t* bbase = wp + (int64_t)n0 * WR;
     uint32_t aoff[C::kAInstr];
 #pragma unroll
     for (int i = 0; i < C::kAInstr; ++i) {
@@ -196,43 +188,12 @@ void gemm_dma_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ga
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
     __syncthreads();
 
-    // KSP > 1: the accumulators of groups 1.. go through LDS (lane-major, one
-    // int per lane and register) to group 0, whose waves own the epilogue
-    constexpr int kAccInts = C::kWaves * TM * TN * 16 * kWave;  // one group's accumulators
-    int* red = reinterpret_cast<int*>(lds);
-    int* S = reinterpret_cast<int*>(lds) + (KSP > 1 ? kAccInts : 0);  // [BM], all 0 (no offset)
+    int* S = reinterpret_cast<int*>(lds);  // [BM], all 0 (no offset)
     float* Ssc = reinterpret_cast<float*>(S + C::BM);
-    static_assert((int64_t)((KSP > 1 ? kAccInts : 0) + 2 * C::BM) * 4 <=
-                      (int64_t)KSP * STAGES * C::kStageBytes,
-                  "the accumulator exchange and the row tables fit the rings");
-    if constexpr (KSP > 1) {
-        for (int g = 1; g < KSP; ++g) {
-            if (kgrp == g) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int t = 0; t < TN; ++t)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            red[((wv * TM * TN + i * TN + t) * 16 + v) * kWave + lane] = acc[i][t][v];
-            }
-            __syncthreads();
-            if (kgrp == 0) {
-#pragma unroll
-                for (int i = 0; i < TM; ++i)
-#pragma unroll
-                    for (int t = 0; t < TN; ++t)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            acc[i][t][v] += red[((wv * TM * TN + i * TN + t) * 16 + v) * kWave + lane];
-            }
-            __syncthreads();
-        }
-    }
-    epilogue_tables(nullptr, 0, C::BM, m0, M, gamma, beta, S, Ssc, tid, KSP * C::kThreads);
+    static_assert((int64_t)2 * C::BM * 4 <= (int64_t)STAGES * C::kStageBytes, "the row tables fit the ring");
+    epilogue_tables(nullptr, 0, C::BM, m0, M, gamma, beta, S, Ssc, tid, C::kThreads);
     __syncthreads();
-    if (kgrp == 0)
-        store_tiles<TM, TN>(acc, S, Ssc, wm * TM * 32, wn * TN * 32, m0, n0, M, N, y, acc_out, lane);
+    store_tiles<TM, TN>(acc, S, Ssc, wm * TM * 32, wn * TN * 32, m0, n0, M, N, y, acc_out, lane);
 }
 
 
@@ -397,18 +358,18 @@ hipError_t launch_pair(const int8_t* xq, const float* gamma, int M, int K, const
 }
 
 
-template <int WM, int WN, int TM, int TN, int STAGES, int KSP = 1>
+template <int WM, int WN, int TM, int TN, int STAGES>
 hipError_t launch_dcfg(const int8_t* xq, const float* gamma, int M, int K, const uint32_t* wp,
                        int N, float beta, float* y, int32_t* acc, hipStream_t s) {
     using C = DCfg<WM, WN, TM, TN, STAGES>;
-    if (K % (BK * KSP) != 0) return hipErrorInvalidValue;
+    if (K % BK != 0) return hipErrorInvalidValue;
     const int tm = (M + C::BM - 1) / C::BM;
     const int tn = (N + C::BN - 1) / C::BN;
     const int64_t total = (int64_t)tm * tn;
     if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
-    gemm_dma_kernel<WM, WN, TM, TN, STAGES, KSP>
-        <<<dim3((unsigned)total), dim3(KSP * C::kThreads), 0, s>>>(xq, gamma, M, K, wp, N, beta, y,
-                                                                   acc, tn, (int)total);
+    gemm_dma_kernel<WM, WN, TM, TN, STAGES>
+        <<<dim3((unsigned)total), dim3(C::kThreads), 0, s>>>(xq, gamma, M, K, wp, N, beta, y, acc, tn,
+                                                             (int)total);
     return hipGetLastError();
 }
 
@@ -447,26 +408,26 @@ hipError_t launch_gemm_dma(const int8_t* xq, const float* gamma, int M, int K,
     // 29.1 -> 28.0 us; M = 512, K = 2560, N = 2560 11.3 -> 10.6 us; M = 96,
     // K = 4096, N = 11008 15.3 both.
     const int64_t tiles64 = (int64_t)((M + 63) / 64) * ((N + 127) / 128);
-    // long K in a multiple of 3 steps: three K groups (12 waves, 3 a SIMD)
-    // shorten each tile's sequence of steps further (M = 512, K = 6912,
-    // N = 2560: 22.8 -> 22.2 us; with the side-by-side waves 21.9 -> 19.5 us)
-    if (tiles64 <= 256 && K >= 36 * BK && K % (3 * BK) == 0)
-        return launch_dcfg<1, 4, 2, 1, 3, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
-    // otherwise the two groups sharing each weight copy (gemm_pair_kernel):
-    // with K % 512 == 0 two steps a group per stage (8 columns x 128 bytes a
-    // copy) in two 48 KB stages, against one step in three or four stages,
-    // weights streamed from HBM, bit-identical: M = 64, K = 8192, N = 28672
-    // 22.9-24.4 -> 22.6-22.8 us; M = 32 23.0-24.6 -> 22.5-22.7 us; M = 96,
-    // K = 4096, N = 11008 13.4-13.9 -> 12.9-13.1 us; M = 512, K = 2560,
-    // N = 2560 9.0-9.3 -> 8.8 us; M = 200, K = 8192, N = 4096 19.2-19.7 ->
-    // 18.9-19.1 us (M = 64, K = 4096 11.8-12.0 -> 12.1-12.2 us).  One step a
-    // group: four stages from 32 step pairs on (M = 64, K = 8192 24.9 ->
-    // 24.5 us), three below.
-    if (tiles64 <= 256 && K % (4 * BK) == 0)
+    // the two groups sharing each weight copy (gemm_pair_kernel): with
+    // K % 512 == 0 up to K = 8192 two steps a group per stage (8 columns x
+    // 128 bytes a copy) in two 48 KB stages, against one step in three or
+    // four stages, weights streamed from HBM, bit-identical: M = 64, K = 8192,
+    // N = 28672 22.9-24.4 -> 22.6-22.8 us; M = 32 23.0-24.6 -> 22.5-22.7 us;
+    // M = 96, K = 4096, N = 11008 13.4-13.9 -> 12.9-13.1 us; M = 512,
+    // K = 2560, N = 2560 9.0-9.3 -> 8.8 us; M = 200, K = 8192, N = 4096
+    // 19.2-19.7 -> 18.9-19.1 us (M = 64, K = 4096 11.8-12.0 -> 12.1-12.2 us).
+    // Longer K over fewer tiles keeps one step a group in four stages
+    // (M = 64, K = 9216, N = 11008 21.2-21.5 against 21.9-22.1 us; K = 12288,
+    // N = 8192 26.6-26.7 against 28.2 us).  Both replaced a route with three
+    // K groups of separate rings for K >= 4608 in a multiple of 384, which
+    // they beat on its shapes: M = 512, K = 6912, N = 2560 17.8-18.4 ->
+    // 16.9-17.3 us; M = 300, N = 1536 18.1-18.2 -> 17.6-17.7 us; M = 100,
+    // K = 4608, N = 1000 14.0-14.2 -> 13.3 us; M = 64, K = 9216, N = 11008
+    // 23.9-24.4 -> 21.2-21.5 us.
+    if (tiles64 <= 256 && K % (4 * BK) == 0 && K <= 64 * BK)
         return launch_pair<2, 2>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     if (tiles64 <= 256 && K % (2 * BK) == 0)
-        return K >= 64 * BK ? launch_pair<4, 1>(xq, gamma, M, K, wp, N, beta, y, acc, s)
-                            : launch_pair<3, 1>(xq, gamma, M, K, wp, N, beta, y, acc, s);
+        return launch_pair<4, 1>(xq, gamma, M, K, wp, N, beta, y, acc, s);
     // else 128 x 128 tiles (2 x 2 waves of 64 x 64)
     return launch_dcfg<2, 2, 2, 2, 3>(xq, gamma, M, K, wp, N, beta, y, acc, s);
 }

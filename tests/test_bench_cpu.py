@@ -128,7 +128,7 @@ def test_kernel_labels_follow_the_dispatch():
     assert bench.forward_kernel(16, 4096, 11008) == "decode_lds_kernel"
     assert bench.forward_kernel(64, 8192, 28672) == "gemm_pair_kernel"
     assert bench.forward_kernel(512, 2560, 2560) == "gemm_pair_kernel"
-    assert bench.forward_kernel(512, 6912, 2560) == "gemm_dma_kernel"    # three K groups
+    assert bench.forward_kernel(512, 6912, 2560) == "gemm_pair_kernel"
     assert bench.forward_kernel(512, 8192, 28672) == "gemm_dma_kernel"   # 128 x 256 tiles
     assert bench.forward_kernel(2048, 4096, 11008) == "gemm_dma_kernel"
     assert bench.forward_kernel(512, 2560, 13824) == "gemm_dma_kernel"   # 128 x 128 tiles

@@ -99,10 +99,10 @@ def test_ring_gemm_waits_match_its_copies(tmp_path):
         copies = sum(l.startswith("global_load_lds") for l in body)
         others = [l for l in body if re.match(r"(global|buffer|flat)_(load|store|atomic)", l)
                   and not l.startswith("global_load_lds")]
-        # gemm_dma_kernel<WM, WN, TM, TN, STAGES, KSP> / gemm_pair_kernel<STAGES>:
+        # gemm_dma_kernel<WM, WN, TM, TN, STAGES> / gemm_pair_kernel<STAGES, P>:
         # STAGES - 2 later steps stay in flight while the wave waits for the
         # step it multiplies next
-        m = re.search(r"gemm_dma_kernelILi\d+ELi\d+ELi\d+ELi\d+ELi(\d+)ELi", name) or \
+        m = re.search(r"gemm_dma_kernelILi\d+ELi\d+ELi\d+ELi\d+ELi(\d+)E", name) or \
             re.search(r"gemm_pair_kernelILi(\d+)E", name)
         stages = int(m.group(1))
         assert waits == [(stages - 2) * copies], (
