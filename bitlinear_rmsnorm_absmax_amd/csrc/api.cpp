@@ -536,6 +536,9 @@ bitlinear_status_t bitlinear_floor_mfma(const int8_t* x_q, int64_t M, int64_t K,
     BL_TRY(check_rows(fn, "N", N, kMaxN));
     if (K % 128 != 0)
         return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld must be a multiple of 128", fn, (long long)K);
+    if (((M + 127) / 128) * ((N + 255) / 256) > 0x7FFFFFFF)
+        return fail(BITLINEAR_ERR_SHAPE, "%s: M=%lld, N=%lld need more than 2^31-1 tiles of 128 x 256", fn,
+                    (long long)M, (long long)N);
     const bool any = M > 0 && N > 0 && K > 0;
     BL_TRY(need(fn, "x_q", x_q, any, 16));
     BL_TRY(need(fn, "w_packed", w_packed, any, 16));

@@ -396,7 +396,8 @@ bitlinear_status_t bitlinear_floor_stream_read(const void* p, int64_t bytes, uin
  *   the first 128 inputs) and then multiplied from registers only.  Its
  *   duration is what those multiplies take on this device with that data and
  *   nothing else to wait for.  M in [0, 65535 * 128], N in [0, 2^30],
- *   K in [0, 131072] a multiple of 128; M, N or K = 0 launches nothing.
+ *   K in [0, 131072] a multiple of 128, at most 2^31 - 1 tiles of 128 x 256;
+ *   M, N or K = 0 launches nothing.
  *   sink: device uint32 [1], stored only if the xor of all accumulators equals
  *   0x9E3779B9, so its content carries no meaning.
  */

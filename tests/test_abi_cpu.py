@@ -511,5 +511,6 @@ def test_floor_mfma_rejects():
     assert f(FAKE, 512, 128, FAKE, 256, None, None) == bl.ERR_NULL
     assert f(FAKE + 8, 512, 128, FAKE, 256, FAKE, None) == bl.ERR_ALIGN
     assert f(FAKE, 512, 128, FAKE + 4, 256, FAKE, None) == bl.ERR_ALIGN
+    assert f(FAKE, 65535 * 128, 128, FAKE, 1 << 30, FAKE, None) == bl.ERR_SHAPE  # > 2^31-1 tiles
     assert f(None, 0, 128, None, 256, None, None) == bl.OK                # nothing to launch
     assert f(None, 512, 0, None, 256, None, None) == bl.OK
